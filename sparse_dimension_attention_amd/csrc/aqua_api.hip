@@ -1,0 +1,190 @@
+// libaqua C ABI: argument validation (before any HIP call), workspace sizing and dispatch to the
+// gfx950 kernels.  The library never allocates device memory and never synchronises.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/aqua.h"
+#include "aqua_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+aqua_status fail(aqua_status st, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+aqua_status hip_status(hipError_t e, const char *what) {
+  if (e == hipSuccess) return AQUA_OK;
+  return fail(AQUA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t elem_size(int dtype) { return dtype == AQUA_BF16 ? 2 : 4; }
+
+aqua_status check_cache(const aqua_cache *c) {
+  if (!c) return fail(AQUA_ERR_NULL, "cache descriptor is NULL");
+  if (!c->kp || !c->v) return fail(AQUA_ERR_NULL, "cache kp/v pointer is NULL");
+  if (c->dtype != AQUA_F32 && c->dtype != AQUA_BF16)
+    return fail(AQUA_ERR_DTYPE, "cache dtype %d is not AQUA_F32 or AQUA_BF16", c->dtype);
+  if (c->d_head != 64 && c->d_head != 128)
+    return fail(AQUA_ERR_SHAPE, "d_head %d not in {64, 128}", c->d_head);
+  if (c->d_store < 1 || c->d_store > c->d_head)
+    return fail(AQUA_ERR_SHAPE, "d_store %d not in [1, d_head=%d]", c->d_store, c->d_head);
+  if (c->B < 1 || c->Hkv < 1) return fail(AQUA_ERR_SHAPE, "B=%d, Hkv=%d must be >= 1", c->B, c->Hkv);
+  if (c->T_cap < 64 || c->T_cap % 64 != 0)
+    return fail(AQUA_ERR_SHAPE, "T_cap %d must be a positive multiple of 64", c->T_cap);
+  if (c->len < 0 || c->len > c->T_cap)
+    return fail(AQUA_ERR_CAPACITY, "len %d not in [0, T_cap=%d]", c->len, c->T_cap);
+  if (!aligned16(c->kp) || !aligned16(c->v))
+    return fail(AQUA_ERR_ALIGN, "cache kp/v must be 16-byte aligned");
+  return AQUA_OK;
+}
+
+aqua_status check_heads(const aqua_cache *c, int32_t Hq) {
+  if (Hq < 1 || Hq % c->Hkv != 0)
+    return fail(AQUA_ERR_SHAPE, "Hq=%d must be a positive multiple of Hkv=%d", Hq, c->Hkv);
+  const int G = Hq / c->Hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(AQUA_ERR_SHAPE, "group size Hq/Hkv=%d not in {1, 2, 4, 8}", G);
+  return AQUA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *aqua_version(void) { return "libaqua 0.1.0 (gfx950)"; }
+
+const char *aqua_last_error(void) { return g_err; }
+
+aqua_status aqua_project_keys(aqua_cache *c, const void *k_raw, const void *v_raw,
+                              const float *P, int32_t n, const int32_t *slots, void *stream) {
+  g_err[0] = 0;
+  if (aqua_status st = check_cache(c)) return st;
+  if (n < 0) return fail(AQUA_ERR_SHAPE, "n=%d must be >= 0", n);
+  if (!k_raw || !P) return fail(AQUA_ERR_NULL, "k_raw and P are required");
+  if (!aligned16(k_raw) || !aligned16(P) || (v_raw && !aligned16(v_raw)))
+    return fail(AQUA_ERR_ALIGN, "k_raw, v_raw and P must be 16-byte aligned");
+  if (!slots && static_cast<int64_t>(c->len) + n > c->T_cap)
+    return fail(AQUA_ERR_CAPACITY, "append of n=%d at len=%d exceeds T_cap=%d", n, c->len,
+                c->T_cap);
+  if (n == 0) return AQUA_OK;
+  hipError_t e = aqua::launch_project_keys(c->dtype, k_raw, v_raw, P, c->B, c->Hkv, n, c->d_head,
+                                           c->d_store, c->T_cap, c->len, slots, c->kp, c->v,
+                                           static_cast<hipStream_t>(stream));
+  if (aqua_status st = hip_status(e, "aqua_project_keys launch")) return st;
+  if (!slots) c->len += n;
+  return AQUA_OK;
+}
+
+aqua_status aqua_select_dims(const void *q, int32_t qdt, int32_t N, int32_t d, const float *P,
+                             int32_t d_sel, int32_t k, float *q_proj, uint32_t *mask,
+                             int16_t *idx, void *stream) {
+  g_err[0] = 0;
+  if (!q || !P || !mask) return fail(AQUA_ERR_NULL, "q, P and mask are required");
+  if (qdt != AQUA_F32 && qdt != AQUA_BF16)
+    return fail(AQUA_ERR_DTYPE, "q dtype %d is not AQUA_F32 or AQUA_BF16", qdt);
+  if (d != 64 && d != 128) return fail(AQUA_ERR_SHAPE, "d %d not in {64, 128}", d);
+  if (N < 0) return fail(AQUA_ERR_SHAPE, "N=%d must be >= 0", N);
+  if (!(1 <= k && k <= d_sel && d_sel <= d))
+    return fail(AQUA_ERR_SHAPE, "need 1 <= k (%d) <= d_sel (%d) <= d (%d)", k, d_sel, d);
+  if (!aligned16(q) || !aligned16(P) || !aligned16(mask) || (q_proj && !aligned16(q_proj)))
+    return fail(AQUA_ERR_ALIGN, "q, P, mask and q_proj must be 16-byte aligned");
+  if (N == 0) return AQUA_OK;
+  return hip_status(aqua::launch_select(q, qdt, N, d, P, d_sel, k, q_proj, mask, idx,
+                                        static_cast<hipStream_t>(stream)),
+                    "aqua_select_dims launch");
+}
+
+aqua_status aqua_decode_workspace(const aqua_cache *c, int32_t Hq, size_t *bytes) {
+  g_err[0] = 0;
+  if (aqua_status st = check_cache(c)) return st;
+  if (aqua_status st = check_heads(c, Hq)) return st;
+  if (!bytes) return fail(AQUA_ERR_NULL, "bytes is NULL");
+  *bytes = aqua::decode_workspace_bytes(c->dtype, c->B, Hq, c->Hkv, c->d_head, c->T_cap);
+  return AQUA_OK;
+}
+
+aqua_status aqua_decode(const aqua_cache *c, int32_t Hq, const float *q_proj,
+                        const uint32_t *mask, float scale, float *mass, float *out, void *ws,
+                        size_t ws_bytes, void *stream) {
+  g_err[0] = 0;
+  if (aqua_status st = check_cache(c)) return st;
+  if (aqua_status st = check_heads(c, Hq)) return st;
+  if (!q_proj || !mask || !out) return fail(AQUA_ERR_NULL, "q_proj, mask and out are required");
+  if (!ws) return fail(AQUA_ERR_WORKSPACE, "workspace is NULL");
+  if (c->len < 1) return fail(AQUA_ERR_SHAPE, "len=%d: decode needs at least one token", c->len);
+  if (!aligned16(q_proj) || !aligned16(mask) || !aligned16(out) || !aligned16(ws) ||
+      (mass && !aligned16(mass)))
+    return fail(AQUA_ERR_ALIGN, "q_proj, mask, out, mass and ws must be 16-byte aligned");
+  const size_t need =
+      aqua::decode_workspace_bytes(c->dtype, c->B, Hq, c->Hkv, c->d_head, c->T_cap);
+  if (ws_bytes < need)
+    return fail(AQUA_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, need);
+
+  const aqua::DecodeLayout L = aqua::decode_layout(c->dtype, Hq / c->Hkv);
+  aqua::DecodeArgs a{};
+  a.kp = c->kp;
+  a.v = c->v;
+  a.q_proj = q_proj;
+  a.mask = mask;
+  a.mass = mass;
+  a.out = out;
+  aqua::decode_workspace_carve(ws, c->dtype, c->B, Hq, c->Hkv, c->d_head, c->T_cap,
+                               &a.counters, &a.partials, &a.scores);
+  a.B = c->B;
+  a.Hq = Hq;
+  a.Hkv = c->Hkv;
+  a.d = c->d_head;
+  a.d_store = c->d_store;
+  a.T_cap = c->T_cap;
+  a.len = c->len;
+  a.S = (c->len + L.split - 1) / L.split;
+  a.qscale = scale * 1.4426950408889634f;  // log2(e): scores are kept in log2 units
+  return hip_status(aqua::launch_decode(c->dtype, a, static_cast<hipStream_t>(stream)),
+                    "aqua_decode launch");
+}
+
+aqua_status aqua_prefill_workspace(const aqua_cache *c, int32_t Hq, int32_t Lq, size_t *bytes) {
+  g_err[0] = 0;
+  if (aqua_status st = check_cache(c)) return st;
+  if (aqua_status st = check_heads(c, Hq)) return st;
+  if (!bytes) return fail(AQUA_ERR_NULL, "bytes is NULL");
+  if (Lq < 1) return fail(AQUA_ERR_SHAPE, "Lq=%d must be >= 1", Lq);
+  *bytes = 0;
+  return AQUA_OK;
+}
+
+aqua_status aqua_prefill_chunk(const aqua_cache *c, int32_t Hq, const void *q, int32_t Lq,
+                               int32_t pos0, const float *P, int32_t d_sel, int32_t k,
+                               float scale, float *out, float *q_proj_out, uint32_t *mask_out,
+                               void *ws, size_t ws_bytes, void *stream) {
+  g_err[0] = 0;
+  (void)q; (void)Lq; (void)pos0; (void)P; (void)d_sel; (void)k; (void)scale; (void)out;
+  (void)q_proj_out; (void)mask_out; (void)ws; (void)ws_bytes; (void)stream; (void)Hq;
+  if (aqua_status st = check_cache(c)) return st;
+  return fail(AQUA_ERR_SHAPE, "aqua_prefill_chunk: not available in this build");
+}
+
+aqua_status aqua_h2o_victim(float *mass, int32_t *slot_pos, int32_t B, int32_t Hkv,
+                            int32_t n_slots, int32_t t_new, int32_t recent, int32_t *victim,
+                            void *stream) {
+  g_err[0] = 0;
+  if (!mass || !slot_pos || !victim) return fail(AQUA_ERR_NULL, "mass, slot_pos, victim required");
+  if (B < 1 || Hkv < 1 || n_slots < 1)
+    return fail(AQUA_ERR_SHAPE, "B=%d, Hkv=%d, n_slots=%d must be >= 1", B, Hkv, n_slots);
+  if (recent < 0 || t_new < 0)
+    return fail(AQUA_ERR_SHAPE, "t_new=%d and recent=%d must be >= 0", t_new, recent);
+  return hip_status(aqua::launch_h2o_victim(mass, slot_pos, B, Hkv, n_slots, t_new, recent,
+                                            victim, static_cast<hipStream_t>(stream)),
+                    "aqua_h2o_victim launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,90 @@
+// Internal declarations shared by the libaqua host layer and its HIP kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace aqua {
+
+// ------------------------------------------------------------------ bf16 storage helpers
+// bf16 is the upper half of an fp32 bit pattern.  Widening is exact; narrowing rounds to
+// nearest with ties to even by adding 0x7fff plus the lowest kept bit before truncation.
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) {
+  return __uint_as_float(pair & 0xffff0000u);
+}
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);  // NaN
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// Storage element types: float (AQUA_F32) or raw bf16 bits (AQUA_BF16).
+using bf16_t = uint16_t;
+
+template <typename T> __device__ __forceinline__ float load_elem(const T *p);
+template <> __device__ __forceinline__ float load_elem<float>(const float *p) { return *p; }
+template <> __device__ __forceinline__ float load_elem<bf16_t>(const bf16_t *p) {
+  return bf16_to_f32(*p);
+}
+template <typename T> __device__ __forceinline__ T store_elem(float f);
+template <> __device__ __forceinline__ float store_elem<float>(float f) { return f; }
+template <> __device__ __forceinline__ bf16_t store_elem<bf16_t>(float f) {
+  return f32_to_bf16_rne(f);
+}
+
+// ------------------------------------------------------------------ wave helpers (wave64)
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// ------------------------------------------------------------------ launch parameter blocks
+struct DecodeArgs {
+  const void *kp;        // [B][Hkv][d_store][T_cap]
+  const void *v;         // [B][Hkv][T_cap][d]
+  const float *q_proj;   // [B][Hq][d]
+  const uint32_t *mask;  // [B][Hq][d/32]
+  float *mass;           // [B][Hkv][T_cap] or nullptr
+  float *out;            // [B][Hq][d]
+  uint32_t *counters;    // [B*Hkv], zero between calls
+  float *partials;       // [B][Hq][S][d+2]  (m, l, o[d]) in log2 units
+  float *scores;         // [B][Hq][T_cap]   log2-domain scores (mass mode only)
+  int B, Hq, Hkv, d, d_store, T_cap, len;
+  int S;                 // splits per (b, g)
+  float qscale;          // scale * log2(e)
+};
+
+struct DecodeLayout {
+  int waves;        // waves per workgroup
+  int tokens_wave;  // tokens per wave
+  int split;        // tokens per workgroup (= waves * tokens_wave)
+};
+
+// Launch geometry of the decode kernel for a storage dtype (0 f32, 1 bf16) and group size.
+DecodeLayout decode_layout(int dtype, int G);
+size_t decode_workspace_bytes(int dtype, int B, int Hq, int Hkv, int d, int T_cap);
+void decode_workspace_carve(void *ws, int dtype, int B, int Hq, int Hkv, int d, int T_cap,
+                            uint32_t **counters, float **partials, float **scores);
+
+hipError_t launch_select(const void *q, int qdt, int N, int d, const float *P, int d_sel, int k,
+                         float *q_proj, uint32_t *mask, int16_t *idx, hipStream_t s);
+hipError_t launch_project_keys(int dtype, const void *k_raw, const void *v_raw, const float *P,
+                               int B, int Hkv, int n, int d, int d_store, int T_cap, int len0,
+                               const int32_t *slots, void *kp, void *v, hipStream_t s);
+hipError_t launch_decode(int dtype, const DecodeArgs &a, hipStream_t s);
+hipError_t launch_h2o_victim(float *mass, int32_t *slot_pos, int B, int Hkv, int n_slots,
+                             int t_new, int recent, int32_t *victim, hipStream_t s);
+
+}  // namespace aqua

@@ -1,0 +1,130 @@
+"""libaqua's C ABI without a GPU: the library loads, exports every call include/aqua.h declares,
+and rejects bad arguments with the documented status before any HIP call (no pointer given
+here is ever dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_dimension_attention_amd as aq
+from sparse_dimension_attention_amd import aqua as A
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(aq.LIB_PATH):
+        import __graft_entry__
+
+        __graft_entry__.build()
+    return aq.load_library()
+
+
+def _declared():
+    with open(os.path.join(ROOT, "include", "aqua.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:const char \*|aqua_status )(aqua_\w+)\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert len(names) == 9
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(aq.EXPORTS)
+    assert "gfx950" in aq.aqua_version()
+
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced
+
+
+def _cache(**kw):
+    c = dict(kp=FAKE, v=FAKE, B=2, Hkv=2, d_head=128, d_store=128, T_cap=256, len=10,
+             dtype=A.AQUA_BF16)
+    c.update(kw)
+    return A.aqua_cache(**c)
+
+
+def _decode(lib, cache, Hq=8, ws_bytes=1 << 30, q=FAKE, mask=FAKE, out=FAKE, ws=FAKE):
+    return lib.aqua_decode(ctypes.byref(cache), Hq, q, mask, 0.1, None, out, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,Hq,status", [
+    (dict(), 6, A.AQUA_ERR_SHAPE),                   # Hq not a multiple of Hkv
+    (dict(), 2 * 16, A.AQUA_ERR_SHAPE),              # group size 16
+    (dict(len=0), 8, A.AQUA_ERR_SHAPE),              # nothing to attend
+    (dict(len=300), 8, A.AQUA_ERR_CAPACITY),         # len > T_cap
+    (dict(T_cap=100), 8, A.AQUA_ERR_SHAPE),          # T_cap not a multiple of 64
+    (dict(d_head=96), 8, A.AQUA_ERR_SHAPE),
+    (dict(d_store=0), 8, A.AQUA_ERR_SHAPE),
+    (dict(d_store=129), 8, A.AQUA_ERR_SHAPE),
+    (dict(dtype=5), 8, A.AQUA_ERR_DTYPE),
+    (dict(kp=None), 8, A.AQUA_ERR_NULL),
+    (dict(v=FAKE + 8), 8, A.AQUA_ERR_ALIGN),
+])
+def test_decode_rejects(lib, kw, Hq, status):
+    assert _decode(lib, _cache(**kw), Hq) == status
+    assert lib.aqua_last_error().decode() != ""
+
+
+def test_decode_rejects_buffers(lib):
+    c = _cache()
+    assert _decode(lib, c, q=None) == A.AQUA_ERR_NULL
+    assert _decode(lib, c, ws=None) == A.AQUA_ERR_WORKSPACE
+    assert _decode(lib, c, out=FAKE + 4) == A.AQUA_ERR_ALIGN
+    need = ctypes.c_size_t(0)
+    assert lib.aqua_decode_workspace(ctypes.byref(c), 8, ctypes.byref(need)) == A.AQUA_OK
+    assert need.value > 0
+    assert _decode(lib, c, ws_bytes=need.value - 1) == A.AQUA_ERR_WORKSPACE
+
+
+def test_workspace_grows_with_capacity(lib):
+    sizes = []
+    for T_cap in (64, 2048, 8192, 131072):
+        n = ctypes.c_size_t(0)
+        assert lib.aqua_decode_workspace(ctypes.byref(_cache(T_cap=T_cap, len=1)), 8,
+                                         ctypes.byref(n)) == A.AQUA_OK
+        sizes.append(n.value)
+    assert sizes == sorted(sizes) and sizes[0] > 0
+
+
+def test_project_keys_rejects(lib):
+    c = _cache(len=250)
+    assert lib.aqua_project_keys(ctypes.byref(c), FAKE, FAKE, FAKE, 7, None, None) == \
+        A.AQUA_ERR_CAPACITY
+    assert c.len == 250
+    assert lib.aqua_project_keys(ctypes.byref(c), None, FAKE, FAKE, 1, None, None) == \
+        A.AQUA_ERR_NULL
+    assert lib.aqua_project_keys(ctypes.byref(c), FAKE + 2, FAKE, FAKE, 1, None, None) == \
+        A.AQUA_ERR_ALIGN
+    assert lib.aqua_project_keys(ctypes.byref(c), FAKE, FAKE, FAKE, -1, None, None) == \
+        A.AQUA_ERR_SHAPE
+    # n == 0 is a no-op that touches nothing
+    assert lib.aqua_project_keys(ctypes.byref(c), FAKE, FAKE, FAKE, 0, None, None) == A.AQUA_OK
+    assert c.len == 250
+
+
+@pytest.mark.parametrize("qdt,N,d,d_sel,k,status", [
+    (A.AQUA_BF16, 4, 96, 96, 10, A.AQUA_ERR_SHAPE),
+    (A.AQUA_BF16, 4, 128, 128, 0, A.AQUA_ERR_SHAPE),
+    (A.AQUA_BF16, 4, 128, 64, 65, A.AQUA_ERR_SHAPE),
+    (A.AQUA_BF16, 4, 128, 129, 96, A.AQUA_ERR_SHAPE),
+    (A.AQUA_BF16, -1, 128, 128, 96, A.AQUA_ERR_SHAPE),
+    (7, 4, 128, 128, 96, A.AQUA_ERR_DTYPE),
+    (A.AQUA_F32, 0, 128, 128, 96, A.AQUA_OK),  # empty: no-op
+])
+def test_select_rejects(lib, qdt, N, d, d_sel, k, status):
+    assert lib.aqua_select_dims(FAKE, qdt, N, d, FAKE, d_sel, k, FAKE, FAKE, None, None) == status
+
+
+def test_h2o_victim_rejects(lib):
+    assert lib.aqua_h2o_victim(None, FAKE, 1, 1, 4, 10, 2, FAKE, None) == A.AQUA_ERR_NULL
+    assert lib.aqua_h2o_victim(FAKE, FAKE, 1, 1, 0, 10, 2, FAKE, None) == A.AQUA_ERR_SHAPE
+    assert lib.aqua_h2o_victim(FAKE, FAKE, 1, 1, 4, 10, -1, FAKE, None) == A.AQUA_ERR_SHAPE
+
+
+def test_binding_raises_with_message(lib):
+    with pytest.raises(aq.AquaError, match="AQUA_ERR_SHAPE"):
+        A._check(_decode(lib, _cache(len=0)))

@@ -1,0 +1,137 @@
+"""GPU parity of aqua_decode (with selection and key projection in front) against the oracle."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import sparse_dimension_attention_amd as aq
+from gpu_util import (DEV, assert_close, oracle_decode, rel_l2, run_decode, unpack_mask)
+from oracle import aqua_oracle as O
+from synth import config, make_decode_inputs, storage_to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_masks(r, c, d_sel=None, k=None):
+    d = c["d"]
+    m = unpack_mask(r["mask"], d)
+    qp = r["qp"].cpu().double().numpy()
+    assert np.array_equal(m, O.select(qp, d_sel or c.get("d_sel", d), k or c["k"]))
+    return m
+
+
+def test_tiny_decode_f32():
+    c = config(1)
+    inp = make_decode_inputs(c)
+    r = run_decode(inp, c)
+    m = _check_masks(r, c)
+    ref = oracle_decode(inp, c, m)
+    assert_close(r["out"].cpu().double().numpy(), ref, "f32", "tiny decode")
+
+
+@pytest.mark.parametrize("Hq,Hkv,T,k,d", [
+    (8, 2, 3000, 96, 128),     # G=4, two splits, ragged tail
+    (4, 4, 2049, 64, 128),     # G=1
+    (8, 4, 777, 128, 128),     # G=2, k = d
+    (16, 2, 1500, 32, 128),    # G=8
+    (8, 2, 1, 96, 128),        # a single token
+    (4, 1, 513, 40, 64),       # d = 64
+])
+def test_decode_bf16_shapes(Hq, Hkv, T, k, d):
+    c = config(2, B=2, Hq=Hq, Hkv=Hkv, T=T, k=k, d=d, d_store=d, d_sel=d)
+    inp = make_decode_inputs(c)
+    r = run_decode(inp, c)
+    m = _check_masks(r, c)
+    ref = oracle_decode(inp, c, m)
+    assert_close(r["out"].cpu().double().numpy(), ref, "bf16", f"decode {Hq},{Hkv},{T}")
+
+
+@pytest.mark.parametrize("length", [1, 63, 511, 512, 2047, 2048, 2049, 4100])
+def test_decode_ragged_lengths_f32(length):
+    """fp32 storage: tight tolerance across split and wavefront boundaries; T_cap > len."""
+    c = config(1, B=1, Hq=4, Hkv=2, d=128, T=length, k=100, d_store=128, d_sel=128)
+    inp = make_decode_inputs(c)
+    r = run_decode(inp, c, T_cap=4160)
+    m = _check_masks(r, c)
+    ref = oracle_decode(inp, c, m)
+    assert_close(r["out"].cpu().double().numpy(), ref, "f32", f"len {length}")
+
+
+def test_decode_deterministic_and_reusable_workspace():
+    c = config(2, B=2, Hq=8, Hkv=2, T=5000)
+    inp = make_decode_inputs(c)
+    r = run_decode(inp, c)
+    outs = []
+    for _ in range(3):
+        out = torch.full_like(r["out"], float("nan"))
+        aq.aqua_decode(r["cache"], c["Hq"], r["qp"], r["mask"], 1 / math.sqrt(c["d"]), out,
+                       r["ws"])
+        outs.append(out)
+    torch.cuda.synchronize()
+    for o in outs:
+        assert torch.equal(o, r["out"])
+    # the workspace is left cleared
+    ws = r["ws"]
+    n = c["B"] * c["Hkv"] * 4
+    assert int(ws[:n].count_nonzero()) == 0
+
+
+def test_decode_llama8b_full_size_sampled():
+    """B=16, Hq=32, Hkv=8, T=8192, k=96 (the benchmark workload): every mask checked, outputs
+    of a sample of heads checked against the oracle one by one."""
+    c = config(2)
+    inp = make_decode_inputs(c)
+    r = run_decode(inp, c)
+    m = _check_masks(r, c)
+    heads = [(0, 0), (0, 31), (5, 13), (9, 2), (15, 30), (15, 31), (7, 16), (3, 9)]
+    ref = oracle_decode(inp, c, m, heads=heads)
+    got = r["out"].cpu().double().numpy()
+    for b, h in heads:
+        assert_close(got[b, h], ref[b, h], "bf16", f"head {(b, h)}")
+    assert np.isfinite(got).all()
+
+
+@pytest.fixture(scope="module")
+def long_inputs():
+    return make_decode_inputs(config(3))
+
+
+@pytest.mark.parametrize("k", [128, 96, 64, 32])
+def test_decode_long_context_sampled(k, long_inputs):
+    """B=1, T=131072 (many splits per group), every k of the sweep; sampled heads."""
+    c = config(3, k=k)
+    inp = long_inputs
+    r = run_decode(inp, c, k=k)
+    m = _check_masks(r, c, k=k)
+    heads = [(0, 0), (0, 5), (0, 22), (0, 31)]
+    ref = oracle_decode(inp, c, m, heads=heads)
+    got = r["out"].cpu().double().numpy()
+    for b, h in heads:
+        assert_close(got[b, h], ref[b, h], "bf16", f"k={k} head {h}")
+
+
+def test_decode_mass_accumulation():
+    """Mass mode: mass[t] grows by the sum over the group's heads of the softmax weights."""
+    c = config(2, B=2, Hq=8, Hkv=2, T=3000, d_store=96, d_sel=96, k=64)
+    inp = make_decode_inputs(c)
+    T_cap = 3008
+    mass0 = torch.rand(c["B"], c["Hkv"], T_cap, device=DEV)
+    mass = mass0.clone()
+    r = run_decode(inp, c, T_cap=T_cap, mass=mass)
+    m = _check_masks(r, c)
+    P64 = storage_to_f64(inp["P"])
+    qp64 = O.project(storage_to_f64(inp["q"]), P64)
+    G = c["Hq"] // c["Hkv"]
+    got = mass.cpu().double().numpy() - mass0.cpu().double().numpy()
+    for b in range(c["B"]):
+        for g in range(c["Hkv"]):
+            Kp = O.project_keys_stored(storage_to_f64(inp["k"][b, g]), P64, "bf16", 96)
+            V = storage_to_f64(inp["v"][b, g])
+            add = np.zeros(c["T"])
+            for h in range(g * G, (g + 1) * G):
+                _, p = O.attend(qp64[b, h], m[b, h], Kp, V, 1 / math.sqrt(c["d"]))
+                add += p
+            assert np.max(np.abs(got[b, g, :c["T"]] - add)) <= 1e-3 * add.max()
+            assert abs(got[b, g, :c["T"]].sum() - G) < 1e-3
+            assert np.all(got[b, g, c["T"]:] == 0)
