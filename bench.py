@@ -1,0 +1,219 @@
+"""Benchmark of AQUA decode attention on one MI355X.
+
+One step = one decode step of a Llama-3.1-8B-shaped attention layer (B=16, 32 query heads, 8 KV
+heads, d_head=128, context 8192 bf16 tokens, keep k=96 of 128 projected dims), run as the single
+launch aqua_decode_step: append the new token's K' = k P and v to the dimension-major cache,
+project the 512 queries and keep each one's top-96 |q'| dims, attend every query over the 8192
+tokens on its own dims (split-T, partials merged inside the same launch).  The same step as three
+calls (aqua_project_keys + aqua_select_dims + aqua_decode) is timed too and reported beside it.
+Inputs are seeded synthetic tensors resident in HBM before timing starts.
+
+Prints one JSON line.  value = query-head x token pairs attended per second over the whole step;
+roofline = algorithmic HBM bytes of the step's launch (the K' rows of each KV group's mask union
+and all of V over the context, raw q, the new token in and out, P, output) / its average
+duration from HIP events on the launch stream.
+cpu_baseline = the fp64 oracle timed on the host cores on a bounded sample of the same step.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import sparse_dimension_attention_amd as aq  # noqa: E402
+from synth import config, make_decode_inputs  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "AQUA decode attn: query-heads·tokens/s and achieved HBM GB/s vs peak (k=96)"
+
+
+def union_rows(mask_words: np.ndarray, B: int, Hkv: int, G: int, d: int, d_store: int):
+    """Per (b, g): number of K' rows in the union of the group's masks."""
+    bits = np.unpackbits(mask_words.view(np.uint8), bitorder="little").reshape(B, Hkv, G, d)
+    u = bits.any(axis=2)[..., :d_store]
+    return u.sum(axis=-1)
+
+
+def step_bytes(U: np.ndarray, c: dict, T: int) -> int:
+    """Algorithmic bytes of one fused decode step: the K' rows of U and all of V over the T-1
+    cached tokens, raw q, the new token's k and v in, its K' and V out, P once, fp32 output."""
+    d, B, Hq, Hkv = c["d"], c["B"], c["Hq"], c["Hkv"]
+    es = 2 if c["dtype"] == "bf16" else 4
+    kv = int(U.sum()) * (T - 1) * es + B * Hkv * (T - 1) * d * es
+    new_tok = B * Hkv * d * es * 2 + B * Hkv * (c["d_store"] + d) * es
+    return kv + B * Hq * d * es + new_tok + d * d * 4 + B * Hq * d * 4
+
+
+def cpu_baseline(c: dict, n_groups: int, reps: int):
+    """The oracle, as it stands, on n_groups KV groups of the same decode step."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import aqua_oracle as O
+    from synth import storage_to_f64
+
+    rng = np.random.default_rng(0)
+    all_g = [(b, g) for b in range(c["B"]) for g in range(c["Hkv"])]
+    groups = [all_g[i] for i in sorted(rng.choice(len(all_g), n_groups, replace=False))]
+    inp = make_decode_inputs(c, groups=groups)
+    P = storage_to_f64(inp["P"])
+    q, K, V = (storage_to_f64(inp[x]) for x in ("q", "k", "v"))
+    T, d, k = c["T"], c["d"], c["k"]
+    cached = [O.project_keys_stored(K[i, :T - 1], P, c["dtype"], c["d_store"])
+              for i in range(n_groups)]  # the cache before the step (not timed)
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        for i in range(n_groups):
+            Kp = np.concatenate([cached[i],
+                                 O.project_keys_stored(K[i, T - 1:], P, c["dtype"], c["d_store"])])
+            qp = O.project(q[i], P)
+            m = O.select(qp, c["d_sel"], k)
+            for h in range(qp.shape[0]):
+                O.attend(qp[h], m[h], Kp, V[i], 1 / math.sqrt(d))
+        times.append(time.perf_counter() - t0)
+    t = statistics.median(times)
+    G = c["Hq"] // c["Hkv"]
+    threads = max([x.get("num_threads", 1) for x in threadpool_info()] or [1])
+    return {"value": n_groups * G * T / t, "unit": "q-head·tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{n_groups} of {c['B'] * c['Hkv']} (b, KV-head) groups of one decode step "
+                      f"(new key projected and appended, {n_groups * G} queries projected, "
+                      f"selected and attended over T={T}); median of {reps} runs; "
+                      f"host has {os.cpu_count()} CPUs, affinity {len(os.sched_getaffinity(0))}"}
+
+
+def copy_probe(nbytes: int, reps: int):
+    """A plain device copy of known size (for scaling HBM byte counters)."""
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": nbytes, "reps": reps}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--cpu-groups", type=int, default=48)
+    ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the AQUA decode path here runs on a single MI355X "
+              "(--gpus 1); multi-GPU runs are not part of this build.", file=sys.stderr)
+        sys.exit(2)
+    if not os.path.exists(aq.LIB_PATH):
+        import __graft_entry__
+
+        __graft_entry__.build()
+    aq.load_library()
+    if args.copy_probe:
+        copy_probe(args.copy_probe, 10)
+        return
+
+    dev = torch.device("cuda:0")
+    c = config(2)
+    B, Hq, Hkv, d, T, k = c["B"], c["Hq"], c["Hkv"], c["d"], c["T"], c["k"]
+    G = Hq // Hkv
+    inp = make_decode_inputs(c, workers=16)
+    P = inp["P"].to(dev)
+    kp = torch.empty(B, Hkv, d, T, dtype=torch.bfloat16, device=dev)
+    v = torch.empty(B, Hkv, T, d, dtype=torch.bfloat16, device=dev)
+    cache = aq.make_cache(kp, v, 0)
+    k_all, v_all = inp["k"].to(dev), inp["v"].to(dev)
+    aq.aqua_project_keys(cache, k_all[:, :, :T - 1].contiguous(), v_all[:, :, :T - 1].contiguous(),
+                         P, T - 1)
+    k_new = k_all[:, :, T - 1].contiguous()
+    v_new = v_all[:, :, T - 1].contiguous()
+    del k_all, v_all
+    q = inp["q"].to(dev)
+    qp = torch.empty(B * Hq, d, device=dev)
+    mask = torch.empty(B * Hq, d // 32, dtype=torch.int32, device=dev)
+    out = torch.empty(B, Hq, d, device=dev)
+    ws = torch.zeros(aq.aqua_decode_workspace(cache, Hq), dtype=torch.uint8, device=dev)
+    scale = 1.0 / math.sqrt(d)
+    torch.cuda.synchronize()
+
+    ev = []
+
+    def step(timed: bool):
+        cache.len = T - 1
+        if timed:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+        aq.aqua_decode_step(cache, Hq, q, k_new, v_new, P, d, k, scale, out, ws)
+        if timed:
+            e1.record()
+            ev.append((e0, e1))
+
+    def step_unfused():
+        cache.len = T - 1
+        aq.aqua_project_keys(cache, k_new[:, :, None], v_new[:, :, None], P, 1)
+        aq.aqua_select_dims(q.reshape(B * Hq, d), P, d, k, qp, mask)
+        aq.aqua_decode(cache, Hq, qp, mask, scale, out, ws)
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    k_ms = [a.elapsed_time(b) for a, b in ev]
+    k_avg_s = statistics.mean(k_ms) * 1e-3
+
+    # the same step as three launches (for comparison; not the headline)
+    for _ in range(5):
+        step_unfused()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n_unf = max(10, args.steps // 4)
+    for _ in range(n_unf):
+        step_unfused()
+    torch.cuda.synchronize()
+    ms_unfused = (time.perf_counter() - t0) * 1e3 / n_unf
+
+    U = union_rows(mask.cpu().numpy().reshape(B, Hq, d // 32), B, Hkv, G, d, c["d_store"])
+    nbytes = step_bytes(U, c, T)
+    achieved = nbytes / k_avg_s / 1e9
+    value = B * Hq * T / (ms_per_step * 1e-3)
+    rec = {
+        "metric": METRIC, "value": value, "unit": "q-head·tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded; q, K = Z diag(exp(-i/40)+0.05) P^T, V ~ N(0,1))",
+        "config": {"workload": c["name"], "B": B, "Hq": Hq, "Hkv": Hkv, "d_head": d, "T": T,
+                   "k": k, "storage": c["dtype"], "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+        "kernel": "decode_kernel (fused step: append + select + split-T decode + merge)",
+        "kernel_us": k_avg_s * 1e6,
+        "kernel_us_p10_p90": [float(np.percentile(k_ms, 10) * 1e3),
+                              float(np.percentile(k_ms, 90) * 1e3)],
+        "bytes_per_launch": nbytes,
+        "mean_union_rows": float(U.mean()),
+        "ms_per_step_three_launches": ms_unfused,
+    }
+    if not args.no_cpu:
+        rec["cpu_baseline"] = cpu_baseline(c, args.cpu_groups, args.cpu_reps)
+    print(json.dumps(rec))
+
+
+if __name__ == "__main__":
+    main()

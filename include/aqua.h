@@ -117,6 +117,23 @@ aqua_status aqua_decode(const aqua_cache *c, int32_t Hq, const float *q_proj,
                         const uint32_t *mask, float scale, float *mass, float *out, void *ws,
                         size_t ws_bytes, void *stream);
 
+/* One whole decode step in one launch (the online step of the digest's 技术框架 and the blog's
+ * "How AQUA Works", step 2, for a token being generated): appends the new token, then every
+ * query head projects its query, selects its top-k dims and attends over [0, len + 1).
+ * Equivalent to aqua_project_keys(c, k_new, v_new, P, 1, NULL) + aqua_select_dims(q, ...) +
+ * aqua_decode(...), fused so that no small launch sits on the critical path.
+ *   q     : device [B][Hq][d_head], c->dtype (raw queries).
+ *   k_new, v_new: device [B][Hkv][d_head], c->dtype (the new token's raw key and value); its K'
+ *           and V are written at column len, then c->len += 1 (AQUA_ERR_CAPACITY if full).
+ *   P     : device [d_head][d_head] fp32.   1 <= k <= d_sel <= d_store.
+ *   mass, out, ws, ws_bytes: as aqua_decode (same workspace size, same zero-fill contract).
+ *   q_proj_out, mask_out: NULL, or out device [B][Hq][d_head] fp32 and [B][Hq][d_head/32]
+ *           uint32 (the q' and masks used, as aqua_select_dims would write them). */
+aqua_status aqua_decode_step(aqua_cache *c, int32_t Hq, const void *q, const void *k_new,
+                             const void *v_new, const float *P, int32_t d_sel, int32_t k,
+                             float scale, float *mass, float *out, float *q_proj_out,
+                             uint32_t *mask_out, void *ws, size_t ws_bytes, void *stream);
+
 /* Bytes of workspace aqua_prefill_chunk needs for a chunk of Lq queries (no clearing needed). */
 aqua_status aqua_prefill_workspace(const aqua_cache *c, int32_t Hq, int32_t Lq, size_t *bytes);
 

@@ -25,8 +25,8 @@ _STATUS_NAMES = {0: "AQUA_OK", 1: "AQUA_ERR_NULL", 2: "AQUA_ERR_SHAPE", 3: "AQUA
                  7: "AQUA_ERR_HIP"}
 
 EXPORTS = ("aqua_version", "aqua_last_error", "aqua_project_keys", "aqua_select_dims",
-           "aqua_decode_workspace", "aqua_decode", "aqua_prefill_workspace", "aqua_prefill_chunk",
-           "aqua_h2o_victim")
+           "aqua_decode_workspace", "aqua_decode", "aqua_decode_step", "aqua_prefill_workspace",
+           "aqua_prefill_chunk", "aqua_h2o_victim")
 
 
 class AquaError(RuntimeError):
@@ -61,6 +61,8 @@ def load_library() -> ctypes.CDLL:
         "aqua_select_dims": ([P, I32, I32, I32, P, I32, I32, P, P, P, P], ctypes.c_int),
         "aqua_decode_workspace": ([cp, I32, ctypes.POINTER(SZ)], ctypes.c_int),
         "aqua_decode": ([cp, I32, P, P, ctypes.c_float, P, P, P, SZ, P], ctypes.c_int),
+        "aqua_decode_step": ([cp, I32, P, P, P, P, I32, I32, ctypes.c_float, P, P, P, P, P, SZ,
+                              P], ctypes.c_int),
         "aqua_prefill_workspace": ([cp, I32, I32, ctypes.POINTER(SZ)], ctypes.c_int),
         "aqua_prefill_chunk": ([cp, I32, P, I32, I32, P, I32, I32, ctypes.c_float, P, P, P, P,
                                 SZ, P], ctypes.c_int),
@@ -140,6 +142,17 @@ def aqua_decode(cache: aqua_cache, Hq: int, q_proj, mask, scale: float, out, ws,
     _check(load_library().aqua_decode(ctypes.byref(cache), int(Hq), _ptr(q_proj), _ptr(mask),
                                       float(scale), _ptr(mass), _ptr(out), _ptr(ws), nbytes,
                                       _stream(stream)))
+
+
+def aqua_decode_step(cache: aqua_cache, Hq: int, q, k_new, v_new, P, d_sel: int, k: int,
+                     scale: float, out, ws, mass=None, q_proj_out=None, mask_out=None,
+                     stream=None):
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(load_library().aqua_decode_step(ctypes.byref(cache), int(Hq), _ptr(q), _ptr(k_new),
+                                           _ptr(v_new), _ptr(P), int(d_sel), int(k),
+                                           float(scale), _ptr(mass), _ptr(out),
+                                           _ptr(q_proj_out), _ptr(mask_out), _ptr(ws), nbytes,
+                                           _stream(stream)))
 
 
 def aqua_prefill_workspace(cache: aqua_cache, Hq: int, Lq: int) -> int:

@@ -7,6 +7,7 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 OUT = os.path.join(HERE, "libaqua.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -24,7 +25,7 @@ def sources():
 def build(verbose: bool = False) -> str:
     """Compile every HIP source into libaqua.so; returns its path.  Always recompiles."""
     tmp = OUT + ".tmp"
-    cmd = [HIPCC, *FLAGS, f"-I{CSRC}", *sources(), "-o", tmp]
+    cmd = [HIPCC, *FLAGS, f"-I{CSRC}", f"-I{INCLUDE}", *sources(), "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     msgs = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if noise not in l)

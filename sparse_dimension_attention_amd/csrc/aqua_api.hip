@@ -4,7 +4,7 @@
 #include <cstdio>
 #include <cstring>
 
-#include "../../include/aqua.h"
+#include "aqua.h"
 #include "aqua_internal.h"
 
 namespace {
@@ -150,6 +150,65 @@ aqua_status aqua_decode(const aqua_cache *c, int32_t Hq, const float *q_proj,
   a.qscale = scale * 1.4426950408889634f;  // log2(e): scores are kept in log2 units
   return hip_status(aqua::launch_decode(c->dtype, a, static_cast<hipStream_t>(stream)),
                     "aqua_decode launch");
+}
+
+aqua_status aqua_decode_step(aqua_cache *c, int32_t Hq, const void *q, const void *k_new,
+                             const void *v_new, const float *P, int32_t d_sel, int32_t k,
+                             float scale, float *mass, float *out, float *q_proj_out,
+                             uint32_t *mask_out, void *ws, size_t ws_bytes, void *stream) {
+  g_err[0] = 0;
+  if (aqua_status st = check_cache(c)) return st;
+  if (aqua_status st = check_heads(c, Hq)) return st;
+  if (!q || !k_new || !v_new || !P || !out)
+    return fail(AQUA_ERR_NULL, "q, k_new, v_new, P and out are required");
+  if (!ws) return fail(AQUA_ERR_WORKSPACE, "workspace is NULL");
+  if (!(1 <= k && k <= d_sel && d_sel <= c->d_store))
+    return fail(AQUA_ERR_SHAPE, "need 1 <= k (%d) <= d_sel (%d) <= d_store (%d)", k, d_sel,
+                c->d_store);
+  if (static_cast<int64_t>(c->len) + 1 > c->T_cap)
+    return fail(AQUA_ERR_CAPACITY, "append at len=%d exceeds T_cap=%d", c->len, c->T_cap);
+  if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(P) ||
+      !aligned16(out) || !aligned16(ws) || (mass && !aligned16(mass)) ||
+      (q_proj_out && !aligned16(q_proj_out)) || (mask_out && !aligned16(mask_out)))
+    return fail(AQUA_ERR_ALIGN, "all buffers must be 16-byte aligned");
+  const size_t need =
+      aqua::decode_workspace_bytes(c->dtype, c->B, Hq, c->Hkv, c->d_head, c->T_cap);
+  if (ws_bytes < need)
+    return fail(AQUA_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, need);
+
+  const aqua::DecodeLayout L = aqua::decode_layout(c->dtype, Hq / c->Hkv);
+  aqua::DecodeArgs a{};
+  a.kp = c->kp;
+  a.v = c->v;
+  a.kp_w = c->kp;
+  a.v_w = c->v;
+  a.mass = mass;
+  a.out = out;
+  aqua::decode_workspace_carve(ws, c->dtype, c->B, Hq, c->Hkv, c->d_head, c->T_cap,
+                               &a.counters, &a.partials, &a.scores);
+  a.B = c->B;
+  a.Hq = Hq;
+  a.Hkv = c->Hkv;
+  a.d = c->d_head;
+  a.d_store = c->d_store;
+  a.T_cap = c->T_cap;
+  a.len = c->len + 1;
+  a.S = (a.len + L.split - 1) / L.split;
+  a.qscale = scale * 1.4426950408889634f;
+  a.q_raw = q;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.P = P;
+  a.q_proj_out = q_proj_out;
+  a.mask_out = mask_out;
+  a.d_sel = d_sel;
+  a.k = k;
+  if (aqua_status st = hip_status(
+          aqua::launch_decode_step(c->dtype, a, static_cast<hipStream_t>(stream)),
+          "aqua_decode_step launch"))
+    return st;
+  c->len += 1;
+  return AQUA_OK;
 }
 
 aqua_status aqua_prefill_workspace(const aqua_cache *c, int32_t Hq, int32_t Lq, size_t *bytes) {

@@ -50,6 +50,64 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Top-k of one row of D = 64 * E values held by a wavefront, lane l holding dims l + 64 e.
+// Magnitudes are compared exactly, as the fp32 bit patterns with the sign cleared (+0 and -0
+// tie, denormals are not flushed); equal magnitudes go to the lower index.  MSB-first radix
+// select with wave ballots: at each bit the candidates with the bit set are either all kept
+// (when they do not exceed the number still needed) or become the only candidates; it stops as
+// soon as the candidates left are exactly the number still needed, and whatever ties after the
+// last bit is filled in index order (mbcnt prefix).  Exactly k flags are set, all at dims
+// < d_sel (callers guarantee 1 <= k <= d_sel <= D).
+template <int E>
+__device__ __forceinline__ void wave_topk(const float (&x)[E], int d_sel, int k, bool (&sel)[E]) {
+  const int lane = threadIdx.x & 63;
+  uint32_t u[E];
+  bool cand[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    u[e] = __float_as_uint(x[e]) & 0x7fffffffu;
+    cand[e] = (lane + 64 * e) < d_sel;
+    sel[e] = false;
+  }
+  int need = k;
+  for (int bit = 30; bit >= 0; --bit) {
+    bool hi[E];
+    int cnt = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      hi[e] = cand[e] && ((u[e] >> bit) & 1u);
+      cnt += __popcll(__ballot(hi[e]));
+    }
+    if (cnt <= need) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        sel[e] = sel[e] || hi[e];
+        cand[e] = cand[e] && !hi[e];
+      }
+      need -= cnt;
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) cand[e] = hi[e];
+    }
+    int left = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) left += __popcll(__ballot(cand[e]));
+    if (left <= need || need == 0) break;
+  }
+  if (need > 0) {
+    int before = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const uint64_t b = __ballot(cand[e]);
+      const int rank = before + static_cast<int>(__builtin_amdgcn_mbcnt_hi(
+                                    static_cast<uint32_t>(b >> 32),
+                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(b), 0u)));
+      if (cand[e] && rank < need) sel[e] = true;
+      before += __popcll(b);
+    }
+  }
+}
+
 // ------------------------------------------------------------------ launch parameter blocks
 struct DecodeArgs {
   const void *kp;        // [B][Hkv][d_store][T_cap]
@@ -64,6 +122,15 @@ struct DecodeArgs {
   int B, Hq, Hkv, d, d_store, T_cap, len;
   int S;                 // splits per (b, g)
   float qscale;          // scale * log2(e)
+  // fused decode step only: raw queries and the new token, selection parameters
+  const void *q_raw;     // [B][Hq][d]
+  const void *k_new;     // [B][Hkv][d]
+  const void *v_new;     // [B][Hkv][d]
+  const float *P;        // [d][d]
+  float *q_proj_out;     // [B][Hq][d] or nullptr
+  uint32_t *mask_out;    // [B][Hq][d/32] or nullptr
+  void *kp_w, *v_w;      // the cache, written at column len - 1
+  int d_sel, k;
 };
 
 struct DecodeLayout {
@@ -84,6 +151,7 @@ hipError_t launch_project_keys(int dtype, const void *k_raw, const void *v_raw, 
                                int B, int Hkv, int n, int d, int d_store, int T_cap, int len0,
                                const int32_t *slots, void *kp, void *v, hipStream_t s);
 hipError_t launch_decode(int dtype, const DecodeArgs &a, hipStream_t s);
+hipError_t launch_decode_step(int dtype, const DecodeArgs &a, hipStream_t s);
 hipError_t launch_h2o_victim(float *mass, int32_t *slot_pos, int B, int Hkv, int n_slots,
                              int t_new, int recent, int32_t *victim, hipStream_t s);
 

@@ -7,8 +7,10 @@
 //  * The G query heads of a KV group each keep their own dims; the workgroup reads the K' rows
 //    of the union U of those masks, once, and every head uses its own masked q' (zero on dims it
 //    did not keep).  K' is dimension-major, so each selected row is a contiguous run of tokens:
-//    lane l reads 16 bytes (8 bf16 / 4 fp32 tokens) of a row, a wavefront 1 KiB, fully coalesced;
-//    rows outside U are never touched.
+//    lane l reads 16 bytes (8 bf16 / 4 fp32 tokens) of a row, a wavefront 1 KiB, fully coalesced,
+//    non-temporal; rows outside U are never touched.  Loads are issued a batch ahead of the
+//    arithmetic (ping-pong registers), and each workgroup starts its walk over U at its own
+//    offset so that concurrent workgroups spread over the HBM channels.
 //  * Each wavefront owns a contiguous run of 64 * 16/sizeof(elem) tokens and computes all of
 //    its scores before any exponential, so there is no running rescale inside a wavefront.
 //    Scores live in log2 units (q' pre-multiplied by scale * log2 e) and use v_exp_f32.
@@ -19,6 +21,11 @@
 //    workspace) merges all partials of the group, writes the output and resets its counter.
 //  * H2O mass mode additionally stores the raw scores and lets that last workgroup add every
 //    token's normalised probability, summed over the group's heads, to its mass.
+//
+// The fused decode step (FUSED) does a whole step in this one launch: each workgroup stages P in
+// LDS, projects its group's raw queries (and, in the workgroup that holds the new position, the
+// new key), selects every head's top-k dims with wave_topk, appends the new token's K' and V to
+// the cache, and attends over the cached tokens plus the new one, taken from LDS.
 #include "aqua_internal.h"
 
 namespace aqua {
@@ -49,42 +56,173 @@ __device__ __forceinline__ uint4 load16(const void *p) {
   const u32x4 r = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
   return make_uint4(r.x, r.y, r.z, r.w);
 }
+// Cross-workgroup hand-off without cache-wide fences.  Partials and scores are written and read
+// with system-scope relaxed atomics (sc0 sc1: written through / read past every non-coherent
+// cache level); the writer drains its stores (s_waitcnt) before the workgroup barrier that
+// precedes the counter increment, and the reader issues its loads only after the counter RMW
+// has told it that it is last.  An agent-scope fence here would instead write back and
+// invalidate the whole L2 of the XCD once per workgroup, which stalls every streaming load.
+__device__ __forceinline__ void publish(float *p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
 __device__ __forceinline__ float coherent_load(const float *p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
-template <typename KT, int D, int G, int NW>
+template <typename KT, int D, int G, int NW, bool FUSED>
+struct DecodeSmem {
+  static constexpr int TPL = Vec<KT>::N;
+  static constexpr int WT = 64 * TPL;
+  static constexpr int NWORD = D / 32;
+  // prologue region (fused only): P and the raw rows (G queries + the new key)
+  static constexpr int PRO = FUSED ? (D * D + (G + 1) * D) * 4 : 0;
+  // main region: softmax numerators [wave][token][head], reused for the wave merge
+  static constexpr int MAIN = NW * WT * G * 4;
+  static constexpr int BIG = PRO > MAIN ? PRO : MAIN;
+  // persistent small arrays
+  static constexpr int OFF_DL = BIG;                                     // int   [D]
+  static constexpr int OFF_QW = OFF_DL + D * 4;                          // float [D][G]
+  static constexpr int OFF_QP = OFF_QW + D * G * 4;                      // float [G+1][D]
+  static constexpr int OFF_MW = OFF_QP + (FUSED ? (G + 1) * D * 4 : 0);  // uint  [G][NWORD]
+  static constexpr int OFF_KN = OFF_MW + G * NWORD * 4;                  // float [D] new K'
+  static constexpr int OFF_VN = OFF_KN + (FUSED ? D * 4 : 0);            // float [D] new V
+  static constexpr int OFF_WM = OFF_VN + (FUSED ? D * 4 : 0);            // float [NW][G]
+  static constexpr int OFF_WL = OFF_WM + NW * G * 4;                     // float [NW][G]
+  static constexpr int OFF_ML = OFF_WL + NW * G * 4;                     // float [2][G]
+  static constexpr int BYTES = OFF_ML + 2 * G * 4 + 16;
+};
+
+template <typename KT, int D, int G, int NW, bool FUSED>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
-  constexpr int TPL = Vec<KT>::N;  // tokens per lane per K' row load
-  constexpr int WT = 64 * TPL;     // tokens per wavefront
+  using SM = DecodeSmem<KT, D, G, NW, FUSED>;
+  constexpr int TPL = SM::TPL;     // tokens per lane per K' row load
+  constexpr int WT = SM::WT;       // tokens per wavefront
   constexpr int EPL = Vec<KT>::N;  // V elements per lane per load
   constexpr int LPT = D / EPL;     // lanes per V row
   constexpr int TPI = 64 / LPT;    // V rows per wavefront load
-  constexpr int NWORD = D / 32;
+  constexpr int NWORD = SM::NWORD;
   constexpr int NT = NW * 64;
+  constexpr int E = D / 64;        // dims per lane in wave_topk
+  constexpr int SPLIT = NW * WT;   // tokens per workgroup
   static_assert(WT % (TPI * kUnroll) == 0, "V loop tiling");
-  static_assert(NW * G * D <= NW * WT * G, "LDS reuse");
+  static_assert(D <= WT, "LDS reuse of the numerator buffer for the wave merge");
 
-  __shared__ int s_dl[D];
-  __shared__ float s_qw[D][G];
-  __shared__ float s_p[NW * WT * G];  // [wave][token][head]; reused for the wave merge
-  __shared__ float s_wm[NW][G], s_wl[NW][G];
-  __shared__ float s_M[G], s_L[G];
+  __shared__ __align__(16) unsigned char smem[SM::BYTES];
+  int *s_dl = reinterpret_cast<int *>(smem + SM::OFF_DL);
+  float(*s_qw)[G] = reinterpret_cast<float(*)[G]>(smem + SM::OFF_QW);
+  float(*s_qp)[D] = reinterpret_cast<float(*)[D]>(smem + SM::OFF_QP);
+  uint32_t(*s_mw)[NWORD] = reinterpret_cast<uint32_t(*)[NWORD]>(smem + SM::OFF_MW);
+  float *s_knew = reinterpret_cast<float *>(smem + SM::OFF_KN);
+  float *s_vnew = reinterpret_cast<float *>(smem + SM::OFF_VN);
+  float(*s_wm)[G] = reinterpret_cast<float(*)[G]>(smem + SM::OFF_WM);
+  float(*s_wl)[G] = reinterpret_cast<float(*)[G]>(smem + SM::OFF_WL);
+  float *s_M = reinterpret_cast<float *>(smem + SM::OFF_ML);
+  float *s_L = s_M + G;
   __shared__ int s_last;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int bg = blockIdx.x / a.S, split = blockIdx.x - bg * a.S;
   const int b = bg / a.Hkv, g = bg - b * a.Hkv;
   const size_t head0 = static_cast<size_t>(b) * a.Hq + static_cast<size_t>(g) * G;
+  // Fused: the cache holds len - 1 tokens, the new one is position len - 1.
+  const int len_c = FUSED ? a.len - 1 : a.len;
+  const bool owner = FUSED && split == (a.len - 1) / SPLIT;
+
+  // ---- fused prologue: project the group's queries (and the new key), select their dims
+  if constexpr (FUSED) {
+    float *sP = reinterpret_cast<float *>(smem);
+    float(*sq)[D] = reinterpret_cast<float(*)[D]>(smem + D * D * 4);
+    {
+      // P into LDS in chunks of CH 16-byte loads per thread (each chunk one L2 round trip)
+      constexpr int NV = D * D / (NT * 4);
+      constexpr int CH = NV < 4 ? NV : 4;
+#pragma unroll
+      for (int v0 = 0; v0 < NV; v0 += CH) {
+        float4 st[CH];
+#pragma unroll
+        for (int v = 0; v < CH; ++v)
+          st[v] = *reinterpret_cast<const float4 *>(&a.P[((v0 + v) * NT + tid) * 4]);
+#pragma unroll
+        for (int v = 0; v < CH; ++v)
+          *reinterpret_cast<float4 *>(&sP[((v0 + v) * NT + tid) * 4]) = st[v];
+      }
+    }
+    const KT *qr = static_cast<const KT *>(a.q_raw) + head0 * D;
+    for (int e = tid; e < G * D; e += NT) sq[e / D][e % D] = load_elem<KT>(qr + e);
+    if (owner && tid < D) {
+      const size_t at = static_cast<size_t>(bg) * D + tid;
+      sq[G][tid] = load_elem<KT>(static_cast<const KT *>(a.k_new) + at);
+      s_vnew[tid] = load_elem<KT>(static_cast<const KT *>(a.v_new) + at);
+    }
+    __syncthreads();
+    // q'_h[i] = sum_j q_h[j] P[j][i] (fp32, j ascending); thread -> dim i, rows r0, r0+NT/D, ...
+    // The j loop is fully unrolled and branch-free (rows past the last are computed on a
+    // clamped row and discarded), so the LDS reads of later j are issued ahead of the fmas.
+    {
+      constexpr int RSTEP = NT / D;
+      constexpr int RPT = (G + 1 + RSTEP - 1) / RSTEP;
+      const int nrows = G + (owner ? 1 : 0);
+      const int i = tid % D, r0 = tid / D;
+      float acc[RPT];
+      int row[RPT];
+#pragma unroll
+      for (int r = 0; r < RPT; ++r) {
+        acc[r] = 0.0f;
+        row[r] = min(r0 + r * RSTEP, G);
+      }
+#pragma unroll
+      for (int j = 0; j < D; ++j) {
+        const float p = sP[j * D + i];
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) acc[r] = fmaf(sq[row[r]][j], p, acc[r]);
+      }
+#pragma unroll
+      for (int r = 0; r < RPT; ++r)
+        if (r0 + r * RSTEP < nrows) s_qp[r0 + r * RSTEP][i] = acc[r];
+    }
+    __syncthreads();
+    if (owner && tid < D) {
+      // the new token's K' as it will be stored (rounded once); it reaches the cache only after
+      // this workgroup's K' loads are done (they cover the same 16-byte chunk)
+      const KT kq = store_elem<KT>(s_qp[G][tid]);
+      s_knew[tid] = load_elem<KT>(&kq);
+    }
+    for (int h = w; h < G; h += NW) {
+      float x[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) x[e] = s_qp[h][lane + 64 * e];
+      bool sel[E];
+      wave_topk<E>(x, a.d_sel, a.k, sel);
+      uint64_t sb[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) sb[e] = __ballot(sel[e]);
+      if (lane < NWORD) {
+        const uint64_t bb = (lane >> 1) ? sb[E - 1] : sb[0];
+        const uint32_t word =
+            (lane & 1) ? static_cast<uint32_t>(bb >> 32) : static_cast<uint32_t>(bb);
+        s_mw[h][lane] = word;
+        if (split == 0 && a.mask_out) a.mask_out[(head0 + h) * NWORD + lane] = word;
+      }
+      if (split == 0 && a.q_proj_out) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) a.q_proj_out[(head0 + h) * D + lane + 64 * e] = x[e];
+      }
+    }
+    __syncthreads();
+  }
 
   // ---- union of the group's masks, restricted to stored dims (uniform per workgroup)
+  auto mask_word = [&](int h, int wd) -> uint32_t {
+    if constexpr (FUSED) return s_mw[h][wd];
+    else return a.mask[(head0 + h) * NWORD + wd];
+  };
   uint32_t U[NWORD];
   int nU = 0, last_dim = 0;
 #pragma unroll
   for (int wd = 0; wd < NWORD; ++wd) {
     uint32_t u = 0;
 #pragma unroll
-    for (int h = 0; h < G; ++h) u |= a.mask[(head0 + h) * NWORD + wd];
+    for (int h = 0; h < G; ++h) u |= mask_word(h, wd);
     const int lo = wd * 32;
     if (a.d_store <= lo) u = 0;
     else if (a.d_store < lo + 32) u &= (1u << (a.d_store - lo)) - 1u;
@@ -100,8 +238,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     float qv[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      mw[h] = a.mask[(head0 + h) * NWORD + wd];
-      qv[h] = a.q_proj[(head0 + h) * D + tid];
+      mw[h] = mask_word(h, wd);
+      if constexpr (FUSED) qv[h] = s_qp[h][tid];
+      else qv[h] = a.q_proj[(head0 + h) * D + tid];
     }
     uint32_t uw = 0;
     int pos = 0;
@@ -110,28 +249,35 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
       if (x < wd) pos += __popc(U[x]);
       if (x == wd) uw = U[x];
     }
+    pos += __popc(uw & ((1u << bit) - 1u));
+    // Each workgroup walks the list from its own batch-aligned offset, so that workgroups
+    // running at the same time read different K' rows (rows of one group are T_cap apart, and
+    // a lock-step walk would send every workgroup to the same few HBM channels).
+    const int nb = nUp / kUnroll;
+    const int rot = nb ? ((blockIdx.x * 5) % nb) * kUnroll : 0;
     if ((uw >> bit) & 1u) {
-      pos += __popc(uw & ((1u << bit) - 1u));
-      s_dl[pos] = tid;
+      const int at = (pos + nUp - rot) % nUp;
+      s_dl[at] = tid;
 #pragma unroll
-      for (int h = 0; h < G; ++h) s_qw[pos][h] = ((mw[h] >> bit) & 1u) ? qv[h] * a.qscale : 0.0f;
+      for (int h = 0; h < G; ++h) s_qw[at][h] = ((mw[h] >> bit) & 1u) ? qv[h] * a.qscale : 0.0f;
     }
     if (tid >= nU && tid < nUp) {
-      s_dl[tid] = last_dim;
+      const int at = (tid + nUp - rot) % nUp;
+      s_dl[at] = last_dim;
 #pragma unroll
-      for (int h = 0; h < G; ++h) s_qw[tid][h] = 0.0f;
+      for (int h = 0; h < G; ++h) s_qw[at][h] = 0.0f;
     }
   }
   __syncthreads();
 
-  // ---- phase 1: log2-domain scores of this wavefront's tokens
-  // Lanes past len read the last valid 16-byte chunk instead (same cache line as a live lane);
-  // their scores are discarded below.  Loads are unconditional so that the prefetch of the
-  // next batch overlaps the arithmetic of the current one (vmcnt stays at one batch).
-  const int tw0 = split * (NW * WT) + w * WT;
+  // ---- phase 1: log2-domain scores of this wavefront's cached tokens
+  // Lanes past the cached length read the last valid 16-byte chunk instead (same cache line as
+  // a live lane); their scores are discarded below.  Loads are unconditional so that the
+  // prefetch of the next batch overlaps the arithmetic of the current one.
+  const int tw0 = split * SPLIT + w * WT;
   const int tl = tw0 + lane * TPL;
-  const bool wave_live = tw0 < a.len;
-  const int tl_ld = min(tl, ((a.len - 1) / TPL) * TPL);
+  const bool wave_live = tw0 < len_c;
+  const int tl_ld = len_c > 0 ? min(tl, ((len_c - 1) / TPL) * TPL) : 0;
   const KT *kbase = static_cast<const KT *>(a.kp) +
                     static_cast<size_t>(bg) * a.d_store * a.T_cap + tl_ld;
   float acc[G][TPL];
@@ -140,60 +286,81 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int j = 0; j < TPL; ++j) acc[h][j] = 0.0f;
 
-  auto k_load = [&](uint4 (&buf)[kUnroll], int u) {
-#pragma unroll
-    for (int i = 0; i < kUnroll; ++i)
-      buf[i] = load16(kbase + static_cast<size_t>(s_dl[u + i]) * a.T_cap);
-  };
-  auto k_fma = [&](const uint4 (&buf)[kUnroll], int u) {
-#pragma unroll
-    for (int i = 0; i < kUnroll; ++i) {
-      float kv[TPL];
-      Vec<KT>::unpack(buf[i], kv);
-      float qw[G];
-#pragma unroll
-      for (int h = 0; h < G; ++h) qw[h] = s_qw[u + i][h];
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int j = 0; j < TPL; ++j) acc[h][j] = fmaf(qw[h], kv[j], acc[h][j]);
-    }
-  };
-  if (wave_live && nUp > 0) {
-    uint4 bA[kUnroll], bB[kUnroll];
-    k_load(bA, 0);
-    for (int u = 0;;) {
-      if (u + kUnroll >= nUp) { k_fma(bA, u); break; }
-      k_load(bB, u + kUnroll);
-      k_fma(bA, u);
-      u += kUnroll;
-      if (u + kUnroll >= nUp) { k_fma(bB, u); break; }
-      k_load(bA, u + kUnroll);
-      k_fma(bB, u);
-      u += kUnroll;
+  // Software pipeline over batches of kUnroll rows, two register sets A and B in turn: the
+  // loads of batch i + 1 are issued before the arithmetic of batch i.  Every load is
+  // unconditional (past the end it re-reads the last batch, which hits in cache), so the
+  // wait before each batch's arithmetic is exactly "one batch still in flight"; only the
+  // arithmetic of a missing odd batch is skipped, by a uniform branch.
+#define AQUA_K_LOAD(BUF, BATCH)                                                          \
+  _Pragma("unroll") for (int i = 0; i < kUnroll; ++i) BUF[i] = load16(                   \
+      kbase + static_cast<size_t>(s_dl[min(BATCH, nbat - 1) * kUnroll + i]) * a.T_cap)
+#define AQUA_K_FMA(BUF, BATCH)                                                           \
+  _Pragma("unroll") for (int i = 0; i < kUnroll; ++i) {                                  \
+    float kv[TPL];                                                                        \
+    Vec<KT>::unpack(BUF[i], kv);                                                          \
+    float qw[G];                                                                          \
+    _Pragma("unroll") for (int h = 0; h < G; ++h) qw[h] = s_qw[(BATCH) * kUnroll + i][h]; \
+    _Pragma("unroll") for (int h = 0; h < G; ++h)                                        \
+        _Pragma("unroll") for (int j = 0; j < TPL; ++j) acc[h][j] =                       \
+        fmaf(qw[h], kv[j], acc[h][j]);                                                    \
+  }
+  const int nbat = nUp / kUnroll;
+  if (wave_live && nbat > 0) {
+    uint4 kA[kUnroll], kB[kUnroll];
+    AQUA_K_LOAD(kA, 0);
+    for (int bi = 0; bi < nbat; bi += 2) {
+      AQUA_K_LOAD(kB, bi + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      AQUA_K_FMA(kA, bi);
+      AQUA_K_LOAD(kA, bi + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      if (bi + 1 < nbat) { AQUA_K_FMA(kB, bi + 1); }
     }
   }
+#undef AQUA_K_LOAD
+#undef AQUA_K_FMA
 
   // ---- softmax numerators within the wavefront
 #pragma unroll
   for (int j = 0; j < TPL; ++j)
-    if (tl + j >= a.len)
+    if (tl + j >= len_c)
 #pragma unroll
       for (int h = 0; h < G; ++h) acc[h][j] = -INFINITY;
+  // fused: the new token's score (uniform over the wavefront that owns its position), from its
+  // K' in LDS; it enters the softmax as one more term next to the cached tokens
+  const int off_new = FUSED ? (a.len - 1) - tw0 : -1;
+  const bool new_here = FUSED && owner && off_new >= 0 && off_new < WT;
+  float s_new[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) s_new[h] = -INFINITY;
+  if (new_here) {
+    float part[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) part[h] = 0.0f;
+    for (int u = lane; u < nUp; u += 64) {
+      const float kv = s_knew[s_dl[u]];
+#pragma unroll
+      for (int h = 0; h < G; ++h) part[h] = fmaf(s_qw[u][h], kv, part[h]);
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) s_new[h] = wave_sum(part[h]);
+  }
   if (a.mass) {
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+    for (int h = 0; h < G; ++h) {
 #pragma unroll
       for (int j = 0; j < TPL; ++j)
-        if (tl + j < a.len) a.scores[(head0 + h) * a.T_cap + tl + j] = acc[h][j];
+        if (tl + j < len_c) publish(a.scores + (head0 + h) * a.T_cap + tl + j, acc[h][j]);
+      if (new_here && lane == 0) publish(a.scores + (head0 + h) * a.T_cap + (a.len - 1), s_new[h]);
+    }
   }
-  float m[G], l[G];
+  float m[G], l[G], p_new[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     float mx = acc[h][0];
 #pragma unroll
     for (int j = 1; j < TPL; ++j) mx = fmaxf(mx, acc[h][j]);
-    m[h] = wave_max(mx);
+    m[h] = fmaxf(wave_max(mx), s_new[h]);
     float sum = 0.0f;
 #pragma unroll
     for (int j = 0; j < TPL; ++j) {
@@ -201,19 +368,32 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
       acc[h][j] = p;
       sum += p;
     }
-    l[h] = wave_sum(sum);
+    p_new[h] = new_here ? __builtin_amdgcn_exp2f(s_new[h] - m[h]) : 0.0f;
+    l[h] = wave_sum(sum) + p_new[h];
   }
+  float *s_p = reinterpret_cast<float *>(smem);
   float *sp = s_p + w * (WT * G);
 #pragma unroll
   for (int j = 0; j < TPL; ++j)
 #pragma unroll
     for (int h = 0; h < G; ++h) sp[(lane * TPL + j) * G + h] = acc[h][j];
   __syncthreads();
+  if (owner && tid < D) {
+    // append the new token: every K' load of this workgroup has been consumed by now, and the
+    // V pass below never reads row len - 1 (it takes the new V from LDS)
+    const size_t col = static_cast<size_t>(a.len - 1);
+    if (tid < a.d_store)
+      static_cast<KT *>(a.kp_w)[(static_cast<size_t>(bg) * a.d_store + tid) * a.T_cap + col] =
+          store_elem<KT>(s_knew[tid]);
+    static_cast<KT *>(a.v_w)[(static_cast<size_t>(bg) * a.T_cap + col) * D + tid] =
+        static_cast<const KT *>(a.v_new)[static_cast<size_t>(bg) * D + tid];
+  }
 
-  // ---- phase 2: o = sum_t p_t V_t over this wavefront's tokens
-  // Rows past len read the last valid row (their p is 0), again to keep loads unconditional.
+  // ---- phase 2: o = sum_t p_t V_t over this wavefront's cached tokens
+  // Rows past the cached length read the last valid row (their p is 0), to keep loads
+  // unconditional.
   const int sub = lane / LPT, cl = lane - sub * LPT;
-  const int nrow = min(WT, a.len - tw0);  // may be <= 0
+  const int nrow = min(WT, len_c - tw0);  // may be <= 0
   const KT *vbase = static_cast<const KT *>(a.v) +
                     (static_cast<size_t>(bg) * a.T_cap + tw0) * D + cl * EPL;
   float o[G][EPL];
@@ -222,41 +402,40 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int e = 0; e < EPL; ++e) o[h][e] = 0.0f;
   constexpr int RB = TPI * kUnroll;  // rows per batch
-  auto v_load = [&](uint4 (&buf)[kUnroll], int r0) {
-#pragma unroll
-    for (int i = 0; i < kUnroll; ++i) {
-      const int t = min(r0 + i * TPI + sub, nrow - 1);
-      buf[i] = load16(vbase + static_cast<size_t>(t) * D);
+  // same pipeline over batches of RB rows
+#define AQUA_V_LOAD(BUF, BATCH)                                                          \
+  _Pragma("unroll") for (int i = 0; i < kUnroll; ++i) BUF[i] = load16(                   \
+      vbase + static_cast<size_t>(min(min(BATCH, vbat - 1) * RB + i * TPI + sub, nrow - 1)) * D)
+#define AQUA_V_FMA(BUF, BATCH)                                                           \
+  _Pragma("unroll") for (int i = 0; i < kUnroll; ++i) {                                  \
+    const int t = (BATCH) * RB + i * TPI + sub;                                           \
+    float vv[EPL];                                                                        \
+    Vec<KT>::unpack(BUF[i], vv);                                                          \
+    float p[G];                                                                           \
+    _Pragma("unroll") for (int h = 0; h < G; ++h) p[h] = sp[t * G + h];                 \
+    _Pragma("unroll") for (int h = 0; h < G; ++h)                                        \
+        _Pragma("unroll") for (int e = 0; e < EPL; ++e) o[h][e] = fmaf(p[h], vv[e], o[h][e]); \
+  }
+  const int vbat = nrow > 0 ? (nrow + RB - 1) / RB : 0;
+  if (vbat > 0) {
+    uint4 vA[kUnroll], vB[kUnroll];
+    AQUA_V_LOAD(vA, 0);
+    for (int bi = 0; bi < vbat; bi += 2) {
+      AQUA_V_LOAD(vB, bi + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      AQUA_V_FMA(vA, bi);
+      AQUA_V_LOAD(vA, bi + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      if (bi + 1 < vbat) { AQUA_V_FMA(vB, bi + 1); }
     }
-  };
-  auto v_fma = [&](const uint4 (&buf)[kUnroll], int r0) {
+  }
+#undef AQUA_V_LOAD
+#undef AQUA_V_FMA
+  if (new_here && sub == 0) {
 #pragma unroll
-    for (int i = 0; i < kUnroll; ++i) {
-      const int t = r0 + i * TPI + sub;
-      float vv[EPL];
-      Vec<KT>::unpack(buf[i], vv);
-      float p[G];
+    for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int h = 0; h < G; ++h) p[h] = sp[t * G + h];
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) o[h][e] = fmaf(p[h], vv[e], o[h][e]);
-    }
-  };
-  if (nrow > 0) {
-    uint4 bA[kUnroll], bB[kUnroll];
-    v_load(bA, 0);
-    for (int r0 = 0;;) {
-      if (r0 + RB >= nrow) { v_fma(bA, r0); break; }
-      v_load(bB, r0 + RB);
-      v_fma(bA, r0);
-      r0 += RB;
-      if (r0 + RB >= nrow) { v_fma(bB, r0); break; }
-      v_load(bA, r0 + RB);
-      v_fma(bB, r0);
-      r0 += RB;
-    }
+      for (int e = 0; e < EPL; ++e) o[h][e] = fmaf(p_new[h], s_vnew[cl * EPL + e], o[h][e]);
   }
 #pragma unroll
   for (int off = LPT; off < 64; off <<= 1)
@@ -264,7 +443,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     for (int h = 0; h < G; ++h)
 #pragma unroll
       for (int e = 0; e < EPL; ++e) o[h][e] += __shfl_xor(o[h][e], off, 64);
-  __syncthreads();  // every wavefront is done with s_p
+  __syncthreads();  // every wavefront is done with the numerators
 
   // ---- merge the workgroup's wavefronts, write this split's partials
   float *so = s_p;  // [wave][head][D]
@@ -297,19 +476,18 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     }
     float *part = a.partials + ((head0 + h) * a.S + split) * (D + 2);
     if (dd == 0) {
-      part[0] = M;
-      part[1] = L;
+      publish(part + 0, M);
+      publish(part + 1, L);
     }
-    part[2 + dd] = O;
+    publish(part + 2 + dd, O);
   }
 
   // ---- the last workgroup of this (b, g) merges all splits
-  __threadfence();
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's partials and scores have landed
   __syncthreads();
   if (tid == 0) s_last = (atomicAdd(&a.counters[bg], 1u) == static_cast<unsigned>(a.S - 1));
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
 
   for (int e = tid; e < G * D; e += NT) {
     const int h = e / D, dd = e - h * D;
@@ -344,21 +522,21 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   if (tid == 0) atomicExch(&a.counters[bg], 0u);
 }
 
-template <typename KT, int D, int G>
+template <typename KT, int D, int G, bool FUSED>
 hipError_t launch_g(const DecodeArgs &a, hipStream_t s) {
   constexpr int NW = (G == 8) ? 2 : 4;
   const dim3 grid(a.B * a.Hkv * a.S), block(NW * 64);
-  decode_kernel<KT, D, G, NW><<<grid, block, 0, s>>>(a);
+  decode_kernel<KT, D, G, NW, FUSED><<<grid, block, 0, s>>>(a);
   return hipGetLastError();
 }
 
-template <typename KT, int D>
+template <typename KT, int D, bool FUSED>
 hipError_t launch_d(const DecodeArgs &a, hipStream_t s) {
   switch (a.Hq / a.Hkv) {
-    case 1: return launch_g<KT, D, 1>(a, s);
-    case 2: return launch_g<KT, D, 2>(a, s);
-    case 4: return launch_g<KT, D, 4>(a, s);
-    default: return launch_g<KT, D, 8>(a, s);
+    case 1: return launch_g<KT, D, 1, FUSED>(a, s);
+    case 2: return launch_g<KT, D, 2, FUSED>(a, s);
+    case 4: return launch_g<KT, D, 4, FUSED>(a, s);
+    default: return launch_g<KT, D, 8, FUSED>(a, s);
   }
 }
 
@@ -395,8 +573,15 @@ void decode_workspace_carve(void *ws, int dtype, int B, int Hq, int Hkv, int d, 
 }
 
 hipError_t launch_decode(int dtype, const DecodeArgs &a, hipStream_t s) {
-  if (dtype == 1) return a.d == 128 ? launch_d<bf16_t, 128>(a, s) : launch_d<bf16_t, 64>(a, s);
-  return a.d == 128 ? launch_d<float, 128>(a, s) : launch_d<float, 64>(a, s);
+  if (dtype == 1)
+    return a.d == 128 ? launch_d<bf16_t, 128, false>(a, s) : launch_d<bf16_t, 64, false>(a, s);
+  return a.d == 128 ? launch_d<float, 128, false>(a, s) : launch_d<float, 64, false>(a, s);
+}
+
+hipError_t launch_decode_step(int dtype, const DecodeArgs &a, hipStream_t s) {
+  if (dtype == 1)
+    return a.d == 128 ? launch_d<bf16_t, 128, true>(a, s) : launch_d<bf16_t, 64, true>(a, s);
+  return a.d == 128 ? launch_d<float, 128, true>(a, s) : launch_d<float, 64, true>(a, s);
 }
 
 }  // namespace aqua

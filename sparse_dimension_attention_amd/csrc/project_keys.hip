@@ -93,11 +93,69 @@ __global__ __launch_bounds__(256) void project_keys_kernel(
   }
 }
 
+// Few tokens per (b, g), as in a decode step: one workgroup of 256 threads per (b, g) stages
+// P in LDS with 16-byte loads (all in flight at once: one L2 round trip), then thread i < D
+// owns projected dimension i of every token (P's row j read from LDS, consecutive banks).
+constexpr int kSmallN = 8;
+
+template <typename KT, int D>
+__global__ __launch_bounds__(256) void project_keys_small_kernel(
+    const KT *__restrict__ k_raw, const KT *__restrict__ v_raw, const float *__restrict__ P,
+    int n, int d_store, int T_cap, int len0, const int32_t *__restrict__ slots,
+    KT *__restrict__ kp, KT *__restrict__ vc) {
+  __shared__ float sP[D * D];
+  __shared__ float ks[kSmallN][D];
+  __shared__ int cols[kSmallN];
+  const int bg = blockIdx.x, tid = threadIdx.x;
+  {
+    constexpr int NV = D * D / (256 * 4);
+    float4 st[NV];
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+      st[v] = *reinterpret_cast<const float4 *>(&P[(v * 256 + tid) * 4]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int v = 0; v < NV; ++v) *reinterpret_cast<float4 *>(&sP[(v * 256 + tid) * 4]) = st[v];
+  }
+  for (int e = tid; e < n * D; e += 256)
+    ks[e / D][e % D] = load_elem<KT>(k_raw + static_cast<size_t>(bg) * n * D + e);
+  if (tid < n) {
+    const int col = slots ? slots[static_cast<size_t>(bg) * n + tid] : len0 + tid;
+    cols[tid] = (col >= 0 && col < T_cap) ? col : -1;
+  }
+  __syncthreads();
+  if (tid < D) {
+    // one fully unrolled, branch-free j chain per token: the LDS reads are issued ahead
+    const int i = tid;
+    for (int t = 0; t < n; ++t) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int j = 0; j < D; ++j) acc = fmaf(ks[t][j], sP[j * D + i], acc);
+      if (i < d_store && cols[t] >= 0)
+        kp[(static_cast<size_t>(bg) * d_store + i) * T_cap + cols[t]] = store_elem<KT>(acc);
+    }
+  }
+  if (v_raw) {
+    for (int e = tid; e < n * D; e += 256) {
+      const int t = e / D;
+      if (cols[t] >= 0)
+        vc[(static_cast<size_t>(bg) * T_cap + cols[t]) * D + e % D] =
+            v_raw[static_cast<size_t>(bg) * n * D + e];
+    }
+  }
+}
+
 template <typename KT, int D>
 hipError_t launch_pk(const void *k_raw, const void *v_raw, const float *P, int B, int Hkv, int n,
                      int d_store, int T_cap, int len0, const int32_t *slots, void *kp, void *v,
                      hipStream_t s) {
   using C = ProjCfg<KT, D>;
+  if (n <= kSmallN) {
+    project_keys_small_kernel<KT, D><<<dim3(B * Hkv), dim3(256), 0, s>>>(
+        static_cast<const KT *>(k_raw), static_cast<const KT *>(v_raw), P, n, d_store, T_cap,
+        len0, slots, static_cast<KT *>(kp), static_cast<KT *>(v));
+    return hipGetLastError();
+  }
   const dim3 grid((n + C::TT - 1) / C::TT, B * Hkv), block(256);
   project_keys_kernel<KT, D><<<grid, block, 0, s>>>(
       static_cast<const KT *>(k_raw), static_cast<const KT *>(v_raw), P, n, d_store, T_cap, len0,

@@ -7,15 +7,12 @@
 // word pair of dims 0..63 (and 64..127).
 //
 // Projection: q'_i = sum_j q_j P[j][i] in fp32, j ascending (fma chain); q_j is broadcast from
-// its owner lane with v_readlane, P rows are read coalesced (each row is 256/512 contiguous
-// bytes across the wave; P stays resident in L2).
+// its owner lane with v_readlane.  The workgroup first stages all of P in LDS with 16-byte
+// loads (one round trip to L2 instead of one per row j), then each wavefront reads P's rows
+// from LDS (consecutive lanes, consecutive banks).
 //
-// Selection: magnitudes are compared as integers, the fp32 bit pattern with the sign cleared,
-// which orders finite values exactly (no flush of denormals, +0 == -0).  MSB-first radix select
-// over bits 30..0 with wave ballots: at each bit, the candidates with the bit set are either all
-// kept (if they do not exceed the number still needed) or become the only candidates.  The
-// loop stops as soon as the candidates left are exactly the number still needed.  Whatever
-// remains after bit 0 ties exactly; the lowest indices among them are kept (mbcnt prefix).
+// Selection: wave_topk (exact comparison of sign-cleared fp32 bit patterns, ties to the lower
+// index, wave-ballot radix select).
 #include "aqua_internal.h"
 
 namespace aqua {
@@ -28,6 +25,18 @@ __global__ __launch_bounds__(256) void select_kernel(const QT *__restrict__ q, i
                                                      uint32_t *__restrict__ mask,
                                                      int16_t *__restrict__ idx) {
   constexpr int E = D / 64;  // dims per lane: lane, lane + 64
+  __shared__ float sP[D * D];
+  {
+    constexpr int NV = D * D / (256 * 4);  // float4 per thread; all in flight at once
+    float4 st[NV];
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+      st[v] = *reinterpret_cast<const float4 *>(&P[(v * 256 + threadIdx.x) * 4]);
+    __builtin_amdgcn_sched_barrier(0);  // all loads in flight before the first LDS store
+#pragma unroll
+    for (int v = 0; v < NV; ++v) *reinterpret_cast<float4 *>(&sP[(v * 256 + threadIdx.x) * 4]) = st[v];
+  }
+  __syncthreads();
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= N) return;  // whole wave leaves; no workgroup barrier follows
@@ -40,61 +49,16 @@ __global__ __launch_bounds__(256) void select_kernel(const QT *__restrict__ q, i
   float acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.0f;
-#pragma unroll 8
+#pragma unroll
   for (int j = 0; j < D; ++j) {
     const float src = (j < 64) ? qv[0] : qv[E - 1];
     const float qj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(src), j & 63));
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] = fmaf(qj, P[j * D + lane + 64 * e], acc[e]);
+    for (int e = 0; e < E; ++e) acc[e] = fmaf(qj, sP[j * D + lane + 64 * e], acc[e]);
   }
 
-  // ---- selection on sign-cleared bit patterns
-  uint32_t u[E];
-  bool cand[E], sel[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    u[e] = __float_as_uint(acc[e]) & 0x7fffffffu;
-    cand[e] = (lane + 64 * e) < d_sel;
-    sel[e] = false;
-  }
-  int need = k;
-  for (int bit = 30; bit >= 0; --bit) {
-    bool hi[E];
-    int cnt = 0;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      hi[e] = cand[e] && ((u[e] >> bit) & 1u);
-      cnt += __popcll(__ballot(hi[e]));
-    }
-    if (cnt <= need) {
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        sel[e] = sel[e] || hi[e];
-        cand[e] = cand[e] && !hi[e];
-      }
-      need -= cnt;
-    } else {
-#pragma unroll
-      for (int e = 0; e < E; ++e) cand[e] = hi[e];
-    }
-    int left = 0;
-#pragma unroll
-    for (int e = 0; e < E; ++e) left += __popcll(__ballot(cand[e]));
-    if (left <= need || need == 0) break;
-  }
-  // remaining candidates tie exactly (or number exactly `need`): keep the lowest indices
-  if (need > 0) {
-    int before = 0;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const uint64_t b = __ballot(cand[e]);
-      const int rank = before + __builtin_amdgcn_mbcnt_hi(
-                                    static_cast<uint32_t>(b >> 32),
-                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(b), 0u));
-      if (cand[e] && rank < need) sel[e] = true;
-      before += __popcll(b);
-    }
-  }
+  bool sel[E];
+  wave_topk<E>(acc, d_sel, k, sel);
 
   // ---- outputs
   uint64_t sb[E];

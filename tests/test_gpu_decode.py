@@ -77,6 +77,25 @@ def test_decode_deterministic_and_reusable_workspace():
     assert int(ws[:n].count_nonzero()) == 0
 
 
+def test_decode_workspace_reuse_across_inputs():
+    """Calls that share one workspace but attend different queries and contexts, alternating:
+    each output must match a fresh single call (no stale partials, counters reset)."""
+    c = config(2, B=2, Hq=8, Hkv=2, T=6000)
+    runs = []
+    for seed_cfg in (2, 4):
+        cc = dict(c, id=seed_cfg)
+        inp = make_decode_inputs(cc)
+        runs.append(run_decode(inp, cc))
+    ws = torch.zeros_like(runs[0]["ws"])
+    scale = 1 / math.sqrt(c["d"])
+    for it in range(6):
+        r = runs[it % 2]
+        out = torch.full_like(r["out"], float("nan"))
+        aq.aqua_decode(r["cache"], c["Hq"], r["qp"], r["mask"], scale, out, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(out, r["out"]), f"call {it}"
+
+
 def test_decode_llama8b_full_size_sampled():
     """B=16, Hq=32, Hkv=8, T=8192, k=96 (the benchmark workload): every mask checked, outputs
     of a sample of heads checked against the oracle one by one."""

@@ -1,0 +1,137 @@
+"""GPU parity of the fused aqua_decode_step (append + select + decode in one launch)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import sparse_dimension_attention_amd as aq
+from gpu_util import DEV, assert_close, new_cache, oracle_decode, unpack_mask
+from oracle import aqua_oracle as O
+from synth import config, make_decode_inputs, storage_to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _step(inp, c, T, T_cap=None, mass=None, d_store=None, d_sel=None):
+    """Cache holds tokens [0, T-1); the step appends token T-1 and attends [0, T)."""
+    B, Hq, Hkv, d, k = c["B"], c["Hq"], c["Hkv"], c["d"], c["k"]
+    d_store = d_store or c.get("d_store", d)
+    d_sel = d_sel or c.get("d_sel", d)
+    T_cap = T_cap or ((T + 63) // 64 * 64)
+    kp, v = new_cache(B, Hkv, d, d_store, T_cap, c["dtype"])
+    cache = aq.make_cache(kp, v, 0)
+    P = inp["P"].to(DEV)
+    if T > 1:
+        aq.aqua_project_keys(cache, inp["k"][:, :, :T - 1].contiguous().to(DEV),
+                             inp["v"][:, :, :T - 1].contiguous().to(DEV), P, T - 1)
+    ws = torch.zeros(aq.aqua_decode_workspace(cache, Hq), dtype=torch.uint8, device=DEV)
+    out = torch.full((B, Hq, d), float("nan"), device=DEV)
+    qp = torch.full((B, Hq, d), float("nan"), device=DEV)
+    mask = torch.full((B, Hq, d // 32), -1, dtype=torch.int32, device=DEV)
+    aq.aqua_decode_step(cache, Hq, inp["q"].to(DEV), inp["k"][:, :, T - 1].contiguous().to(DEV),
+                        inp["v"][:, :, T - 1].contiguous().to(DEV), P, d_sel, k,
+                        1 / math.sqrt(d), out, ws, mass=mass, q_proj_out=qp, mask_out=mask)
+    torch.cuda.synchronize()
+    assert cache.len == T
+    return dict(out=out, qp=qp, mask=mask, kp=kp, v=v, ws=ws, cache=cache, P=P)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,T,k,d,dtype", [
+    (2, 8, 2, 3000, 96, 128, "bf16"),
+    (2, 8, 2, 2049, 96, 128, "bf16"),   # the new token opens a new split
+    (1, 8, 2, 2048, 64, 128, "bf16"),   # the new token closes a split
+    (1, 8, 2, 1, 96, 128, "bf16"),      # empty cache: the new token alone
+    (2, 4, 4, 700, 48, 128, "bf16"),    # G = 1
+    (1, 16, 2, 1000, 32, 128, "bf16"),  # G = 8
+    (1, 4, 2, 1500, 100, 128, "f32"),
+    (1, 1, 1, 256, 48, 64, "f32"),      # the tiny fp32 shape
+])
+def test_step_matches_oracle(B, Hq, Hkv, T, k, d, dtype):
+    c = config(2 if dtype == "bf16" else 1, B=B, Hq=Hq, Hkv=Hkv, T=T, k=k, d=d, d_store=d,
+               d_sel=d, dtype=dtype)
+    inp = make_decode_inputs(c)
+    r = _step(inp, c, T)
+    m = unpack_mask(r["mask"], d)
+    assert np.array_equal(m, O.select(r["qp"].cpu().double().numpy(), d, k))
+    ref = oracle_decode(inp, c, m)
+    assert_close(r["out"].cpu().double().numpy(), ref, dtype, "decode step")
+    # the new token's K' and V are in the cache
+    P64 = storage_to_f64(inp["P"])
+    kn = O.project_keys_stored(storage_to_f64(inp["k"][:, :, T - 1]), P64, dtype, d)
+    got = storage_to_f64(r["kp"])[:, :, :, T - 1]
+    ulp = np.abs(kn) * (2.0 ** -7 if dtype == "bf16" else 2.0 ** -23)
+    acc = d * 2.0 ** -24 * (np.abs(storage_to_f64(inp["k"][:, :, T - 1])) @ np.abs(P64))
+    assert np.all(np.abs(got - kn) <= ulp + acc)
+    assert np.array_equal(storage_to_f64(r["v"])[:, :, T - 1], storage_to_f64(inp["v"][:, :, T - 1]))
+
+
+def test_step_equals_separate_calls():
+    """q', masks and the cache are bit-identical to project + select + decode; outputs agree to
+    fp32 summation order."""
+    c = config(2, B=4, Hq=32, Hkv=8, T=5000)
+    inp = make_decode_inputs(c)
+    T, d, k, B, Hq = c["T"], c["d"], c["k"], c["B"], c["Hq"]
+    r = _step(inp, c, T)
+    kp, v = new_cache(B, c["Hkv"], d, d, r["kp"].shape[-1], "bf16")
+    cache = aq.make_cache(kp, v, 0)
+    P = r["P"]
+    aq.aqua_project_keys(cache, inp["k"].to(DEV), inp["v"].to(DEV), P, T)
+    qp = torch.empty(B * Hq, d, device=DEV)
+    mask = torch.empty(B * Hq, d // 32, dtype=torch.int32, device=DEV)
+    aq.aqua_select_dims(inp["q"].reshape(B * Hq, d).to(DEV), P, d, k, qp, mask)
+    ws = torch.zeros_like(r["ws"])
+    out = torch.empty_like(r["out"])
+    aq.aqua_decode(cache, Hq, qp, mask, 1 / math.sqrt(d), out, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(qp.reshape(B, Hq, d), r["qp"])
+    assert torch.equal(mask.reshape(B, Hq, d // 32), r["mask"])
+    assert torch.equal(kp[..., :T], r["kp"][..., :T])
+    assert torch.equal(v[:, :, :T], r["v"][:, :, :T])
+    assert torch.allclose(out, r["out"], rtol=1e-5, atol=1e-7)
+
+
+def test_step_sequence_appends():
+    """Several steps in a row on one cache and workspace: each appends and attends correctly."""
+    c = config(2, B=2, Hq=8, Hkv=2, T=2600)
+    inp = make_decode_inputs(c)
+    B, Hq, d, k = c["B"], c["Hq"], c["d"], c["k"]
+    T0 = 2045
+    kp, v = new_cache(B, c["Hkv"], d, d, 2624, "bf16")
+    cache = aq.make_cache(kp, v, 0)
+    P = inp["P"].to(DEV)
+    aq.aqua_project_keys(cache, inp["k"][:, :, :T0].contiguous().to(DEV),
+                         inp["v"][:, :, :T0].contiguous().to(DEV), P, T0)
+    ws = torch.zeros(aq.aqua_decode_workspace(cache, Hq), dtype=torch.uint8, device=DEV)
+    q = inp["q"].to(DEV)
+    for t in range(T0, T0 + 6):  # crosses the 2048-token split boundary
+        out = torch.full((B, Hq, d), float("nan"), device=DEV)
+        mask = torch.empty(B, Hq, d // 32, dtype=torch.int32, device=DEV)
+        aq.aqua_decode_step(cache, Hq, q, inp["k"][:, :, t].contiguous().to(DEV),
+                            inp["v"][:, :, t].contiguous().to(DEV), P, d, k, 1 / math.sqrt(d),
+                            out, ws, mask_out=mask)
+        torch.cuda.synchronize()
+        assert cache.len == t + 1
+        m = unpack_mask(mask, d)
+        ref = oracle_decode(inp, c, m, length=t + 1)
+        assert_close(out.cpu().double().numpy(), ref, "bf16", f"step at {t}")
+
+
+def test_step_mass_mode():
+    c = config(2, B=1, Hq=8, Hkv=2, T=1280, d_store=96, d_sel=96, k=64)
+    inp = make_decode_inputs(c)
+    mass = torch.zeros(c["B"], c["Hkv"], 1280, device=DEV)
+    r = _step(inp, c, c["T"], T_cap=1280, mass=mass)
+    m = unpack_mask(r["mask"], c["d"])
+    P64 = storage_to_f64(inp["P"])
+    qp64 = O.project(storage_to_f64(inp["q"]), P64)
+    G = c["Hq"] // c["Hkv"]
+    for g in range(c["Hkv"]):
+        Kp = O.project_keys_stored(storage_to_f64(inp["k"][0, g]), P64, "bf16", 96)
+        V = storage_to_f64(inp["v"][0, g])
+        add = np.zeros(c["T"])
+        for h in range(g * G, (g + 1) * G):
+            _, p = O.attend(qp64[0, h], m[0, h], Kp, V, 1 / math.sqrt(c["d"]))
+            add += p
+        got = mass[0, g].cpu().double().numpy()
+        assert np.max(np.abs(got - add)) <= 1e-3 * add.max()

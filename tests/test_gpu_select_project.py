@@ -88,6 +88,9 @@ def _ulp_bf16(x):
     ("f32", 64, 64, 256, 0, 256),
     ("f32", 128, 128, 33, 100, 192),
     ("bf16", 64, 64, 1, 63, 64),
+    ("bf16", 128, 128, 8, 5, 64),      # largest few-token launch
+    ("bf16", 128, 96, 9, 0, 64),       # smallest tiled launch
+    ("f32", 128, 128, 1, 191, 192),    # a decode step filling the last column
 ])
 def test_project_keys_append(dtype, d, d_store, n, len0, T_cap):
     B, Hkv = 2, 3
