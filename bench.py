@@ -54,6 +54,36 @@ def step_bytes(U: np.ndarray, c: dict, T: int) -> int:
     return kv + B * Hq * d * es + new_tok + d * d * 4 + B * Hq * d * 4
 
 
+def decode_bytes(U: np.ndarray, c: dict, T: int) -> int:
+    """Algorithmic bytes of one aqua_decode launch over T tokens: the K' rows of U and all of V,
+    q' and output (fp32), masks."""
+    d, B, Hq, Hkv = c["d"], c["B"], c["Hq"], c["Hkv"]
+    es = 2 if c["dtype"] == "bf16" else 4
+    kv = int(U.sum()) * T * es + B * Hkv * T * d * es
+    return kv + B * Hq * d * 4 * 2 + B * Hq * (d // 32) * 4
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_llama8b_b16_t8192_hbm_traffic.md")
+
+
+def traffic_bytes(path: str):
+    """HBM bytes per launch of the decode kernel from the committed counter summary, if it was
+    taken on the current kernel source (its hash is recorded there); else None."""
+    import hashlib
+    import re
+
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    src = os.path.join(ROOT, "sparse_dimension_attention_amd", "csrc", "decode.hip")
+    h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    m = re.search(r"decode\.hip sha256\[:16\]: `([0-9a-f]+)`", text)
+    t = re.search(rf"traffic_{path}_bytes_per_launch: `(\d+)`", text)
+    if not m or m.group(1) != h or not t:
+        return None
+    return int(t.group(1))
+
+
 def cpu_baseline(c: dict, n_groups: int, reps: int):
     """The oracle, as it stands, on n_groups KV groups of the same decode step."""
     from threadpoolctl import threadpool_info
@@ -111,6 +141,8 @@ def main():
     ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES")
+    ap.add_argument("--only", choices=("fused", "three"), default=None,
+                    help="run one step implementation only, untimed (for counter runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the AQUA decode path here runs on a single MI355X "
@@ -147,68 +179,79 @@ def main():
     ws = torch.zeros(aq.aqua_decode_workspace(cache, Hq), dtype=torch.uint8, device=dev)
     scale = 1.0 / math.sqrt(d)
     torch.cuda.synchronize()
+    if args.only:
+        # a short run of one path only (for counter collection under rocprofv3)
+        for _ in range(args.steps):
+            cache.len = T - 1
+            if args.only == "three":
+                aq.aqua_project_keys(cache, k_new[:, :, None], v_new[:, :, None], P, 1)
+                aq.aqua_select_dims(q.reshape(B * Hq, d), P, d, k, qp, mask)
+                aq.aqua_decode(cache, Hq, qp, mask, scale, out, ws)
+            else:
+                aq.aqua_decode_step(cache, Hq, q, k_new, v_new, P, d, k, scale, out, ws)
+        torch.cuda.synchronize()
+        print(json.dumps({"only": args.only, "steps": args.steps}))
+        return
 
-    ev = []
+    # Two implementations of the same step; both are timed, the faster one is the headline.
+    #  fused: aqua_decode_step (one launch);  three: aqua_project_keys + aqua_select_dims +
+    #  aqua_decode.  Events bracket the dominant launch (the decode kernel) on the launch stream.
+    def run(path: str, n: int, events: list | None):
+        for _ in range(n):
+            cache.len = T - 1
+            if path == "three":
+                aq.aqua_project_keys(cache, k_new[:, :, None], v_new[:, :, None], P, 1)
+                aq.aqua_select_dims(q.reshape(B * Hq, d), P, d, k, qp, mask)
+            if events is not None:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+            if path == "three":
+                aq.aqua_decode(cache, Hq, qp, mask, scale, out, ws)
+            else:
+                aq.aqua_decode_step(cache, Hq, q, k_new, v_new, P, d, k, scale, out, ws,
+                                    mask_out=mask.view(B, Hq, d // 32))
+            if events is not None:
+                e1.record()
+                events.append((e0, e1))
 
-    def step(timed: bool):
-        cache.len = T - 1
-        if timed:
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-        aq.aqua_decode_step(cache, Hq, q, k_new, v_new, P, d, k, scale, out, ws)
-        if timed:
-            e1.record()
-            ev.append((e0, e1))
-
-    def step_unfused():
-        cache.len = T - 1
-        aq.aqua_project_keys(cache, k_new[:, :, None], v_new[:, :, None], P, 1)
-        aq.aqua_select_dims(q.reshape(B * Hq, d), P, d, k, qp, mask)
-        aq.aqua_decode(cache, Hq, qp, mask, scale, out, ws)
-
-    for _ in range(args.warmup):
-        step(False)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step(True)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms_per_step = elapsed * 1e3 / args.steps
-    k_ms = [a.elapsed_time(b) for a, b in ev]
+    res = {}
+    for path in ("fused", "three"):
+        run(path, args.warmup, None)
+        torch.cuda.synchronize()
+        ev = []
+        t0 = time.perf_counter()
+        run(path, args.steps, ev)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        k_ms = [a.elapsed_time(b) for a, b in ev]
+        res[path] = (ms, k_ms)
+    best = min(res, key=lambda p: res[p][0])
+    ms_per_step, k_ms = res[best]
     k_avg_s = statistics.mean(k_ms) * 1e-3
 
-    # the same step as three launches (for comparison; not the headline)
-    for _ in range(5):
-        step_unfused()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    n_unf = max(10, args.steps // 4)
-    for _ in range(n_unf):
-        step_unfused()
-    torch.cuda.synchronize()
-    ms_unfused = (time.perf_counter() - t0) * 1e3 / n_unf
-
     U = union_rows(mask.cpu().numpy().reshape(B, Hq, d // 32), B, Hkv, G, d, c["d_store"])
-    nbytes = step_bytes(U, c, T)
+    nbytes = step_bytes(U, c, T) if best == "fused" else decode_bytes(U, c, T)
     achieved = nbytes / k_avg_s / 1e9
     value = B * Hq * T / (ms_per_step * 1e-3)
+    kname = ("decode_kernel<bf16, d=128, G=4, fused>" if best == "fused"
+             else "decode_kernel<bf16, d=128, G=4>")
     rec = {
         "metric": METRIC, "value": value, "unit": "q-head·tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic (seeded; q, K = Z diag(exp(-i/40)+0.05) P^T, V ~ N(0,1))",
         "config": {"workload": c["name"], "B": B, "Hq": Hq, "Hkv": Hkv, "d_head": d, "T": T,
-                   "k": k, "storage": c["dtype"], "parallelism": "none (1 GPU)"},
+                   "k": k, "storage": c["dtype"], "step": best, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None},
-        "kernel": "decode_kernel (fused step: append + select + split-T decode + merge)",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_bytes(best)},
+        "kernel": kname,
         "kernel_us": k_avg_s * 1e6,
         "kernel_us_p10_p90": [float(np.percentile(k_ms, 10) * 1e3),
                               float(np.percentile(k_ms, 90) * 1e3)],
         "bytes_per_launch": nbytes,
         "mean_union_rows": float(U.mean()),
-        "ms_per_step_three_launches": ms_unfused,
+        "ms_per_step_by_path": {p: res[p][0] for p in res},
+        "kernel_us_by_path": {p: statistics.mean(res[p][1]) * 1e3 for p in res},
     }
     if not args.no_cpu:
         rec["cpu_baseline"] = cpu_baseline(c, args.cpu_groups, args.cpu_reps)

@@ -92,8 +92,11 @@ struct DecodeSmem {
   static constexpr int BYTES = OFF_ML + 2 * G * 4 + 16;
 };
 
+// Two workgroups per CU must stay resident (the decode streams at full bandwidth only then):
+// at least two waves per SIMD, i.e. at most 256 VGPRs.
 template <typename KT, int D, int G, int NW, bool FUSED>
-__global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_kernel(DecodeArgs a) {
   using SM = DecodeSmem<KT, D, G, NW, FUSED>;
   constexpr int TPL = SM::TPL;     // tokens per lane per K' row load
   constexpr int WT = SM::WT;       // tokens per wavefront
@@ -170,7 +173,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
         acc[r] = 0.0f;
         row[r] = min(r0 + r * RSTEP, G);
       }
-#pragma unroll
+#pragma unroll 16
       for (int j = 0; j < D; ++j) {
         const float p = sP[j * D + i];
 #pragma unroll
