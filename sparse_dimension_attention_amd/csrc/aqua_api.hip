@@ -56,6 +56,16 @@ aqua_status check_heads(const aqua_cache *c, int32_t Hq) {
   return AQUA_OK;
 }
 
+aqua_status check_prefill_cache(const aqua_cache *c, int32_t Hq) {
+  if (aqua_status st = check_cache(c)) return st;
+  if (aqua_status st = check_heads(c, Hq)) return st;
+  if (c->dtype != AQUA_BF16) return fail(AQUA_ERR_DTYPE, "prefill needs bf16 storage");
+  if (c->d_head != 128) return fail(AQUA_ERR_SHAPE, "prefill needs d_head == 128");
+  if (c->d_store % 16 != 0)
+    return fail(AQUA_ERR_SHAPE, "prefill needs d_store (%d) a multiple of 16", c->d_store);
+  return AQUA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -213,11 +223,10 @@ aqua_status aqua_decode_step(aqua_cache *c, int32_t Hq, const void *q, const voi
 
 aqua_status aqua_prefill_workspace(const aqua_cache *c, int32_t Hq, int32_t Lq, size_t *bytes) {
   g_err[0] = 0;
-  if (aqua_status st = check_cache(c)) return st;
-  if (aqua_status st = check_heads(c, Hq)) return st;
+  if (aqua_status st = check_prefill_cache(c, Hq)) return st;
   if (!bytes) return fail(AQUA_ERR_NULL, "bytes is NULL");
   if (Lq < 1) return fail(AQUA_ERR_SHAPE, "Lq=%d must be >= 1", Lq);
-  *bytes = 0;
+  *bytes = aqua::prefill_workspace_bytes(c->B, Hq, Lq);
   return AQUA_OK;
 }
 
@@ -226,10 +235,26 @@ aqua_status aqua_prefill_chunk(const aqua_cache *c, int32_t Hq, const void *q, i
                                float scale, float *out, float *q_proj_out, uint32_t *mask_out,
                                void *ws, size_t ws_bytes, void *stream) {
   g_err[0] = 0;
-  (void)q; (void)Lq; (void)pos0; (void)P; (void)d_sel; (void)k; (void)scale; (void)out;
-  (void)q_proj_out; (void)mask_out; (void)ws; (void)ws_bytes; (void)stream; (void)Hq;
-  if (aqua_status st = check_cache(c)) return st;
-  return fail(AQUA_ERR_SHAPE, "aqua_prefill_chunk: not available in this build");
+  if (aqua_status st = check_prefill_cache(c, Hq)) return st;
+  if (!q || !P || !out) return fail(AQUA_ERR_NULL, "q, P and out are required");
+  if (!ws) return fail(AQUA_ERR_WORKSPACE, "workspace is NULL");
+  if (Lq < 1 || pos0 < 0) return fail(AQUA_ERR_SHAPE, "Lq=%d >= 1 and pos0=%d >= 0 needed", Lq, pos0);
+  if (static_cast<int64_t>(pos0) + Lq > c->len)
+    return fail(AQUA_ERR_CAPACITY, "pos0 + Lq = %lld exceeds the cached len %d",
+                static_cast<long long>(pos0) + Lq, c->len);
+  if (!(1 <= k && k <= d_sel && d_sel <= c->d_store))
+    return fail(AQUA_ERR_SHAPE, "need 1 <= k (%d) <= d_sel (%d) <= d_store (%d)", k, d_sel,
+                c->d_store);
+  if (!aligned16(q) || !aligned16(P) || !aligned16(out) || !aligned16(ws) ||
+      (q_proj_out && !aligned16(q_proj_out)) || (mask_out && !aligned16(mask_out)))
+    return fail(AQUA_ERR_ALIGN, "all buffers must be 16-byte aligned");
+  const size_t need = aqua::prefill_workspace_bytes(c->B, Hq, Lq);
+  if (ws_bytes < need)
+    return fail(AQUA_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, need);
+  return hip_status(aqua::launch_prefill(c->kp, c->v, c->B, Hq, c->Hkv, c->d_store, c->T_cap, q,
+                                         Lq, pos0, P, d_sel, k, scale, out, q_proj_out,
+                                         mask_out, ws, static_cast<hipStream_t>(stream)),
+                    "aqua_prefill_chunk launch");
 }
 
 aqua_status aqua_h2o_victim(float *mass, int32_t *slot_pos, int32_t B, int32_t Hkv,

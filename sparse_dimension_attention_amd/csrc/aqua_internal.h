@@ -152,6 +152,11 @@ hipError_t launch_project_keys(int dtype, const void *k_raw, const void *v_raw, 
                                const int32_t *slots, void *kp, void *v, hipStream_t s);
 hipError_t launch_decode(int dtype, const DecodeArgs &a, hipStream_t s);
 hipError_t launch_decode_step(int dtype, const DecodeArgs &a, hipStream_t s);
+size_t prefill_workspace_bytes(int B, int Hq, int Lq);
+hipError_t launch_prefill(const void *kp, const void *v, int B, int Hq, int Hkv, int d_store,
+                          int T_cap, const void *q, int Lq, int pos0, const float *P, int d_sel,
+                          int k, float scale, float *out, float *q_proj_out, uint32_t *mask_out,
+                          void *ws, hipStream_t s);
 hipError_t launch_h2o_victim(float *mass, int32_t *slot_pos, int B, int Hkv, int n_slots,
                              int t_new, int recent, int32_t *victim, hipStream_t s);
 

@@ -1,0 +1,132 @@
+"""GPU parity of aqua_prefill_chunk (per-query selection + causal MFMA attention) against the
+oracle: masks bit-exact given the GPU's q', outputs within the bf16 tolerance."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import sparse_dimension_attention_amd as aq
+from gpu_util import DEV, assert_close, new_cache, unpack_mask
+from oracle import aqua_oracle as O
+from synth import config, make_prefill_inputs, storage_to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_chunks(inp, c, chunk, T_cap=None, d_store=None, d_sel=None, k=None):
+    """Append each chunk's keys, then prefill its queries.  Returns GPU out, q', masks."""
+    B, Hq, Hkv, d, T = c["B"], c["Hq"], c["Hkv"], c["d"], c["T"]
+    d_store = d_store or d
+    d_sel = d_sel or d_store
+    k = k or c["k"]
+    T_cap = T_cap or ((T + 63) // 64 * 64)
+    kp, v = new_cache(B, Hkv, d, d_store, T_cap, "bf16")
+    cache = aq.make_cache(kp, v, 0)
+    P = inp["P"].to(DEV)
+    out = torch.full((B, Hq, T, d), float("nan"), device=DEV)
+    qp = torch.full((B, Hq, T, d), float("nan"), device=DEV)
+    mask = torch.zeros(B, Hq, T, d // 32, dtype=torch.int32, device=DEV)
+    for c0 in range(0, T, chunk):
+        L = min(chunk, T - c0)
+        aq.aqua_project_keys(cache, inp["k"][:, :, c0:c0 + L].contiguous().to(DEV),
+                             inp["v"][:, :, c0:c0 + L].contiguous().to(DEV), P, L)
+        ws = torch.empty(aq.aqua_prefill_workspace(cache, Hq, L), dtype=torch.uint8, device=DEV)
+        o = torch.empty(B, Hq, L, d, device=DEV)
+        qpc = torch.empty(B, Hq, L, d, device=DEV)
+        mc = torch.empty(B, Hq, L, d // 32, dtype=torch.int32, device=DEV)
+        aq.aqua_prefill_chunk(cache, Hq, inp["q"][:, :, c0:c0 + L].contiguous().to(DEV), L, c0, P,
+                              d_sel, k, 1 / math.sqrt(d), o, ws=ws, q_proj_out=qpc, mask_out=mc)
+        out[:, :, c0:c0 + L] = o
+        qp[:, :, c0:c0 + L] = qpc
+        mask[:, :, c0:c0 + L] = mc
+    torch.cuda.synchronize()
+    return out, qp, mask
+
+
+def _oracle_rows(inp, c, m, rows, d_store=None):
+    """Oracle output for (b, h, position) rows, with the given masks."""
+    d = c["d"]
+    d_store = d_store or d
+    G = c["Hq"] // c["Hkv"]
+    P64 = storage_to_f64(inp["P"])
+    cacheK = {}
+    res = []
+    for b, h, p in rows:
+        g = h // G
+        if (b, g) not in cacheK:
+            cacheK[(b, g)] = (O.project_keys_stored(storage_to_f64(inp["k"][b, g]), P64, "bf16",
+                                                    d_store),
+                              storage_to_f64(inp["v"][b, g]))
+        Kp, V = cacheK[(b, g)]
+        qp = O.project(storage_to_f64(inp["q"][b, h, p]), P64)
+        o, _ = O.attend(qp, m[b, h, p], Kp[:p + 1], V[:p + 1], 1 / math.sqrt(d))
+        res.append(o)
+    return np.stack(res)
+
+
+def _check(inp, c, out, qp, mask, rows, d_sel, k, d_store=None):
+    d = c["d"]
+    m = unpack_mask(mask, d)
+    assert np.array_equal(m, O.select(qp.cpu().double().numpy(), d_sel, k))
+    ref = _oracle_rows(inp, c, m, rows, d_store)
+    got = np.stack([out[b, h, p].cpu().double().numpy() for b, h, p in rows])
+    assert_close(got, ref, "bf16", "prefill rows")
+
+
+@pytest.mark.parametrize("Hq,Hkv,T,chunk,k", [
+    (8, 2, 300, 300, 96),     # one ragged chunk
+    (8, 2, 700, 256, 96),     # chunks, ragged tail
+    (4, 4, 333, 128, 64),     # G = 1
+    (8, 4, 260, 100, 128),    # G = 2, k = d
+    (16, 2, 200, 200, 32),    # G = 8
+])
+def test_prefill_small_all_rows(Hq, Hkv, T, chunk, k):
+    c = config(4, B=2, Hq=Hq, Hkv=Hkv, T=T, k=k)
+    inp = make_prefill_inputs(c)
+    out, qp, mask = _run_chunks(inp, c, chunk)
+    rows = [(b, h, p) for b in range(c["B"]) for h in range(Hq) for p in range(T)]
+    _check(inp, c, out, qp, mask, rows, c["d"], k)
+
+
+def test_prefill_memory_cut():
+    """AQUA-Memory: K' keeps dims 0..95, top-64 of those 96."""
+    c = config(4, B=1, Hq=8, Hkv=2, T=400, k=64)
+    inp = make_prefill_inputs(c)
+    out, qp, mask = _run_chunks(inp, c, 160, d_store=96, d_sel=96, k=64)
+    rows = [(0, h, p) for h in range(8) for p in range(400)]
+    _check(inp, c, out, qp, mask, rows, 96, 64, d_store=96)
+
+
+def test_prefill_select_matches_select_dims():
+    """The prefill's q' and masks are bit-identical to aqua_select_dims on the same queries."""
+    c = config(4, B=1, Hq=8, Hkv=2, T=500, k=96)
+    inp = make_prefill_inputs(c)
+    out, qp, mask = _run_chunks(inp, c, 500)
+    q = inp["q"].reshape(-1, 128).to(DEV)
+    qp2 = torch.empty_like(q, dtype=torch.float32)
+    m2 = torch.empty(q.shape[0], 4, dtype=torch.int32, device=DEV)
+    aq.aqua_select_dims(q, inp["P"].to(DEV), 128, 96, qp2, m2)
+    torch.cuda.synchronize()
+    assert torch.equal(qp.reshape(-1, 128), qp2)
+    assert torch.equal(mask.reshape(-1, 4), m2)
+
+
+def test_prefill_llama8b_t16384_sampled():
+    """The chunked-prefill workload: T=16384 in 8 chunks of 2048, k=96; sampled rows from
+    every chunk, head and the first/last positions of chunks."""
+    c = config(4)
+    inp = make_prefill_inputs(c)
+    out, qp, mask = _run_chunks(inp, c, c["chunk"])
+    rng = np.random.default_rng(0)
+    rows = [(0, int(h), int(p)) for h, p in zip(rng.integers(0, 32, 24),
+                                                 rng.integers(0, 16384, 24))]
+    rows += [(0, 0, 0), (0, 31, 16383), (0, 5, 2047), (0, 6, 2048), (0, 17, 14335)]
+    m = unpack_mask(mask, 128)
+    for b, h, p in rows:
+        assert np.array_equal(m[b, h, p], O.select(qp[b, h, p].cpu().double().numpy()[None],
+                                                   128, 96)[0])
+    ref = _oracle_rows(inp, c, m, rows)
+    got = np.stack([out[b, h, p].cpu().double().numpy() for b, h, p in rows])
+    assert_close(got, ref, "bf16", "prefill T16384")
+    assert torch.isfinite(out).all()
