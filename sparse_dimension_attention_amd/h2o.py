@@ -1,0 +1,82 @@
+"""H2O decoding over a compact AQUA-Memory cache (AQUA combined with H2O heavy-hitter eviction:
+abstract of arXiv 2509.11155; edgentiq blog, "Key Advantages").
+
+Each (b, g) keeps ``heavy + recent`` slots.  A step is four libaqua calls on one stream:
+
+1. ``aqua_h2o_victim``: evict the non-recent slot ranked lowest by (mass desc, position asc) and
+   claim it for the new position (its mass restarts at 0);
+2. ``aqua_project_keys`` with ``slots = victim``: the new token's K' (first ``d_store`` dims) and V
+   go into that slot;
+3. ``aqua_select_dims``: every query head's q' and top-k mask over the first ``d_sel`` dims;
+4. ``aqua_decode`` in mass mode over all slots: the attention output, and every slot's mass grows
+   by the group's summed softmax weight.
+
+Only one slot changes per step because a token outside the cache never gains mass while cached
+ones only gain (non-negative fp32 additions), so the full-recompute heavy set of a step is the
+previous set minus one member, plus the token that has just left the recent window.
+
+:meth:`H2OCache.from_full` builds the starting state from a full-context cache and its mass
+(the cumulative attention of earlier steps): the ``heavy`` positions of highest mass among
+those older than the recent window, plus the ``recent`` latest positions.  It is set-up work,
+done once with torch tensor ops; every step after it runs in libaqua's kernels.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import aqua as A
+
+
+class H2OCache:
+    """Compact per-(b, g) cache: K' ``[B][Hkv][d_store][n_slots]``, V ``[B][Hkv][n_slots][d]``,
+    ``slot_pos`` int32 and ``mass`` fp32 ``[B][Hkv][n_slots]``, plus the decode workspace."""
+
+    def __init__(self, kp, v, slot_pos, mass, heavy: int, recent: int):
+        self.kp, self.v, self.slot_pos, self.mass = kp, v, slot_pos, mass
+        self.heavy, self.recent = heavy, recent
+        B, Hkv, _, n_slots = kp.shape
+        self.cache = A.make_cache(kp, v, n_slots)
+        self.victim = torch.empty(B, Hkv, dtype=torch.int32, device=kp.device)
+        self.ws = None
+
+    @classmethod
+    def from_full(cls, kp_full, v_full, mass_full, length: int, heavy: int, recent: int):
+        """Starting state after ``length`` tokens (positions 0..length-1) of a full cache
+        ``kp_full [B][Hkv][d_store][T_cap]``, ``v_full [B][Hkv][T_cap][d]`` whose mass is
+        ``mass_full [B][Hkv][T_cap]``.  Requires ``length - recent >= heavy``."""
+        n_old = length - recent
+        if n_old < heavy:
+            raise ValueError("fewer older tokens than heavy-hitter slots")
+        dev = kp_full.device
+        m_old = mass_full[:, :, :n_old]
+        # stable descending sort: equal masses keep ascending position order
+        order = torch.sort(m_old, dim=-1, descending=True, stable=True).indices[..., :heavy]
+        heavy_pos = torch.sort(order, dim=-1).values
+        B, Hkv = kp_full.shape[:2]
+        rec = torch.arange(n_old, length, device=dev).expand(B, Hkv, recent)
+        pos = torch.cat([heavy_pos, rec], dim=-1).contiguous()          # [B][Hkv][n_slots]
+        d_store = kp_full.shape[2]
+        kp = torch.gather(kp_full, 3, pos[:, :, None, :].expand(B, Hkv, d_store, pos.shape[-1]))
+        v = torch.gather(v_full, 2, pos[..., None].expand(B, Hkv, pos.shape[-1],
+                                                         v_full.shape[-1]))
+        mass = torch.gather(mass_full, 2, pos)
+        return cls(kp.contiguous(), v.contiguous(), pos.to(torch.int32), mass.contiguous(), heavy,
+                   recent)
+
+    def workspace(self, Hq: int):
+        if self.ws is None:
+            n = A.aqua_decode_workspace(self.cache, Hq)
+            self.ws = torch.zeros(n, dtype=torch.uint8, device=self.kp.device)
+        return self.ws
+
+    def step(self, q, k_new, v_new, P, t_new: int, d_sel: int, k: int, scale: float, out,
+             q_proj, mask, stream=None):
+        """One decode step for the token at position ``t_new``.
+        q ``[B][Hq][d]``, k_new/v_new ``[B][Hkv][d]`` (raw, the cache's dtype); out ``[B][Hq][d]``
+        fp32; q_proj ``[B][Hq][d]`` fp32 and mask ``[B][Hq][d/32]`` int32 are written."""
+        Hq = q.shape[1]
+        ws = self.workspace(Hq)
+        A.aqua_h2o_victim(self.mass, self.slot_pos, t_new, self.recent, self.victim, stream)
+        A.aqua_project_keys(self.cache, k_new, v_new, P, 1, slots=self.victim, stream=stream)
+        A.aqua_select_dims(q, P, d_sel, k, q_proj, mask, stream=stream)
+        A.aqua_decode(self.cache, Hq, q_proj, mask, scale, out, ws, mass=self.mass, stream=stream)
