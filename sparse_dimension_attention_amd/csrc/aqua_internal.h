@@ -108,6 +108,56 @@ __device__ __forceinline__ void wave_topk(const float (&x)[E], int d_sel, int k,
   }
 }
 
+// The same top-k by a threshold search: the k-th largest key T is built MSB first (keep bit b
+// of T iff at least k keys are >= T | bit b), stopping early once exactly k keys are >= the
+// running threshold.  Keys of dims >= d_sel are -1, below every magnitude.  If the search ends
+// with more than k keys >= T (ties at T), the keys > T are kept and the ties are taken in index
+// order.  Per bit: two compares and two ballot popcounts, the rest is scalar.
+template <int E>
+__device__ __forceinline__ void wave_topk_threshold(const float (&x)[E], int d_sel, int k,
+                                                    bool (&sel)[E]) {
+  const int lane = threadIdx.x & 63;
+  int u[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    u[e] = (lane + 64 * e) < d_sel ? static_cast<int>(__float_as_uint(x[e]) & 0x7fffffffu) : -1;
+  int T = 0;
+  bool exact = (d_sel == k);
+  if (!exact) {
+    for (int bit = 30; bit >= 0; --bit) {
+      const int c = T | (1 << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) cnt += __popcll(__ballot(u[e] >= c));
+      if (cnt >= k) {
+        T = c;
+        if (cnt == k) {
+          exact = true;
+          break;
+        }
+      }
+    }
+  }
+  if (exact) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) sel[e] = u[e] >= T;
+    return;
+  }
+  int need = k;
+#pragma unroll
+  for (int e = 0; e < E; ++e) need -= __popcll(__ballot(u[e] > T));
+  int before = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const uint64_t b = __ballot(u[e] == T);
+    const int rank = before + static_cast<int>(__builtin_amdgcn_mbcnt_hi(
+                                  static_cast<uint32_t>(b >> 32),
+                                  __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(b), 0u)));
+    sel[e] = u[e] > T || (u[e] == T && rank < need);
+    before += __popcll(b);
+  }
+}
+
 // ------------------------------------------------------------------ launch parameter blocks
 struct DecodeArgs {
   const void *kp;        // [B][Hkv][d_store][T_cap]

@@ -4,9 +4,9 @@
 // a position <= its own.
 //
 // Two launches per chunk:
-//  1. prefill_select_kernel: q' and the top-k mask of every query (the selection of
-//     aqua_select_dims, bit-identical), written out as the MFMA operand: the selected q' dims,
-//     pre-multiplied by scale * log2(e), rounded to bf16, zeros elsewhere.
+//  1. prefill_select_kernel: q' (an fp32-accurate projection on MFMA) and the top-k mask of every
+//     query (the selection rule of aqua_select_dims), written out as the MFMA operand: the
+//     selected q' dims, pre-multiplied by scale * log2(e), rounded to bf16, zeros elsewhere.
 //  2. prefill_attn_kernel: flash-attention style on bf16 MFMA (v_mfma_f32_32x32x16_bf16) with
 //     fp32 accumulation.  The zeroed dims still cost MFMA work: the dense contraction over all
 //     stored dims is the cheapest exact way to apply per-query masks on matrix cores.
@@ -35,65 +35,98 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
 // ------------------------------------------------------------------ 1. selection
-// Each wavefront handles `rpw` consecutive rows; the workgroup stages P in LDS once.
-template <typename QT>
-__global__ __launch_bounds__(256) void prefill_select_kernel(const QT *__restrict__ q, int N,
+// q' = q P on bf16 MFMA at fp32 accuracy: q is bf16, and every fp32 entry of P is the exact sum
+// of three bf16 parts (RNE of P, of the remainder, of the remainder's remainder: 8 + 8 + 8
+// significand bits), so q' = q P_hi + q P_mid + q P_lo with every product exact and fp32
+// accumulation.  A workgroup walks blocks of 32 rows; wavefront w computes output columns
+// [32w, 32w + 32) with its parts of P held in registers, writes its q' tile to LDS, and after one
+// barrier each wavefront selects 8 of the 32 rows (one row at a time, lane l holding dims l and
+// l + 64).
+constexpr int SQS = 128 + 8;  // LDS row stride (floats) of the q' tile
+
+__device__ __forceinline__ void split3(float p, uint32_t &h, uint32_t &m, uint32_t &l) {
+  h = f32_to_bf16_rne(p);
+  const float r1 = p - bf16_to_f32(static_cast<uint16_t>(h));
+  m = f32_to_bf16_rne(r1);
+  const float r2 = r1 - bf16_to_f32(static_cast<uint16_t>(m));
+  l = f32_to_bf16_rne(r2);
+}
+
+__global__ __launch_bounds__(256) void prefill_select_kernel(const bf16_t *__restrict__ q, int N,
                                                              const float *__restrict__ P,
                                                              int d_sel, int k, float qscale,
-                                                             int rpw, float *__restrict__ q_proj,
+                                                             float *__restrict__ q_proj,
                                                              uint32_t *__restrict__ mask,
                                                              bf16_t *__restrict__ qm) {
-  constexpr int D = 128, E = 2;
-  __shared__ float sP[D * D];
-  {
-    constexpr int NV = D * D / (256 * 4);
+  __shared__ __align__(16) float sQ[2][32 * SQS];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int col = 32 * w + (lane & 31);
+  // B operands: P[16 m + 8 (lane / 32) + e][col], e = 0..7, in three bf16 parts
+  u32x4_t bh[8], bm[8], bl[8];
 #pragma unroll
-    for (int v0 = 0; v0 < NV; v0 += 4) {
-      float4 st[4];
+  for (int m = 0; m < 8; ++m) {
+    uint32_t h[8], mi[8], lo[8];
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
-        st[v] = *reinterpret_cast<const float4 *>(&P[((v0 + v) * 256 + threadIdx.x) * 4]);
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-        *reinterpret_cast<float4 *>(&sP[((v0 + v) * 256 + threadIdx.x) * 4]) = st[v];
-    }
+    for (int e = 0; e < 8; ++e)
+      split3(P[(16 * m + 8 * (lane >> 5) + e) * 128 + col], h[e], mi[e], lo[e]);
+    bh[m] = u32x4_t{h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16, h[6] | h[7] << 16};
+    bm[m] = u32x4_t{mi[0] | mi[1] << 16, mi[2] | mi[3] << 16, mi[4] | mi[5] << 16,
+                    mi[6] | mi[7] << 16};
+    bl[m] = u32x4_t{lo[0] | lo[1] << 16, lo[2] | lo[3] << 16, lo[4] | lo[5] << 16,
+                    lo[6] | lo[7] << 16};
   }
-  __syncthreads();
-  const int lane = threadIdx.x & 63;
-  const int row0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * rpw;
-  for (int rr = 0; rr < rpw; ++rr) {
-    const int row = row0 + rr;
-    if (row >= N) break;  // uniform over the wavefront; no workgroup barrier follows
-    const QT *qr = q + static_cast<size_t>(row) * D;
-    float qv[E], acc[E];
+  const int nblk = (N + 31) / 32;
+  int buf = 0;
+  for (int blk = blockIdx.x; blk < nblk; blk += gridDim.x, buf ^= 1) {
+    const int r0 = blk * 32;
+    // ---- projection: rows r0 .. r0+31 (clamped), columns [32w, 32w+32)
+    const int arow = min(r0 + (lane & 31), N - 1);
+    const bf16_t *qa = q + static_cast<size_t>(arow) * 128 + 8 * (lane >> 5);
+    u32x4_t av[8];
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      qv[e] = load_elem<QT>(qr + lane + 64 * e);
-      acc[e] = 0.0f;
-    }
-#pragma unroll 16
-    for (int j = 0; j < D; ++j) {
-      const float src = (j < 64) ? qv[0] : qv[1];
-      const float qj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(src), j & 63));
+    for (int m = 0; m < 8; ++m) av[m] = *reinterpret_cast<const u32x4_t *>(qa + 16 * m);
+    f32x16_t acc_h, acc_l;
 #pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] = fmaf(qj, sP[j * D + lane + 64 * e], acc[e]);
-    }
-    bool sel[E];
-    wave_topk<E>(acc, d_sel, k, sel);
-    uint64_t sb[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) sb[e] = __ballot(sel[e]);
-    if (lane < 4) {
-      const uint64_t bb = (lane >> 1) ? sb[1] : sb[0];
-      mask[static_cast<size_t>(row) * 4 + lane] =
-          (lane & 1) ? static_cast<uint32_t>(bb >> 32) : static_cast<uint32_t>(bb);
+    for (int r = 0; r < 16; ++r) {
+      acc_h[r] = 0.0f;
+      acc_l[r] = 0.0f;
     }
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const size_t at = static_cast<size_t>(row) * D + lane + 64 * e;
-      if (q_proj) q_proj[at] = acc[e];
-      qm[at] = sel[e] ? f32_to_bf16_rne(acc[e] * qscale) : static_cast<bf16_t>(0);
+    for (int m = 0; m < 8; ++m) {
+      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, av[m]);
+      acc_l = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, bl[m]),
+                                                      acc_l, 0, 0, 0);
+      acc_l = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, bm[m]),
+                                                      acc_l, 0, 0, 0);
+      acc_h = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, bh[m]),
+                                                      acc_h, 0, 0, 0);
     }
+    float *tile = sQ[buf];
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      tile[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * SQS + col] = acc_h[r] + acc_l[r];
+    __syncthreads();
+    // ---- selection: wavefront w takes rows 8w .. 8w+7 of the block
+    for (int rr = 8 * w; rr < 8 * w + 8; ++rr) {
+      const int row = r0 + rr;
+      if (row >= N) break;  // uniform over the wavefront
+      const float x[2] = {tile[rr * SQS + lane], tile[rr * SQS + lane + 64]};
+      bool sel[2];
+      wave_topk_threshold<2>(x, d_sel, k, sel);
+      const uint64_t s0 = __ballot(sel[0]), s1 = __ballot(sel[1]);
+      if (lane < 4) {
+        const uint64_t bb = (lane >> 1) ? s1 : s0;
+        mask[static_cast<size_t>(row) * 4 + lane] =
+            (lane & 1) ? static_cast<uint32_t>(bb >> 32) : static_cast<uint32_t>(bb);
+      }
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const size_t at = static_cast<size_t>(row) * 128 + lane + 64 * e;
+        if (q_proj) q_proj[at] = x[e];
+        qm[at] = sel[e] ? f32_to_bf16_rne(x[e] * qscale) : static_cast<bf16_t>(0);
+      }
+    }
+    // the next block writes the other tile; the barrier above it orders this block's reads
   }
 }
 
@@ -289,11 +322,10 @@ hipError_t launch_prefill(const void *kp, const void *v, int B, int Hq, int Hkv,
   const size_t rows = static_cast<size_t>(B) * Hq * Lq;
   bf16_t *qm = static_cast<bf16_t *>(ws);
   uint32_t *mask = mask_out ? mask_out : reinterpret_cast<uint32_t *>(qm + rows * 128);
-  const int rpw = 8;  // rows per wavefront
-  const int nblk = static_cast<int>((rows + 4 * rpw - 1) / (4 * rpw));
-  prefill_select_kernel<bf16_t><<<dim3(nblk), dim3(256), 0, s>>>(
+  const int nblk = static_cast<int>((rows + 31) / 32);
+  prefill_select_kernel<<<dim3(nblk < 512 ? nblk : 512), dim3(256), 0, s>>>(
       static_cast<const bf16_t *>(q), static_cast<int>(rows), P, d_sel, k,
-      scale * 1.4426950408889634f, rpw, q_proj_out, mask, qm);
+      scale * 1.4426950408889634f, q_proj_out, mask, qm);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   PrefillArgs a;
