@@ -131,9 +131,24 @@ __global__ __launch_bounds__(256) void prefill_select_kernel(const bf16_t *__res
 }
 
 // ------------------------------------------------------------------ 2. attention
-constexpr int KT = 64;          // tokens per K'/V tile
-constexpr int KS = 128 + 8;     // LDS row stride (bf16) of the K' tile [token][dim]
-constexpr int VS = KT + 4;      // LDS row stride (bf16) of the V tile [dim][token]
+// Workgroup = 4 wavefronts; a wavefront owns one query head and 64 consecutive positions (two
+// 32-row MFMA blocks that share every K'/V operand read).  The 4 wavefronts cover the heads of
+// one KV group (or, for G < 4, several position blocks), so each 64-token K'/V tile is staged in
+// LDS once for 256 query rows.  Tiles are double-buffered: the global loads of tile t+1 are in
+// flight while tile t is computed, and one barrier per tile hands the buffers over.
+//
+// Operands come out of LDS with ds_read_b64_tr_b16, which within each 16-lane group reads a
+// 4-row x 16-column block of 16-bit elements (lane s of the group supplying the address of row
+// s / 4, columns 4 (s % 4) .. +3) and hands lane i = 4a + b the column i: element e of its result
+// is row e, column i.  So the MFMA A operand (lane l: row l % 32, 8 consecutive k) is read from
+// a tile stored k-major, which is how K' ([dim][token]) and V ([token][dim]) already are in HBM:
+// the staging is a plain 16-byte copy.
+constexpr int KT = 64;          // tokens per tile
+constexpr int KROW = KT + 32;   // LDS row (dim) stride of the K' tile, bf16: 192 B
+constexpr int VROW = 128 + 32;  // LDS row (token) stride of the V tile, bf16: 320 B
+constexpr int KBUF = 128 * KROW;
+constexpr int VBUF = KT * VROW;
+constexpr float RESCALE_SLACK = 8.0f;  // log2 units the running max may lag the true max
 
 struct PrefillArgs {
   const bf16_t *kp;  // [B][Hkv][d_store][T_cap]
@@ -142,169 +157,225 @@ struct PrefillArgs {
   float *out;        // [B][Hq][Lq][128]
   int B, Hq, Hkv, d_store, T_cap, Lq, pos0;
   int qh;            // query heads per workgroup (min(G, 4))
-  int nqb;           // query blocks per (b, group, head subset)
+  int nqb;           // position blocks per (b, group, head subset)
 };
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return static_cast<uint32_t>(f32_to_bf16_rne(lo)) |
-         (static_cast<uint32_t>(f32_to_bf16_rne(hi)) << 16);
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+
+__device__ __forceinline__ bf16x8_t lds_tr_pair(const bf16_t *p0, const bf16_t *p1) {
+  const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t *)(p0));
+  const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t *)(p1));
+  return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
-void prefill_attn_kernel(PrefillArgs a) {
-  __shared__ __align__(16) bf16_t sK[KT * KS];   // K' tile, [token][dim]
-  __shared__ __align__(16) bf16_t sV[128 * VS];  // V tile, [dim][token]
+// Two fp32 values to a bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{lo, hi}), bf16x2_t));
+}
+
+__global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
+  __shared__ __align__(16) bf16_t sK[2][KBUF];  // K' tile, [dim][token]
+  __shared__ __align__(16) bf16_t sV[2][VBUF];  // V tile, [token][dim]
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int G = a.Hq / a.Hkv;
-  const int PB = 4 / a.qh;                      // 32-position blocks per workgroup
-  const int nsub = G / a.qh;                    // head subsets per KV group
-  // heaviest (latest positions) first
-  const int qblk = a.nqb - 1 - (blockIdx.x % a.nqb);
-  const int rest = blockIdx.x / a.nqb;
-  const int sub = rest % nsub;
-  const int bg = rest / nsub;
+  const int PB = 4 / a.qh;      // 64-position blocks per workgroup
+  const int nsub = G / a.qh;    // head subsets per KV group
+  const int ncombo = a.B * a.Hkv * nsub;
+  // consecutive workgroup ids go round-robin over the XCDs: keep one (b, group) per id residue
+  // so that the workgroups sharing a K'/V stream share an L2; latest positions first
+  const int combo = blockIdx.x % ncombo;
+  const int qblk = a.nqb - 1 - blockIdx.x / ncombo;
+  const int sub = combo % nsub;
+  const int bg = combo / nsub;
   const int b = bg / a.Hkv, g = bg - b * a.Hkv;
   const int head = g * G + sub * a.qh + (w % a.qh);
-  const int pblk = qblk * PB + w / a.qh;
-  const int row_local = pblk * 32 + (lane & 31);           // position within the chunk
-  const int row_c = min(row_local, a.Lq - 1);
-  const int pos = a.pos0 + row_c;                           // absolute position of this row
-  const int kend = a.pos0 + min((qblk + 1) * PB * 32, a.Lq);  // keys [0, kend) for the group
-  const int nks = a.d_store / 16;
-
-  // the wavefront's 32 query rows as the B operand of S^T, one 16-dim step per register group
-  const size_t qrow = (static_cast<size_t>(b) * a.Hq + head) * a.Lq + row_c;
-  u32x4_t qreg[8];
-#pragma unroll
-  for (int m = 0; m < 8; ++m)
-    qreg[m] = *reinterpret_cast<const u32x4_t *>(a.qm + qrow * 128 + 16 * m + 8 * (lane >> 5));
-
-  f32x16_t acc_o[4];
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc_o[db][r] = 0.0f;
-  float m_i = -INFINITY, l_i = 0.0f;
-
-  const bf16_t *kbase = a.kp + static_cast<size_t>(bg) * a.d_store * a.T_cap;
-  const bf16_t *vbase = a.v + static_cast<size_t>(bg) * a.T_cap * 128;
+  const int pb = qblk * PB + w / a.qh;                  // this wavefront's 64-position block
+  const int kend = a.pos0 + min((qblk + 1) * PB * 64, a.Lq);  // keys [0, kend) for the group
   const int ntile = (kend + KT - 1) / KT;
 
-  for (int t = 0; t < ntile; ++t) {
-    const int t0 = t * KT;
-    // ---- stage K' (dims [0, d_store) x 64 tokens) as [token][dim], V as [dim][token]
-    for (int ci = tid; ci < a.d_store * 8; ci += 256) {
-      const int d = ci % a.d_store, c = ci / a.d_store;  // consecutive lanes: consecutive dims
-      const u32x4_t r = *reinterpret_cast<const u32x4_t *>(
-          kbase + static_cast<size_t>(d) * a.T_cap + t0 + 8 * c);
-      const uint32_t wds[4] = {r.x, r.y, r.z, r.w};
+  // ---- the wavefront's query rows (B operand of S^T), one 16-dim step per register group
+  int pos[2];
+  u32x4_t qreg[2][8];
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        sK[(8 * c + 2 * x) * KS + d] = static_cast<bf16_t>(wds[x] & 0xffffu);
-        sK[(8 * c + 2 * x + 1) * KS + d] = static_cast<bf16_t>(wds[x] >> 16);
-      }
-    }
-    for (int ci = tid; ci < KT * 16; ci += 256) {
-      const int tok = ci % KT, c = ci / KT;  // consecutive lanes: consecutive tokens
-      u32x4_t r = {0u, 0u, 0u, 0u};
-      if (t0 + tok < kend)  // never multiply garbage V by a zero weight
-        r = *reinterpret_cast<const u32x4_t *>(vbase + static_cast<size_t>(t0 + tok) * 128 +
-                                               8 * c);
-      const uint32_t wds[4] = {r.x, r.y, r.z, r.w};
+  for (int qb = 0; qb < 2; ++qb) {
+    const int rl = min(pb * 64 + qb * 32 + (lane & 31), a.Lq - 1);
+    pos[qb] = a.pos0 + rl;
+    const bf16_t *qr = a.qm + ((static_cast<size_t>(b) * a.Hq + head) * a.Lq + rl) * 128 +
+                       8 * (lane >> 5);
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        sV[(8 * c + 2 * x) * VS + tok] = static_cast<bf16_t>(wds[x] & 0xffffu);
-        sV[(8 * c + 2 * x + 1) * VS + tok] = static_cast<bf16_t>(wds[x] >> 16);
-      }
+    for (int m = 0; m < 8; ++m) {
+      qreg[qb][m] = *reinterpret_cast<const u32x4_t *>(qr + 16 * m);
+      asm volatile("" : "+a"(qreg[qb][m]));  // MFMA B operands only: keep them in AGPRs
     }
-    __syncthreads();
+  }
+  const int pos_first = a.pos0 + min(pb * 64, a.Lq - 1);  // earliest row of the wavefront
 
-    // ---- S^T for two 32-token blocks
-    f32x16_t acc_s[2];
+  // ---- staging: 4 K' chunks and 4 V chunks of 16 B per thread per tile
+  const bf16_t *kbase = a.kp + static_cast<size_t>(bg) * a.d_store * a.T_cap;
+  const bf16_t *vbase = a.v + static_cast<size_t>(bg) * a.T_cap * 128;
+  const int kdim = tid >> 3, kpart = tid & 7;   // K' row kdim + 32 i, 8 tokens at 8 kpart
+  const int vtok = tid >> 4, vpart = tid & 15;  // V row vtok + 16 i, 8 dims at 8 vpart
+  u32x4_t stK[4], stV[4];
+  // unconditional loads from clamped addresses, zeroed afterwards: no divergent branches
+  const int kdim_c[4] = {min(kdim, a.d_store - 1), min(kdim + 32, a.d_store - 1),
+                         min(kdim + 64, a.d_store - 1), min(kdim + 96, a.d_store - 1)};
+  auto load_tile = [&](int t0) {
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc_s[tb][r] = 0.0f;
-      const bf16_t *krow = sK + (tb * 32 + (lane & 31)) * KS + 8 * (lane >> 5);
-      for (int m = 0; m < nks; ++m) {
-        const u32x4_t av = *reinterpret_cast<const u32x4_t *>(krow + 16 * m);
-        acc_s[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            __builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, qreg[m]), acc_s[tb],
-            0, 0, 0);
-      }
+    for (int i = 0; i < 4; ++i) {
+      stK[i] = *reinterpret_cast<const u32x4_t *>(kbase + static_cast<size_t>(kdim_c[i]) * a.T_cap +
+                                                  t0 + 8 * kpart);
+      const int tok = min(t0 + vtok + 16 * i, kend - 1);
+      stV[i] = *reinterpret_cast<const u32x4_t *>(vbase + static_cast<size_t>(tok) * 128 +
+                                                  8 * vpart);
     }
-    // ---- causal mask (token > row position), online softmax in log2 units
-    float mx = -INFINITY;
+  };
+  auto zero_tail = [&](int t0) {  // dims >= d_store, tokens >= kend (never multiply unwritten V)
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb)
+    for (int i = 0; i < 4; ++i) {
+      if (kdim + 32 * i >= a.d_store) stK[i] = u32x4_t{0u, 0u, 0u, 0u};
+      if (t0 + vtok + 16 * i >= kend) stV[i] = u32x4_t{0u, 0u, 0u, 0u};
+    }
+  };
+  auto store_tile = [&](int buf) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int tok = t0 + tb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (tok > pos) acc_s[tb][r] = -INFINITY;
-        mx = fmaxf(mx, acc_s[tb][r]);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_i, mx);
-    const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_i - m_new);
-    float rs = 0.0f;
-    uint32_t pk[2][2][4];  // [tb][k-step][packed pair]
+    for (int i = 0; i < 4; ++i) {
+      *reinterpret_cast<u32x4_t *>(&sK[buf][(kdim + 32 * i) * KROW + 8 * kpart]) = stK[i];
+      *reinterpret_cast<u32x4_t *>(&sV[buf][(vtok + 16 * i) * VROW + 8 * vpart]) = stV[i];
+    }
+  };
+
+  // per-lane parts of the transposed-read addresses (see the comment at the top of this part)
+  const int g16 = (lane >> 4) & 3, s16 = lane & 15;
+  // K': row (dim) 16 m + 8 (g16 / 2) + 4 j + s16 / 4, column (token) 32 tb + 16 (g16 % 2) + 4 (s16 % 4)
+  const int k_off = (8 * (g16 >> 1) + (s16 >> 2)) * KROW + 16 * (g16 & 1) + 4 * (s16 & 3);
+  // V: row (token) 32 tb + 16 s + 4 (g16 / 2) + 8 j + s16 / 4, column (dim) 32 db + 16 (g16 % 2) + 4 (s16 % 4)
+  const int v_off = (4 * (g16 >> 1) + (s16 >> 2)) * VROW + 16 * (g16 & 1) + 4 * (s16 & 3);
+
+  f32x16_t acc_o[2][4];
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          const int r0 = 8 * s + 2 * x;
-          const float p0 = (m_new == -INFINITY) ? 0.0f
-                                                : __builtin_amdgcn_exp2f(acc_s[tb][r0] - m_new);
-          const float p1 = (m_new == -INFINITY)
-                               ? 0.0f
-                               : __builtin_amdgcn_exp2f(acc_s[tb][r0 + 1] - m_new);
-          rs += p0 + p1;
-          pk[tb][s][x] = pack_bf16x2(p0, p1);
-        }
-    rs += __shfl_xor(rs, 32, 64);
-    l_i = l_i * alpha + rs;
-    m_i = m_new;
+  for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc_o[db][r] *= alpha;
+      for (int r = 0; r < 16; ++r) acc_o[qb][db][r] = 0.0f;
+  float m_i[2] = {-INFINITY, -INFINITY}, l_i[2] = {0.0f, 0.0f};
 
-    // ---- O^T += V^T P^T
+  load_tile(0);
+  zero_tail(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int t = 0; t < ntile; ++t) {
+    const int buf = t & 1, t0 = t * KT;
+    if (t + 1 < ntile) load_tile(t0 + KT);
+    const bf16_t *kt = sK[buf] + k_off;
+    const bf16_t *vt = sV[buf] + v_off;
+
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      const bf16_t *vrow = sV + (db * 32 + (lane & 31)) * VS + 4 * (lane >> 5);
+    for (int tb = 0; tb < 2; ++tb) {  // 32-token halves of the tile, one after the other
+      // ---- S^T = K'^T Q'^T for the 32 tokens x 2 query blocks
+      f32x16_t acc_s[2];
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc_s[qb][r] = 0.0f;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const bf16_t *p = kt + 16 * m * KROW + 32 * tb;
+        const bf16x8_t av = lds_tr_pair(p, p + 4 * KROW);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          acc_s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              av, __builtin_bit_cast(bf16x8_t, qreg[qb][m]), acc_s[qb], 0, 0, 0);
+      }
+
+      // ---- causal mask, online softmax (log2 units), probabilities as bf16 B operands
+      const int tok0 = t0 + 32 * tb;
+      uint32_t pk[2][2][4];  // [qb][16-token step][packed pair]
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        if (tok0 + 31 > pos_first + 32 * qb) {  // the block reaches past some row's position
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int tok = tok0 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            if (tok > pos[qb]) acc_s[qb][r] = -INFINITY;
+          }
+        }
+        float mx = acc_s[qb][0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, acc_s[qb][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        // the running max moves only when a score exceeds it by more than the slack, so the
+        // probabilities stay <= 2^slack and the rescale of O is rare after the first block
+        const bool grow = mx > m_i[qb] + RESCALE_SLACK;
+        if (__ballot(grow)) {
+          const float m_new = grow ? mx : m_i[qb];
+          const float alpha = __builtin_amdgcn_exp2f(m_i[qb] - m_new);
+          l_i[qb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc_o[qb][db][r] *= alpha;
+          m_i[qb] = m_new;
+        }
+        float rs = 0.0f;
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            const int r0 = 8 * s + 2 * x;
+            const float p0 = __builtin_amdgcn_exp2f(acc_s[qb][r0] - m_i[qb]);
+            const float p1 = __builtin_amdgcn_exp2f(acc_s[qb][r0 + 1] - m_i[qb]);
+            rs += p0 + p1;
+            pk[qb][s][x] = pack_bf16x2(p0, p1);
+          }
+        l_i[qb] += rs;
+      }
+
+      // ---- O^T += V^T P^T over the 32 tokens
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-          const bf16_t *vp = vrow + tb * 32 + 16 * s;
-          const u32x2_t lo = *reinterpret_cast<const u32x2_t *>(vp);
-          const u32x2_t hi = *reinterpret_cast<const u32x2_t *>(vp + 8);
-          const u32x4_t av = {lo.x, lo.y, hi.x, hi.y};
-          const u32x4_t bv = {pk[tb][s][0], pk[tb][s][1], pk[tb][s][2], pk[tb][s][3]};
-          acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, bv), acc_o[db], 0,
-              0, 0);
+          const bf16_t *p = vt + (32 * tb + 16 * s) * VROW + 32 * db;
+          const bf16x8_t av = lds_tr_pair(p, p + 8 * VROW);
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb) {
+            const u32x4_t bv = {pk[qb][s][0], pk[qb][s][1], pk[qb][s][2], pk[qb][s][3]};
+            acc_o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                av, __builtin_bit_cast(bf16x8_t, bv), acc_o[qb][db], 0, 0, 0);
+          }
         }
     }
-    __syncthreads();  // the next tile overwrites the LDS tiles
+
+    if (t + 1 < ntile) {
+      zero_tail(t0 + KT);
+      store_tile(buf ^ 1);
+    }  // that buffer was last read before the previous barrier
+    __syncthreads();
   }
 
-  // ---- normalise and write: lane l owns query row l%32, dims db*32 + 8*(r/4) + 4*(l/32) + r%4
-  if (row_local < a.Lq) {
-    const float inv = 1.0f / l_i;
-    float *orow = a.out + ((static_cast<size_t>(b) * a.Hq + head) * a.Lq + row_local) * 128;
+  // ---- normalise and write: lane l owns query row l % 32, dims db*32 + 8(r/4) + 4(l/32) + r%4
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+  for (int qb = 0; qb < 2; ++qb) {
+    const int rl = pb * 64 + qb * 32 + (lane & 31);
+    const float inv = 1.0f / (l_i[qb] + __shfl_xor(l_i[qb], 32, 64));
+    if (rl < a.Lq) {
+      float *orow = a.out + ((static_cast<size_t>(b) * a.Hq + head) * a.Lq + rl) * 128;
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        const float4 vv = make_float4(acc_o[db][4 * rq] * inv, acc_o[db][4 * rq + 1] * inv,
-                                      acc_o[db][4 * rq + 2] * inv, acc_o[db][4 * rq + 3] * inv);
-        *reinterpret_cast<float4 *>(orow + db * 32 + 8 * rq + 4 * (lane >> 5)) = vv;
-      }
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const float4 vv =
+              make_float4(acc_o[qb][db][4 * rq] * inv, acc_o[qb][db][4 * rq + 1] * inv,
+                          acc_o[qb][db][4 * rq + 2] * inv, acc_o[qb][db][4 * rq + 3] * inv);
+          *reinterpret_cast<float4 *>(orow + db * 32 + 8 * rq + 4 * (lane >> 5)) = vv;
+        }
+    }
   }
 }
 
@@ -342,7 +413,7 @@ hipError_t launch_prefill(const void *kp, const void *v, int B, int Hq, int Hkv,
   a.pos0 = pos0;
   const int G = Hq / Hkv;
   a.qh = G < 4 ? G : 4;
-  const int rows_per_wg = 32 * (4 / a.qh);
+  const int rows_per_wg = 64 * (4 / a.qh);
   a.nqb = (Lq + rows_per_wg - 1) / rows_per_wg;
   const int grid = a.nqb * (G / a.qh) * B * Hkv;
   prefill_attn_kernel<<<dim3(grid), dim3(256), 0, s>>>(a);
