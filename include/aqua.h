@@ -145,7 +145,11 @@ aqua_status aqua_prefill_workspace(const aqua_cache *c, int32_t Hq, int32_t Lq, 
  *   q_proj_out, mask_out: NULL, or out device [B][Hq][Lq][d_head] fp32 and
  *           [B][Hq][Lq][d_head/32] uint32 (the q' and masks used).
  *   ws    : workspace of at least aqua_prefill_workspace() bytes.
- * Requires d_head == 128, bf16 storage, d_sel <= d_store, Lq >= 1, pos0 >= 0. */
+ * q' is computed at fp32 accuracy (bf16 MFMA on an exact three-part bf16 split of P), so it can
+ * differ from aqua_select_dims' q' in the last bits; the mask is always the exact top-k of the
+ * q' written to q_proj_out.
+ * Requires d_head == 128, bf16 storage, d_store % 16 == 0, T_cap <= 4194304, d_sel <= d_store,
+ * Lq >= 1, pos0 >= 0. */
 aqua_status aqua_prefill_chunk(const aqua_cache *c, int32_t Hq, const void *q, int32_t Lq,
                                int32_t pos0, const float *P, int32_t d_sel, int32_t k,
                                float scale, float *out, float *q_proj_out, uint32_t *mask_out,

@@ -63,6 +63,9 @@ aqua_status check_prefill_cache(const aqua_cache *c, int32_t Hq) {
   if (c->d_head != 128) return fail(AQUA_ERR_SHAPE, "prefill needs d_head == 128");
   if (c->d_store % 16 != 0)
     return fail(AQUA_ERR_SHAPE, "prefill needs d_store (%d) a multiple of 16", c->d_store);
+  // the kernel addresses one (b, group) of K' or V with 32-bit byte offsets
+  if (c->T_cap > (1 << 22))
+    return fail(AQUA_ERR_SHAPE, "prefill needs T_cap (%d) <= 4194304", c->T_cap);
   return AQUA_OK;
 }
 

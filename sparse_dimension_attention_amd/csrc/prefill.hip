@@ -176,13 +176,19 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{lo, hi}), bf16x2_t));
 }
 
-__global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
+// QB: 32-row query blocks per wavefront; NW: wavefronts per workgroup (QB * NW = 8, so a
+// workgroup always holds 256 query rows).
+template <int QB, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(PrefillArgs a) {
+  constexpr int NT = NW * 64;      // threads
+  constexpr int CPT = 1024 / NT;   // 16-byte chunks of K' (and of V) staged per thread per tile
+  constexpr int ROWS = 32 * QB;    // query rows per wavefront
   __shared__ __align__(16) bf16_t sK[2][KBUF];  // K' tile, [dim][token]
   __shared__ __align__(16) bf16_t sV[2][VBUF];  // V tile, [token][dim]
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int G = a.Hq / a.Hkv;
-  const int PB = 4 / a.qh;      // 64-position blocks per workgroup
+  const int WPH = NW / a.qh;    // wavefronts per head: consecutive ROWS-position blocks
   const int nsub = G / a.qh;    // head subsets per KV group
   const int ncombo = a.B * a.Hkv * nsub;
   // consecutive workgroup ids go round-robin over the XCDs: keep one (b, group) per id residue
@@ -193,16 +199,16 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
   const int bg = combo / nsub;
   const int b = bg / a.Hkv, g = bg - b * a.Hkv;
   const int head = g * G + sub * a.qh + (w % a.qh);
-  const int pb = qblk * PB + w / a.qh;                  // this wavefront's 64-position block
-  const int kend = a.pos0 + min((qblk + 1) * PB * 64, a.Lq);  // keys [0, kend) for the group
+  const int pb = qblk * WPH + w / a.qh;  // this wavefront's block of ROWS positions
+  const int kend = a.pos0 + min((qblk + 1) * WPH * ROWS, a.Lq);  // keys [0, kend) for the group
   const int ntile = (kend + KT - 1) / KT;
 
   // ---- the wavefront's query rows (B operand of S^T), one 16-dim step per register group
-  int pos[2];
-  u32x4_t qreg[2][8];
+  int pos[QB];
+  u32x4_t qreg[QB][8];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int rl = min(pb * 64 + qb * 32 + (lane & 31), a.Lq - 1);
+  for (int qb = 0; qb < QB; ++qb) {
+    const int rl = min(pb * ROWS + qb * 32 + (lane & 31), a.Lq - 1);
     pos[qb] = a.pos0 + rl;
     const bf16_t *qr = a.qm + ((static_cast<size_t>(b) * a.Hq + head) * a.Lq + rl) * 128 +
                        8 * (lane >> 5);
@@ -212,39 +218,33 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
       asm volatile("" : "+a"(qreg[qb][m]));  // MFMA B operands only: keep them in AGPRs
     }
   }
-  const int pos_first = a.pos0 + min(pb * 64, a.Lq - 1);  // earliest row of the wavefront
+  const int pos_first = a.pos0 + min(pb * ROWS, a.Lq - 1);  // earliest row of the wavefront
 
-  // ---- staging: 4 K' chunks and 4 V chunks of 16 B per thread per tile
-  const bf16_t *kbase = a.kp + static_cast<size_t>(bg) * a.d_store * a.T_cap;
-  const bf16_t *vbase = a.v + static_cast<size_t>(bg) * a.T_cap * 128;
-  const int kdim = tid >> 3, kpart = tid & 7;   // K' row kdim + 32 i, 8 tokens at 8 kpart
-  const int vtok = tid >> 4, vpart = tid & 15;  // V row vtok + 16 i, 8 dims at 8 vpart
-  u32x4_t stK[4], stV[4];
-  // unconditional loads from clamped addresses, zeroed afterwards: no divergent branches
-  const int kdim_c[4] = {min(kdim, a.d_store - 1), min(kdim + 32, a.d_store - 1),
-                         min(kdim + 64, a.d_store - 1), min(kdim + 96, a.d_store - 1)};
+  // ---- staging through buffer loads: the descriptors' sizes end K' at d_store dims and V at
+  // kend tokens, and reads past a size return zeros (never multiply unwritten V by a zero weight)
+  const __amdgpu_buffer_rsrc_t rK = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t *>(a.kp + static_cast<size_t>(bg) * a.d_store * a.T_cap), (short)0,
+      a.d_store * a.T_cap * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rV = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t *>(a.v + static_cast<size_t>(bg) * a.T_cap * 128), (short)0, kend * 256,
+      0x00020000);
+  const int kdim = tid >> 3, kpart = tid & 7;   // K' rows kdim + (NT/8) i, 8 tokens at 8 kpart
+  const int vtok = tid >> 4, vpart = tid & 15;  // V rows vtok + (NT/16) i, 8 dims at 8 vpart
+  u32x4_t stK[CPT], stV[CPT];
   auto load_tile = [&](int t0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      stK[i] = *reinterpret_cast<const u32x4_t *>(kbase + static_cast<size_t>(kdim_c[i]) * a.T_cap +
-                                                  t0 + 8 * kpart);
-      const int tok = min(t0 + vtok + 16 * i, kend - 1);
-      stV[i] = *reinterpret_cast<const u32x4_t *>(vbase + static_cast<size_t>(tok) * 128 +
-                                                  8 * vpart);
-    }
-  };
-  auto zero_tail = [&](int t0) {  // dims >= d_store, tokens >= kend (never multiply unwritten V)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (kdim + 32 * i >= a.d_store) stK[i] = u32x4_t{0u, 0u, 0u, 0u};
-      if (t0 + vtok + 16 * i >= kend) stV[i] = u32x4_t{0u, 0u, 0u, 0u};
+    for (int i = 0; i < CPT; ++i) {
+      stK[i] = __builtin_amdgcn_raw_buffer_load_b128(
+          rK, (kdim + (NT / 8) * i) * a.T_cap * 2 + 16 * kpart, t0 * 2, 0);
+      stV[i] = __builtin_amdgcn_raw_buffer_load_b128(
+          rV, (vtok + (NT / 16) * i) * 256 + 16 * vpart, t0 * 256, 0);
     }
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<u32x4_t *>(&sK[buf][(kdim + 32 * i) * KROW + 8 * kpart]) = stK[i];
-      *reinterpret_cast<u32x4_t *>(&sV[buf][(vtok + 16 * i) * VROW + 8 * vpart]) = stV[i];
+    for (int i = 0; i < CPT; ++i) {
+      *reinterpret_cast<u32x4_t *>(&sK[buf][(kdim + (NT / 8) * i) * KROW + 8 * kpart]) = stK[i];
+      *reinterpret_cast<u32x4_t *>(&sV[buf][(vtok + (NT / 16) * i) * VROW + 8 * vpart]) = stV[i];
     }
   };
 
@@ -255,17 +255,23 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
   // V: row (token) 32 tb + 16 s + 4 (g16 / 2) + 8 j + s16 / 4, column (dim) 32 db + 16 (g16 % 2) + 4 (s16 % 4)
   const int v_off = (4 * (g16 >> 1) + (s16 >> 2)) * VROW + 16 * (g16 & 1) + 4 * (s16 & 3);
 
-  f32x16_t acc_o[2][4];
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+  f32x16_t acc_o[QB][4];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
+  for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc_o[qb][db][r] = 0.0f;
-  float m_i[2] = {-INFINITY, -INFINITY}, l_i[2] = {0.0f, 0.0f};
+  float m_i[QB], l_i[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m_i[qb] = -INFINITY;
+    l_i[qb] = 0.0f;
+  }
 
   load_tile(0);
-  zero_tail(0);
   store_tile(0);
   __syncthreads();
 
@@ -277,10 +283,10 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
 
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {  // 32-token halves of the tile, one after the other
-      // ---- S^T = K'^T Q'^T for the 32 tokens x 2 query blocks
-      f32x16_t acc_s[2];
+      // ---- S^T = K'^T Q'^T for the 32 tokens x QB query blocks
+      f32x16_t acc_s[QB];
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
+      for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc_s[qb][r] = 0.0f;
 #pragma unroll
@@ -288,16 +294,16 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
         const bf16_t *p = kt + 16 * m * KROW + 32 * tb;
         const bf16x8_t av = lds_tr_pair(p, p + 4 * KROW);
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
+        for (int qb = 0; qb < QB; ++qb)
           acc_s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
               av, __builtin_bit_cast(bf16x8_t, qreg[qb][m]), acc_s[qb], 0, 0, 0);
       }
 
       // ---- causal mask, online softmax (log2 units), probabilities as bf16 B operands
       const int tok0 = t0 + 32 * tb;
-      uint32_t pk[2][2][4];  // [qb][16-token step][packed pair]
+      uint32_t pk[QB][2][4];  // [qb][16-token step][packed pair]
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
+      for (int qb = 0; qb < QB; ++qb) {
         if (tok0 + 31 > pos_first + 32 * qb) {  // the block reaches past some row's position
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
@@ -307,8 +313,12 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
         }
         float mx = acc_s[qb][0];
 #pragma unroll
-        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, acc_s[qb][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        for (int r = 1; r < 16; ++r) mx = __builtin_fmaxf(mx, acc_s[qb][r]);
+        {  // lanes l and l ^ 32 hold the two halves of a row's scores
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx),
+                                                           __float_as_uint(mx), false, false);
+          mx = __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        }
         // the running max moves only when a score exceeds it by more than the slack, so the
         // probabilities stay <= 2^slack and the rescale of O is rare after the first block
         const bool grow = mx > m_i[qb] + RESCALE_SLACK;
@@ -322,18 +332,17 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
             for (int r = 0; r < 16; ++r) acc_o[qb][db][r] *= alpha;
           m_i[qb] = m_new;
         }
-        float rs = 0.0f;
 #pragma unroll
         for (int s = 0; s < 2; ++s)
 #pragma unroll
           for (int x = 0; x < 4; ++x) {
             const int r0 = 8 * s + 2 * x;
-            const float p0 = __builtin_amdgcn_exp2f(acc_s[qb][r0] - m_i[qb]);
-            const float p1 = __builtin_amdgcn_exp2f(acc_s[qb][r0 + 1] - m_i[qb]);
-            rs += p0 + p1;
-            pk[qb][s][x] = pack_bf16x2(p0, p1);
+            pk[qb][s][x] = pack_bf16x2(__builtin_amdgcn_exp2f(acc_s[qb][r0] - m_i[qb]),
+                                       __builtin_amdgcn_exp2f(acc_s[qb][r0 + 1] - m_i[qb]));
+            // the row sum takes the rounded weights, the ones P V multiplies
+            l_i[qb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[qb][s][x]),
+                                                      ones, l_i[qb], false);
           }
-        l_i[qb] += rs;
       }
 
       // ---- O^T += V^T P^T over the 32 tokens
@@ -344,7 +353,7 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
           const bf16_t *p = vt + (32 * tb + 16 * s) * VROW + 32 * db;
           const bf16x8_t av = lds_tr_pair(p, p + 8 * VROW);
 #pragma unroll
-          for (int qb = 0; qb < 2; ++qb) {
+          for (int qb = 0; qb < QB; ++qb) {
             const u32x4_t bv = {pk[qb][s][0], pk[qb][s][1], pk[qb][s][2], pk[qb][s][3]};
             acc_o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                 av, __builtin_bit_cast(bf16x8_t, bv), acc_o[qb][db], 0, 0, 0);
@@ -352,18 +361,17 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
         }
     }
 
-    if (t + 1 < ntile) {
-      zero_tail(t0 + KT);
-      store_tile(buf ^ 1);
-    }  // that buffer was last read before the previous barrier
+    if (t + 1 < ntile) store_tile(buf ^ 1);  // that buffer was last read before the previous barrier
     __syncthreads();
   }
 
   // ---- normalise and write: lane l owns query row l % 32, dims db*32 + 8(r/4) + 4(l/32) + r%4
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int rl = pb * 64 + qb * 32 + (lane & 31);
-    const float inv = 1.0f / (l_i[qb] + __shfl_xor(l_i[qb], 32, 64));
+  for (int qb = 0; qb < QB; ++qb) {
+    const int rl = pb * ROWS + qb * 32 + (lane & 31);
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_i[qb]),
+                                                     __float_as_uint(l_i[qb]), false, false);
+    const float inv = 1.0f / (__uint_as_float(sw[0]) + __uint_as_float(sw[1]));
     if (rl < a.Lq) {
       float *orow = a.out + ((static_cast<size_t>(b) * a.Hq + head) * a.Lq + rl) * 128;
 #pragma unroll
@@ -413,10 +421,15 @@ hipError_t launch_prefill(const void *kp, const void *v, int B, int Hq, int Hkv,
   a.pos0 = pos0;
   const int G = Hq / Hkv;
   a.qh = G < 4 ? G : 4;
-  const int rows_per_wg = 64 * (4 / a.qh);
+  const int rows_per_wg = 256 / a.qh;  // 256 query rows per workgroup over qh heads
   a.nqb = (Lq + rows_per_wg - 1) / rows_per_wg;
   const int grid = a.nqb * (G / a.qh) * B * Hkv;
-  prefill_attn_kernel<<<dim3(grid), dim3(256), 0, s>>>(a);
+#ifdef AQUA_PREFILL_QB
+  constexpr int QB = AQUA_PREFILL_QB;
+#else
+  constexpr int QB = 1;
+#endif
+  prefill_attn_kernel<QB, 8 / QB><<<dim3(grid), dim3(64 * (8 / QB)), 0, s>>>(a);
   return hipGetLastError();
 }
 
