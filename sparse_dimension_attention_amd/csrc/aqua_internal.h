@@ -9,7 +9,8 @@ namespace aqua {
 
 // ------------------------------------------------------------------ bf16 storage helpers
 // bf16 is the upper half of an fp32 bit pattern.  Widening is exact; narrowing rounds to
-// nearest with ties to even by adding 0x7fff plus the lowest kept bit before truncation.
+// nearest with ties to even (v_cvt_pk_bf16_f32: branch-free; identical to adding 0x7fff plus
+// the lowest kept bit and truncating, for every finite input).
 __device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t pair) {
   return __uint_as_float(pair & 0xffff0000u);
@@ -17,11 +18,14 @@ __device__ __forceinline__ float bf16_hi(uint32_t pair) {
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
+// Two fp32 values to a bf16 pair (lo in bits 0-15), round to nearest even.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{lo, hi}), bf16x2_t));
+}
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);  // NaN
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return static_cast<uint16_t>(pack_bf16x2(f, 0.0f) & 0xffffu);
 }
 
 // Storage element types: float (AQUA_F32) or raw bf16 bits (AQUA_BF16).

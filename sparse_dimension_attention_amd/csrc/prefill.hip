@@ -44,12 +44,14 @@ typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 // l + 64).
 constexpr int SQS = 128 + 8;  // LDS row stride (floats) of the q' tile
 
+
 __device__ __forceinline__ void split3(float p, uint32_t &h, uint32_t &m, uint32_t &l) {
-  h = f32_to_bf16_rne(p);
+  const uint32_t hm = pack_bf16x2(p, 0.0f);
+  h = hm & 0xffffu;
   const float r1 = p - bf16_to_f32(static_cast<uint16_t>(h));
-  m = f32_to_bf16_rne(r1);
+  m = pack_bf16x2(r1, 0.0f) & 0xffffu;
   const float r2 = r1 - bf16_to_f32(static_cast<uint16_t>(m));
-  l = f32_to_bf16_rne(r2);
+  l = pack_bf16x2(r2, 0.0f) & 0xffffu;
 }
 
 __global__ __launch_bounds__(256) void prefill_select_kernel(const bf16_t *__restrict__ q, int N,
@@ -59,6 +61,7 @@ __global__ __launch_bounds__(256) void prefill_select_kernel(const bf16_t *__res
                                                              uint32_t *__restrict__ mask,
                                                              bf16_t *__restrict__ qm) {
   __shared__ __align__(16) float sQ[2][32 * SQS];
+  __shared__ __align__(16) bf16_t sM[4 * 8 * 128];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int col = 32 * w + (lane & 31);
   // B operands: P[16 m + 8 (lane / 32) + e][col], e = 0..7, in three bf16 parts
@@ -76,15 +79,20 @@ __global__ __launch_bounds__(256) void prefill_select_kernel(const bf16_t *__res
                     lo[6] | lo[7] << 16};
   }
   const int nblk = (N + 31) / 32;
+  bf16_t *qrows = sM + 8 * 128 * w;  // this wavefront's 8 rows of qm, staged for 16-byte stores
+  // A operands of the first block; each block then loads the next one's before selecting
+  u32x4_t av[8];
+  auto load_rows = [&](int blk) {
+    const int arow = min(blk * 32 + (lane & 31), N - 1);
+    const bf16_t *qa = q + static_cast<size_t>(arow) * 128 + 8 * (lane >> 5);
+#pragma unroll
+    for (int m = 0; m < 8; ++m) av[m] = *reinterpret_cast<const u32x4_t *>(qa + 16 * m);
+  };
+  if (blockIdx.x < nblk) load_rows(blockIdx.x);
   int buf = 0;
   for (int blk = blockIdx.x; blk < nblk; blk += gridDim.x, buf ^= 1) {
     const int r0 = blk * 32;
     // ---- projection: rows r0 .. r0+31 (clamped), columns [32w, 32w+32)
-    const int arow = min(r0 + (lane & 31), N - 1);
-    const bf16_t *qa = q + static_cast<size_t>(arow) * 128 + 8 * (lane >> 5);
-    u32x4_t av[8];
-#pragma unroll
-    for (int m = 0; m < 8; ++m) av[m] = *reinterpret_cast<const u32x4_t *>(qa + 16 * m);
     f32x16_t acc_h, acc_l;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -105,12 +113,14 @@ __global__ __launch_bounds__(256) void prefill_select_kernel(const bf16_t *__res
 #pragma unroll
     for (int r = 0; r < 16; ++r)
       tile[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * SQS + col] = acc_h[r] + acc_l[r];
+    if (blk + static_cast<int>(gridDim.x) < nblk) load_rows(blk + gridDim.x);
     __syncthreads();
     // ---- selection: wavefront w takes rows 8w .. 8w+7 of the block
-    for (int rr = 8 * w; rr < 8 * w + 8; ++rr) {
-      const int row = r0 + rr;
-      if (row >= N) break;  // uniform over the wavefront
-      const float x[2] = {tile[rr * SQS + lane], tile[rr * SQS + lane + 64]};
+    const int nrows = min(8, N - (r0 + 8 * w));  // uniform over the wavefront
+    for (int rr = 0; rr < nrows; ++rr) {
+      const int row = r0 + 8 * w + rr;
+      const float *tr = tile + (8 * w + rr) * SQS;
+      const float x[2] = {tr[lane], tr[lane + 64]};
       bool sel[2];
       wave_topk_threshold<2>(x, d_sel, k, sel);
       const uint64_t s0 = __ballot(sel[0]), s1 = __ballot(sel[1]);
@@ -119,11 +129,24 @@ __global__ __launch_bounds__(256) void prefill_select_kernel(const bf16_t *__res
         mask[static_cast<size_t>(row) * 4 + lane] =
             (lane & 1) ? static_cast<uint32_t>(bb >> 32) : static_cast<uint32_t>(bb);
       }
+      if (q_proj) {
+        q_proj[static_cast<size_t>(row) * 128 + lane] = x[0];
+        q_proj[static_cast<size_t>(row) * 128 + lane + 64] = x[1];
+      }
+      const uint32_t pair = pack_bf16x2(sel[0] ? x[0] * qscale : 0.0f, sel[1] ? x[1] * qscale : 0.0f);
+      qrows[rr * 128 + lane] = static_cast<bf16_t>(pair & 0xffffu);
+      qrows[rr * 128 + lane + 64] = static_cast<bf16_t>(pair >> 16);
+    }
+    // the wavefront's rows of qm are contiguous in HBM: 16-byte stores (LDS is in order within
+    // a wavefront, so the values written above are read back here)
+    if (nrows > 0) {
+      bf16_t *dst = qm + static_cast<size_t>(r0 + 8 * w) * 128;
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const size_t at = static_cast<size_t>(row) * 128 + lane + 64 * e;
-        if (q_proj) q_proj[at] = x[e];
-        qm[at] = sel[e] ? f32_to_bf16_rne(x[e] * qscale) : static_cast<bf16_t>(0);
+      for (int h = 0; h < 2; ++h) {
+        const int c = lane + 64 * h;  // 16-byte chunk: row c / 16
+        if (c < nrows * 16)
+          *reinterpret_cast<u32x4_t *>(dst + 8 * c) =
+              *reinterpret_cast<const u32x4_t *>(qrows + 8 * c);
       }
     }
     // the next block writes the other tile; the barrier above it orders this block's reads
@@ -167,13 +190,6 @@ __device__ __forceinline__ bf16x8_t lds_tr_pair(const bf16_t *p0, const bf16_t *
   const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t *)(p0));
   const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t *)(p1));
   return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-
-// Two fp32 values to a bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  typedef float f32x2_t __attribute__((ext_vector_type(2)));
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{lo, hi}), bf16x2_t));
 }
 
 // QB: 32-row query blocks per wavefront; NW: wavefronts per workgroup (QB * NW = 8, so a
