@@ -13,6 +13,15 @@ roofline = algorithmic HBM bytes of the step's launch (the K' rows of each KV gr
 and all of V over the context, raw q, the new token in and out, P, output) / its average
 duration from HIP events on the launch stream.
 cpu_baseline = the fp64 oracle timed on the host cores on a bounded sample of the same step.
+
+Two further workloads are measured beside the headline and reported in the same line:
+ * prefill: causal chunked prefill of 16384 tokens in 8 chunks of 2048 (32 heads, k=96), each
+   chunk = aqua_prefill_chunk (selection + MFMA attention); executed-useful flops
+   Hq * 4 d * T (T + 1) / 2 against the bf16 MFMA peak;
+ * h2o: 64 heavy-hitter decode steps over a compact AQUA-Memory cache of 1024 heavy + 256
+   recent slots (32768-token context, 96 stored dims, top-64), each step = eviction, slot
+   append, selection and mass-mode decode; timed from a Python loop and as a replayed HIP graph
+   of the 64 steps (launch-bound: about 4.6 MB per step, cache-resident).
 """
 from __future__ import annotations
 
@@ -31,9 +40,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 import sparse_dimension_attention_amd as aq  # noqa: E402
-from synth import config, make_decode_inputs  # noqa: E402
+from synth import config, make_decode_inputs, make_h2o_inputs, make_prefill_inputs  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
 METRIC = "AQUA decode attn: query-heads·tokens/s and achieved HBM GB/s vs peak (k=96)"
 
 
@@ -66,18 +76,27 @@ def decode_bytes(U: np.ndarray, c: dict, T: int) -> int:
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_llama8b_b16_t8192_hbm_traffic.md")
 
 
+def kernel_source_hash() -> str:
+    """sha256[:16] over the decode kernel's sources (decode.hip, then aqua_internal.h)."""
+    import hashlib
+
+    csrc = os.path.join(ROOT, "sparse_dimension_attention_amd", "csrc")
+    h = hashlib.sha256()
+    for f in ("decode.hip", "aqua_internal.h"):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
 def traffic_bytes(path: str):
     """HBM bytes per launch of the decode kernel from the committed counter summary, if it was
     taken on the current kernel source (its hash is recorded there); else None."""
-    import hashlib
     import re
 
     if not os.path.exists(TRAFFIC_FILE):
         return None
     text = open(TRAFFIC_FILE).read()
-    src = os.path.join(ROOT, "sparse_dimension_attention_amd", "csrc", "decode.hip")
-    h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    m = re.search(r"decode\.hip sha256\[:16\]: `([0-9a-f]+)`", text)
+    h = kernel_source_hash()
+    m = re.search(r"kernel source sha256\[:16\]: `([0-9a-f]+)`", text)
     t = re.search(rf"traffic_{path}_bytes_per_launch: `(\d+)`", text)
     if not m or m.group(1) != h or not t:
         return None
@@ -132,6 +151,127 @@ def copy_probe(nbytes: int, reps: int):
     print(json.dumps({"copy_probe_bytes": nbytes, "reps": reps}))
 
 
+def bench_prefill(dev, reps: int):
+    """The 16384-token causal prefill in 8 chunks of 2048 (inputs resident in HBM)."""
+    c = config(4)
+    B, Hq, Hkv, d, T, k, chunk = c["B"], c["Hq"], c["Hkv"], c["d"], c["T"], c["k"], c["chunk"]
+    inp = make_prefill_inputs(c, workers=16)
+    P = inp["P"].to(dev)
+    kp = torch.empty(B, Hkv, d, T, dtype=torch.bfloat16, device=dev)
+    v = torch.empty(B, Hkv, T, d, dtype=torch.bfloat16, device=dev)
+    cache = aq.make_cache(kp, v, 0)
+    aq.aqua_project_keys(cache, inp["k"].to(dev), inp["v"].to(dev), P, T)
+    qs = [inp["q"][:, :, c0:c0 + chunk].contiguous().to(dev) for c0 in range(0, T, chunk)]
+    del inp
+    out = torch.empty(B, Hq, chunk, d, device=dev)
+    ws = torch.empty(aq.aqua_prefill_workspace(cache, Hq, chunk), dtype=torch.uint8, device=dev)
+    scale = 1.0 / math.sqrt(d)
+
+    def run(events):
+        for i, c0 in enumerate(range(0, T, chunk)):
+            if events is not None:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+            aq.aqua_prefill_chunk(cache, Hq, qs[i], chunk, c0, P, d, k, scale, out, ws=ws)
+            if events is not None:
+                e1.record()
+                events.append((e0, e1))
+
+    run(None)
+    torch.cuda.synchronize()
+    per_rep = []
+    for _ in range(reps):
+        ev = []
+        run(ev)
+        torch.cuda.synchronize()
+        per_rep.append([a.elapsed_time(b) for a, b in ev])
+    totals = [sum(r) for r in per_rep]
+    med = int(np.argsort(totals)[len(totals) // 2])
+    ms = totals[med]
+    flops = Hq * 4 * d * T * (T + 1) / 2 * B
+    tflops = flops / (ms * 1e-3) / 1e12
+    return {"workload": c["name"], "chunks": T // chunk, "chunk": chunk, "ms": ms,
+            "per_chunk_ms": per_rep[med], "reps": reps,
+            "flops_executed_useful": flops, "tflops": tflops,
+            "frac_bf16_mfma_peak": tflops / BF16_MFMA_PEAK_TFLOPS,
+            "timing": "HIP events around each aqua_prefill_chunk on the launch stream; median rep"}
+
+
+def bench_h2o(dev, reps: int):
+    """64 heavy-hitter decode steps over a compact AQUA-Memory cache."""
+    from sparse_dimension_attention_amd.h2o import H2OCache
+
+    c = config(5)
+    B, Hq, Hkv, d, T, S = c["B"], c["Hq"], c["Hkv"], c["d"], c["T"], c["steps"]
+    inp = make_h2o_inputs(c, workers=16)
+    P = inp["P"].to(dev)
+    kp = torch.empty(B, Hkv, c["d_store"], T, dtype=torch.bfloat16, device=dev)
+    v = torch.empty(B, Hkv, T, d, dtype=torch.bfloat16, device=dev)
+    full = aq.make_cache(kp, v, 0)
+    aq.aqua_project_keys(full, inp["k"].to(dev), inp["v"].to(dev), P, T)
+    scale = 1.0 / math.sqrt(d)
+    qp = torch.empty(B, Hq, d, device=dev)
+    mask = torch.empty(B, Hq, d // 32, dtype=torch.int32, device=dev)
+    out = torch.empty(B, Hq, d, device=dev)
+    aq.aqua_select_dims(inp["q_seed"].to(dev), P, c["d_sel"], c["k"], qp, mask)
+    mass = torch.zeros(B, Hkv, T, device=dev)
+    ws = torch.zeros(aq.aqua_decode_workspace(full, Hq), dtype=torch.uint8, device=dev)
+    aq.aqua_decode(full, Hq, qp, mask, scale, out, ws, mass=mass)  # the seeding step
+    st = H2OCache.from_full(kp, v, mass, T, c["heavy"], c["recent"])
+    st.workspace(Hq)
+    del kp, v, mass, full, ws
+    qs, ks, vs = (inp[x].to(dev) for x in ("q_steps", "k_steps", "v_steps"))
+
+    def steps():
+        for s in range(S):
+            st.step(qs[s], ks[s], vs[s], P, T + s, c["d_sel"], c["k"], scale, out, qp, mask)
+
+    steps()
+    torch.cuda.synchronize()
+    loop_us = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        steps()
+        e1.record()
+        torch.cuda.synchronize()
+        loop_us.append(e0.elapsed_time(e1) * 1e3 / S)
+    rec = {"workload": c["name"], "steps": S, "slots": c["heavy"] + c["recent"],
+           "us_per_step_python_loop": statistics.median(loop_us)}
+    try:  # the same 64 steps captured once and replayed (no host work inside)
+        g = torch.cuda.CUDAGraph()
+        s_cap = torch.cuda.Stream()
+        with torch.cuda.stream(s_cap):
+            with torch.cuda.graph(g, stream=s_cap):
+                steps()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        graph_us = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            graph_us.append(e0.elapsed_time(e1) * 1e3 / S)
+        rec["us_per_step_graph"] = statistics.median(graph_us)
+    except Exception as exc:  # report, do not fail the headline
+        rec["us_per_step_graph"] = None
+        rec["graph_error"] = str(exc)[:200]
+    U = union_rows(mask.cpu().numpy().reshape(B, Hq, d // 32), B, Hkv, Hq // Hkv, d,
+                   c["d_store"])
+    slots = c["heavy"] + c["recent"]
+    nbytes = (int(U.sum()) * slots * 2 + B * Hkv * slots * d * 2 + B * Hkv * slots * 8
+              + B * Hq * d * 2 + B * Hkv * 2 * d * 2 + B * Hq * d * 4)
+    best = rec["us_per_step_graph"] or rec["us_per_step_python_loop"]
+    rec["bytes_per_step"] = nbytes
+    rec["gbs"] = nbytes / (best * 1e-6) / 1e9
+    rec["note"] = ("launch-bound (4 launches per step, working set cache-resident); GB/s is "
+                   "algorithmic bytes per step / step time")
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -143,6 +283,11 @@ def main():
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES")
     ap.add_argument("--only", choices=("fused", "three"), default=None,
                     help="run one step implementation only, untimed (for counter runs)")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the prefill and H2O workloads")
+    ap.add_argument("--secondary-only", choices=("prefill", "h2o"), default=None,
+                    help="run only that workload and print its record (for profiler runs)")
+    ap.add_argument("--secondary-reps", type=int, default=5)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the AQUA decode path here runs on a single MI355X "
@@ -158,6 +303,10 @@ def main():
         return
 
     dev = torch.device("cuda:0")
+    if args.secondary_only:
+        fn = bench_prefill if args.secondary_only == "prefill" else bench_h2o
+        print(json.dumps({args.secondary_only: fn(dev, args.secondary_reps)}))
+        return
     c = config(2)
     B, Hq, Hkv, d, T, k = c["B"], c["Hq"], c["Hkv"], c["d"], c["T"], c["k"]
     G = Hq // Hkv
@@ -253,6 +402,12 @@ def main():
         "ms_per_step_by_path": {p: res[p][0] for p in res},
         "kernel_us_by_path": {p: statistics.mean(res[p][1]) * 1e3 for p in res},
     }
+    del kp, v, cache, ws
+    torch.cuda.empty_cache()
+    if not args.no_secondary:
+        rec["prefill"] = bench_prefill(dev, args.secondary_reps)
+        torch.cuda.empty_cache()
+        rec["h2o"] = bench_h2o(dev, args.secondary_reps)
     if not args.no_cpu:
         rec["cpu_baseline"] = cpu_baseline(c, args.cpu_groups, args.cpu_reps)
     print(json.dumps(rec))

@@ -154,11 +154,14 @@ __global__ __launch_bounds__(256) void prefill_select_kernel(const bf16_t *__res
 }
 
 // ------------------------------------------------------------------ 2. attention
-// Workgroup = 4 wavefronts; a wavefront owns one query head and 64 consecutive positions (two
-// 32-row MFMA blocks that share every K'/V operand read).  The 4 wavefronts cover the heads of
-// one KV group (or, for G < 4, several position blocks), so each 64-token K'/V tile is staged in
-// LDS once for 256 query rows.  Tiles are double-buffered: the global loads of tile t+1 are in
-// flight while tile t is computed, and one barrier per tile hands the buffers over.
+// A workgroup holds 256 query rows: QB 32-row MFMA blocks per wavefront times NW wavefronts
+// (QB * NW = 8).  The launched form is QB = 1, NW = 8: two wavefronts per SIMD, each owning 32
+// consecutive positions of one head, so one wavefront's softmax can overlap the other's MFMAs;
+// QB = 2, NW = 4 (one wavefront per SIMD, every K'/V operand read feeding two MFMAs) measured
+// slower.  The wavefronts cover the heads of one KV group (or, for G < 4, several position
+// blocks), so each 64-token K'/V tile is staged in LDS once for the 256 rows.  Tiles are
+// double-buffered: the global loads of tile t+1 are in flight while tile t is computed, and one
+// barrier per tile hands the buffers over.
 //
 // Operands come out of LDS with ds_read_b64_tr_b16, which within each 16-lane group reads a
 // 4-row x 16-column block of 16-bit elements (lane s of the group supplying the address of row
