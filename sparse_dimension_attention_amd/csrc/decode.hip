@@ -92,6 +92,18 @@ struct DecodeSmem {
   static constexpr int BYTES = OFF_ML + 2 * G * 4 + 16;
 };
 
+// Two workgroups share each CU, and the issue arbiter favours older wavefronts: left alone, the
+// first workgroup on a CU streams its rows faster and finishes early, and the CU runs the rest
+// of the launch half occupied.  Each wavefront therefore lowers its priority as it progresses
+// (3 in its first quarter of batches, 0 in its last), so that the one behind is served first.
+__device__ __forceinline__ void progress_priority(int done, int total) {
+  const int q = total > 0 ? (4 * done) / total : 3;
+  if (q <= 0) __builtin_amdgcn_s_setprio(3);
+  else if (q == 1) __builtin_amdgcn_s_setprio(2);
+  else if (q == 2) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
 // Two workgroups per CU must stay resident (the decode streams at full bandwidth only then):
 // at least two waves per SIMD, i.e. at most 256 VGPRs.
 template <typename KT, int D, int G, int NW, bool FUSED>
@@ -138,7 +150,7 @@ void decode_kernel(DecodeArgs a) {
     {
       // P into LDS in chunks of CH 16-byte loads per thread (each chunk one L2 round trip)
       constexpr int NV = D * D / (NT * 4);
-      constexpr int CH = NV < 4 ? NV : 4;
+      constexpr int CH = NV < 16 ? NV : 16;
 #pragma unroll
       for (int v0 = 0; v0 < NV; v0 += CH) {
         float4 st[CH];
@@ -173,11 +185,19 @@ void decode_kernel(DecodeArgs a) {
         acc[r] = 0.0f;
         row[r] = min(r0 + r * RSTEP, G);
       }
-#pragma unroll 16
-      for (int j = 0; j < D; ++j) {
-        const float p = sP[j * D + i];
+#pragma unroll 8
+      for (int j = 0; j < D; j += 4) {
+        float p[4];
 #pragma unroll
-        for (int r = 0; r < RPT; ++r) acc[r] = fmaf(sq[row[r]][j], p, acc[r]);
+        for (int c = 0; c < 4; ++c) p[c] = sP[(j + c) * D + i];
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) {
+          const float4 q4 = *reinterpret_cast<const float4 *>(&sq[row[r]][j]);  // broadcast
+          acc[r] = fmaf(q4.x, p[0], acc[r]);
+          acc[r] = fmaf(q4.y, p[1], acc[r]);
+          acc[r] = fmaf(q4.z, p[2], acc[r]);
+          acc[r] = fmaf(q4.w, p[3], acc[r]);
+        }
       }
 #pragma unroll
       for (int r = 0; r < RPT; ++r)
@@ -195,7 +215,7 @@ void decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int e = 0; e < E; ++e) x[e] = s_qp[h][lane + 64 * e];
       bool sel[E];
-      wave_topk<E>(x, a.d_sel, a.k, sel);
+      wave_topk_threshold<E>(x, a.d_sel, a.k, sel);
       uint64_t sb[E];
 #pragma unroll
       for (int e = 0; e < E; ++e) sb[e] = __ballot(sel[e]);
@@ -312,6 +332,7 @@ void decode_kernel(DecodeArgs a) {
     uint4 kA[kUnroll], kB[kUnroll];
     AQUA_K_LOAD(kA, 0);
     for (int bi = 0; bi < nbat; bi += 2) {
+      progress_priority(bi, nbat + WT / (TPI * kUnroll));
       AQUA_K_LOAD(kB, bi + 1);
       __builtin_amdgcn_sched_barrier(0);
       AQUA_K_FMA(kA, bi);
@@ -424,6 +445,7 @@ void decode_kernel(DecodeArgs a) {
     uint4 vA[kUnroll], vB[kUnroll];
     AQUA_V_LOAD(vA, 0);
     for (int bi = 0; bi < vbat; bi += 2) {
+      progress_priority(nbat + bi, nbat + WT / (TPI * kUnroll));
       AQUA_V_LOAD(vB, bi + 1);
       __builtin_amdgcn_sched_barrier(0);
       AQUA_V_FMA(vA, bi);
@@ -434,6 +456,7 @@ void decode_kernel(DecodeArgs a) {
   }
 #undef AQUA_V_LOAD
 #undef AQUA_V_FMA
+  __builtin_amdgcn_s_setprio(0);
   if (new_here && sub == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h)
