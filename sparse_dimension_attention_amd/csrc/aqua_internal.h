@@ -56,67 +56,13 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 // Top-k of one row of D = 64 * E values held by a wavefront, lane l holding dims l + 64 e.
 // Magnitudes are compared exactly, as the fp32 bit patterns with the sign cleared (+0 and -0
-// tie, denormals are not flushed); equal magnitudes go to the lower index.  MSB-first radix
-// select with wave ballots: at each bit the candidates with the bit set are either all kept
-// (when they do not exceed the number still needed) or become the only candidates; it stops as
-// soon as the candidates left are exactly the number still needed, and whatever ties after the
-// last bit is filled in index order (mbcnt prefix).  Exactly k flags are set, all at dims
-// < d_sel (callers guarantee 1 <= k <= d_sel <= D).
-template <int E>
-__device__ __forceinline__ void wave_topk(const float (&x)[E], int d_sel, int k, bool (&sel)[E]) {
-  const int lane = threadIdx.x & 63;
-  uint32_t u[E];
-  bool cand[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    u[e] = __float_as_uint(x[e]) & 0x7fffffffu;
-    cand[e] = (lane + 64 * e) < d_sel;
-    sel[e] = false;
-  }
-  int need = k;
-  for (int bit = 30; bit >= 0; --bit) {
-    bool hi[E];
-    int cnt = 0;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      hi[e] = cand[e] && ((u[e] >> bit) & 1u);
-      cnt += __popcll(__ballot(hi[e]));
-    }
-    if (cnt <= need) {
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        sel[e] = sel[e] || hi[e];
-        cand[e] = cand[e] && !hi[e];
-      }
-      need -= cnt;
-    } else {
-#pragma unroll
-      for (int e = 0; e < E; ++e) cand[e] = hi[e];
-    }
-    int left = 0;
-#pragma unroll
-    for (int e = 0; e < E; ++e) left += __popcll(__ballot(cand[e]));
-    if (left <= need || need == 0) break;
-  }
-  if (need > 0) {
-    int before = 0;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const uint64_t b = __ballot(cand[e]);
-      const int rank = before + static_cast<int>(__builtin_amdgcn_mbcnt_hi(
-                                    static_cast<uint32_t>(b >> 32),
-                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(b), 0u)));
-      if (cand[e] && rank < need) sel[e] = true;
-      before += __popcll(b);
-    }
-  }
-}
-
-// The same top-k by a threshold search: the k-th largest key T is built MSB first (keep bit b
-// of T iff at least k keys are >= T | bit b), stopping early once exactly k keys are >= the
-// running threshold.  Keys of dims >= d_sel are -1, below every magnitude.  If the search ends
-// with more than k keys >= T (ties at T), the keys > T are kept and the ties are taken in index
-// order.  Per bit: two compares and two ballot popcounts, the rest is scalar.
+// tie, denormals are not flushed); equal magnitudes go to the lower index.  Exactly k flags are
+// set, all at dims < d_sel (callers guarantee 1 <= k <= d_sel <= 64 E).
+// Threshold search: the k-th largest key T is built MSB first (keep bit b of T iff at least k
+// keys are >= T | bit b), stopping early once exactly k keys are >= the running threshold.
+// Keys of dims >= d_sel are -1, below every magnitude.  If the search ends with more than k
+// keys >= T (ties at T), the keys > T are kept and the ties are taken in index order.  Per
+// bit: two compares and two ballot popcounts, the rest is scalar.
 template <int E>
 __device__ __forceinline__ void wave_topk_threshold(const float (&x)[E], int d_sel, int k,
                                                     bool (&sel)[E]) {

@@ -24,8 +24,8 @@
 //
 // The fused decode step (FUSED) does a whole step in this one launch: each workgroup stages P in
 // LDS, projects its group's raw queries (and, in the workgroup that holds the new position, the
-// new key), selects every head's top-k dims with wave_topk, appends the new token's K' and V to
-// the cache, and attends over the cached tokens plus the new one, taken from LDS.
+// new key), selects every head's top-k dims with wave_topk_threshold, appends the new token's
+// K' and V to the cache, and attends over the cached tokens plus the new one, taken from LDS.
 #include "aqua_internal.h"
 
 namespace aqua {
@@ -117,7 +117,7 @@ void decode_kernel(DecodeArgs a) {
   constexpr int TPI = 64 / LPT;    // V rows per wavefront load
   constexpr int NWORD = SM::NWORD;
   constexpr int NT = NW * 64;
-  constexpr int E = D / 64;        // dims per lane in wave_topk
+  constexpr int E = D / 64;        // dims per lane in the top-k
   constexpr int SPLIT = NW * WT;   // tokens per workgroup
   static_assert(WT % (TPI * kUnroll) == 0, "V loop tiling");
   static_assert(D <= WT, "LDS reuse of the numerator buffer for the wave merge");

@@ -11,8 +11,9 @@
 // loads (one round trip to L2 instead of one per row j), then each wavefront reads P's rows
 // from LDS (consecutive lanes, consecutive banks).
 //
-// Selection: wave_topk (exact comparison of sign-cleared fp32 bit patterns, ties to the lower
-// index, wave-ballot radix select).
+// Selection: wave_topk_threshold (exact comparison of sign-cleared fp32 bit patterns, ties to
+// the lower index; the k-th largest key built MSB first from wave ballots, stopping as soon as
+// exactly k keys clear the running threshold).
 #include "aqua_internal.h"
 
 namespace aqua {
@@ -58,7 +59,7 @@ __global__ __launch_bounds__(256) void select_kernel(const QT *__restrict__ q, i
   }
 
   bool sel[E];
-  wave_topk<E>(acc, d_sel, k, sel);
+  wave_topk_threshold<E>(acc, d_sel, k, sel);
 
   // ---- outputs
   uint64_t sb[E];
