@@ -142,7 +142,6 @@ aqua_status aqua_decode(const aqua_cache *c, int32_t Hq, const float *q_proj,
   if (ws_bytes < need)
     return fail(AQUA_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, need);
 
-  const aqua::DecodeLayout L = aqua::decode_layout(c->dtype, Hq / c->Hkv);
   aqua::DecodeArgs a{};
   a.kp = c->kp;
   a.v = c->v;
@@ -159,7 +158,7 @@ aqua_status aqua_decode(const aqua_cache *c, int32_t Hq, const float *q_proj,
   a.d_store = c->d_store;
   a.T_cap = c->T_cap;
   a.len = c->len;
-  a.S = (c->len + L.split - 1) / L.split;
+  a.S = aqua::decode_splits(c->dtype, Hq / c->Hkv, c->len);
   a.qscale = scale * 1.4426950408889634f;  // log2(e): scores are kept in log2 units
   return hip_status(aqua::launch_decode(c->dtype, a, static_cast<hipStream_t>(stream)),
                     "aqua_decode launch");

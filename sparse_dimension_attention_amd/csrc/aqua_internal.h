@@ -141,6 +141,11 @@ struct DecodeLayout {
 
 // Launch geometry of the decode kernel for a storage dtype (0 f32, 1 bf16) and group size.
 DecodeLayout decode_layout(int dtype, int G);
+// aqua_decode takes the short-context kernel (workgroups of 256 tokens that split the union of
+// K' rows over their wavefronts) up to this many tokens, the split-T kernel above it.
+constexpr int kDecodeShortMax = 4096;
+bool decode_short(int len);
+int decode_splits(int dtype, int G, int len);  // partials per head that aqua_decode writes
 size_t decode_workspace_bytes(int dtype, int B, int Hq, int Hkv, int d, int T_cap);
 void decode_workspace_carve(void *ws, int dtype, int B, int Hq, int Hkv, int d, int T_cap,
                             uint32_t **counters, float **partials, float **scores);

@@ -26,6 +26,8 @@
 // LDS, projects its group's raw queries (and, in the workgroup that holds the new position, the
 // new key), selects every head's top-k dims with wave_topk_threshold, appends the new token's
 // K' and V to the cache, and attends over the cached tokens plus the new one, taken from LDS.
+#include <type_traits>
+
 #include "aqua_internal.h"
 
 namespace aqua {
@@ -91,6 +93,76 @@ struct DecodeSmem {
   static constexpr int OFF_ML = OFF_WL + NW * G * 4;                     // float [2][G]
   static constexpr int BYTES = OFF_ML + 2 * G * 4 + 16;
 };
+
+// The last workgroup of a (b, g): merge the S partials (m, l, o) of every head into the output
+// and, in mass mode, add every token's normalised probability (summed over the group's heads)
+// to its mass.  The partials and scores were written by other workgroups, possibly on other
+// XCDs, so they are read past the non-coherent caches; each thread issues up to 8 such loads
+// at once, so that the merge costs a few memory round trips rather than one per split.
+template <int D, int G, int NT>
+__device__ void merge_splits(const DecodeArgs &a, size_t head0, int bg, float *s_M, float *s_L) {
+  constexpr int CH = 8;
+  for (int e = threadIdx.x; e < G * D; e += NT) {
+    const int h = e / D, dd = e - h * D;
+    const float *part = a.partials + (head0 + h) * a.S * (D + 2);
+    float ms[CH], M = -INFINITY, O = 0.0f, L = 0.0f;
+    for (int s0 = 0; s0 < a.S; s0 += CH) {  // running (M, L, O) over chunks of CH splits
+      float ls[CH], os[CH];
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        const int sp = min(s0 + c, a.S - 1);  // past the last split: re-read it, weight 0
+        ms[c] = coherent_load(part + sp * (D + 2));
+        ls[c] = coherent_load(part + sp * (D + 2) + 1);
+        os[c] = coherent_load(part + sp * (D + 2) + 2 + dd);
+      }
+      float Mc = M;
+#pragma unroll
+      for (int c = 0; c < CH; ++c)
+        if (s0 + c < a.S) Mc = fmaxf(Mc, ms[c]);
+      const float sc = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(M - Mc);
+      O *= sc;
+      L *= sc;
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        const float al = (s0 + c >= a.S || ms[c] == -INFINITY)
+                             ? 0.0f
+                             : __builtin_amdgcn_exp2f(ms[c] - Mc);
+        L = fmaf(al, ls[c], L);
+        O = fmaf(al, os[c], O);
+      }
+      M = Mc;
+    }
+    a.out[(head0 + h) * D + dd] = O / L;
+    if (dd == 0) {
+      s_M[h] = M;
+      s_L[h] = L;
+    }
+  }
+  if (a.mass) {
+    __syncthreads();
+    float *mass = a.mass + static_cast<size_t>(bg) * a.T_cap;
+    for (int t0 = threadIdx.x; t0 < a.len; t0 += NT * CH) {
+      float sc[CH][G];
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        const int t = min(t0 + c * NT, a.len - 1);
+#pragma unroll
+        for (int h = 0; h < G; ++h) sc[c][h] = coherent_load(a.scores + (head0 + h) * a.T_cap + t);
+      }
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        const int t = t0 + c * NT;
+        if (t < a.len) {
+          float add = 0.0f;
+#pragma unroll
+          for (int h = 0; h < G; ++h) add += __builtin_amdgcn_exp2f(sc[c][h] - s_M[h]) / s_L[h];
+          mass[t] += add;
+        }
+      }
+    }
+  }
+  if (threadIdx.x == 0) atomicExch(&a.counters[bg], 0u);
+}
 
 // Two workgroups share each CU, and the issue arbiter favours older wavefronts: left alone, the
 // first workgroup on a CU streams its rows faster and finishes early, and the CU runs the rest
@@ -515,37 +587,227 @@ void decode_kernel(DecodeArgs a) {
   __syncthreads();
   if (!s_last) return;
 
-  for (int e = tid; e < G * D; e += NT) {
-    const int h = e / D, dd = e - h * D;
-    const float *part = a.partials + (head0 + h) * a.S * (D + 2);
-    float M = -INFINITY;
-    for (int s = 0; s < a.S; ++s) M = fmaxf(M, coherent_load(part + s * (D + 2)));
-    float O = 0.0f, L = 0.0f;
-    for (int s = 0; s < a.S; ++s) {
-      const float ms = coherent_load(part + s * (D + 2));
-      const float al = (ms == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
-      L = fmaf(al, coherent_load(part + s * (D + 2) + 1), L);
-      O = fmaf(al, coherent_load(part + s * (D + 2) + 2 + dd), O);
-    }
-    a.out[(head0 + h) * D + dd] = O / L;
-    if (dd == 0) {
-      s_M[h] = M;
-      s_L[h] = L;
-    }
-  }
-  if (a.mass) {
-    __syncthreads();
-    float *mass = a.mass + static_cast<size_t>(bg) * a.T_cap;
-    for (int t = tid; t < a.len; t += NT) {
-      float add = 0.0f;
+  merge_splits<D, G, NT>(a, head0, bg, s_M, s_L);
+}
+
+// ------------------------------------------------------------------ short contexts
+// With few tokens (a compact H2O cache of 1280 slots, a prompt's first steps) the split-T layout
+// above gives one workgroup per KV group, whose wavefronts each walk the whole union U of K'
+// rows one batch after another: latency, not bandwidth.  Here a workgroup takes 256 tokens and
+// its 4 wavefronts split U instead (wavefront w reads rows w, w + 4, ...; every load of a
+// wavefront is in flight at once), add their partial scores in LDS, and then split the tokens
+// (64 each) for the softmax and the V pass.  Partials, the last-workgroup merge and the mass
+// update are as above.
+constexpr int kShortChunk = 256;
+
+template <typename KT, int D, int G>
+__global__ __launch_bounds__(256) void decode_short_kernel(DecodeArgs a) {
+  constexpr int NWORD = D / 32;
+  constexpr int TPL = 4;                  // tokens per lane per K' row load
+  constexpr int EPL = 16 / sizeof(KT);    // V elements per lane per 16-byte load
+  constexpr int LPT = D / EPL;            // lanes per V row
+  constexpr int TPI = 64 / LPT;           // V rows per wavefront load
+  constexpr int RW = (D + 3) / 4;         // most K' rows a wavefront reads
+  typedef typename std::conditional<sizeof(KT) == 2, uint2, uint4>::type kvec;
+  __shared__ int s_dl[D];
+  __shared__ float s_qw[D][G];
+  __shared__ float s_part[4][kShortChunk][G];  // partial scores; then the probabilities
+  __shared__ float s_o[4][G][D];
+  __shared__ float s_wm[4][G], s_wl[4][G], s_M[G], s_L[G];
+  __shared__ int s_last;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int bg = blockIdx.x / a.S, split = blockIdx.x - bg * a.S;
+  const int b = bg / a.Hkv, g = bg - b * a.Hkv;
+  const size_t head0 = static_cast<size_t>(b) * a.Hq + static_cast<size_t>(g) * G;
+  const int t0 = split * kShortChunk;
+
+  // ---- union of the group's masks (stored dims only), as a list of rows with head weights
+  uint32_t U[NWORD];
+  int nU = 0;
 #pragma unroll
-      for (int h = 0; h < G; ++h)
-        add += __builtin_amdgcn_exp2f(coherent_load(a.scores + (head0 + h) * a.T_cap + t) -
-                                      s_M[h]) / s_L[h];
-      mass[t] += add;
+  for (int wd = 0; wd < NWORD; ++wd) {
+    uint32_t u = 0;
+#pragma unroll
+    for (int h = 0; h < G; ++h) u |= a.mask[(head0 + h) * NWORD + wd];
+    const int lo = wd * 32;
+    if (a.d_store <= lo) u = 0;
+    else if (a.d_store < lo + 32) u &= (1u << (a.d_store - lo)) - 1u;
+    U[wd] = u;
+    nU += __popc(u);
+  }
+  if (tid < D) {
+    const int wd = tid >> 5, bit = tid & 31;
+    uint32_t uw = 0;
+    int pos = 0;
+#pragma unroll
+    for (int x = 0; x < NWORD; ++x) {
+      if (x < wd) pos += __popc(U[x]);
+      if (x == wd) uw = U[x];
+    }
+    if ((uw >> bit) & 1u) {
+      pos += __popc(uw & ((1u << bit) - 1u));
+      s_dl[pos] = tid;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const uint32_t mw = a.mask[(head0 + h) * NWORD + wd];
+        s_qw[pos][h] = ((mw >> bit) & 1u) ? a.q_proj[(head0 + h) * D + tid] * a.qscale : 0.0f;
+      }
     }
   }
-  if (tid == 0) atomicExch(&a.counters[bg], 0u);
+  __syncthreads();
+
+  // ---- partial scores: wavefront w takes rows w, w + 4, ... of the list, all loads at once
+  const int tl = min(t0 + TPL * lane, a.T_cap - TPL);  // stays inside the row; masked below
+  const KT *kbase = static_cast<const KT *>(a.kp) + static_cast<size_t>(bg) * a.d_store * a.T_cap + tl;
+  const int nw = nU > w ? (nU - w + 3) / 4 : 0;  // rows of this wavefront
+  float acc[G][TPL];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int j = 0; j < TPL; ++j) acc[h][j] = 0.0f;
+  {
+    kvec kr[RW];
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {  // rows past nw re-read row w (their weight is 0)
+      const int u = i < nw ? w + 4 * i : w;
+      kr[i] = nw > 0 ? *reinterpret_cast<const kvec *>(kbase + static_cast<size_t>(s_dl[u]) * a.T_cap)
+                     : kvec{};
+    }
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {
+      if (i < nw) {  // uniform over the wavefront
+        float kv[TPL];
+        if constexpr (sizeof(KT) == 2) {
+          kv[0] = bf16_lo(kr[i].x); kv[1] = bf16_hi(kr[i].x);
+          kv[2] = bf16_lo(kr[i].y); kv[3] = bf16_hi(kr[i].y);
+        } else {
+          kv[0] = __uint_as_float(kr[i].x); kv[1] = __uint_as_float(kr[i].y);
+          kv[2] = __uint_as_float(kr[i].z); kv[3] = __uint_as_float(kr[i].w);
+        }
+        const int u = w + 4 * i;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float qw = s_qw[u][h];
+#pragma unroll
+          for (int j = 0; j < TPL; ++j) acc[h][j] = fmaf(qw, kv[j], acc[h][j]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < TPL; ++j)
+#pragma unroll
+    for (int h = 0; h < G; ++h) s_part[w][TPL * lane + j][h] = acc[h][j];
+  __syncthreads();
+
+  // ---- wavefront w now owns tokens t0 + 64 w + lane: full scores, softmax numerators
+  const int lt = 64 * w + lane, tk = t0 + lt;
+  const bool valid = tk < a.len;
+  float sc[G], m[G], l[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float x = s_part[0][lt][h] + s_part[1][lt][h] + s_part[2][lt][h] + s_part[3][lt][h];
+    sc[h] = valid ? x : -INFINITY;
+    if (a.mass && valid) publish(a.scores + (head0 + h) * a.T_cap + tk, sc[h]);
+    m[h] = wave_max(sc[h]);
+    const float p = (m[h] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sc[h] - m[h]);
+    l[h] = wave_sum(p);
+    s_part[0][lt][h] = p;  // only this wavefront reads its own tokens' slots
+  }
+
+  // ---- o = sum_t p_t V_t over the wavefront's 64 tokens, all loads at once
+  const int sub = lane / LPT, cl = lane - sub * LPT;
+  const int last = a.len - 1;
+  const KT *vbase = static_cast<const KT *>(a.v) + static_cast<size_t>(bg) * a.T_cap * D + cl * EPL;
+  float o[G][EPL];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[h][e] = 0.0f;
+  {
+    constexpr int NL = 64 / TPI;
+    uint4 vr[NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {  // rows past the last token re-read it (their p is 0)
+      const int t = min(t0 + 64 * w + i * TPI + sub, last);
+      vr[i] = load16(vbase + static_cast<size_t>(t) * D);
+    }
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      float vv[EPL];
+      Vec<KT>::unpack(vr[i], vv);
+      const int r = 64 * w + i * TPI + sub;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float p = s_part[0][r][h];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[h][e] = fmaf(p, vv[e], o[h][e]);
+      }
+    }
+  }
+#pragma unroll
+  for (int off = LPT; off < 64; off <<= 1)
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[h][e] += __shfl_xor(o[h][e], off, 64);
+
+  // ---- merge the 4 wavefronts, write this chunk's partials
+  if (sub == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) s_o[w][h][cl * EPL + e] = o[h][e];
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      s_wm[w][h] = m[h];
+      s_wl[w][h] = l[h];
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < G * D; e += 256) {
+    const int h = e / D, dd = e - h * D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) M = fmaxf(M, s_wm[x][h]);
+    float O = 0.0f, L = 0.0f;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const float mw = s_wm[x][h];
+      const float al = (mw == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
+      O = fmaf(al, s_o[x][h][dd], O);
+      L = fmaf(al, s_wl[x][h], L);
+    }
+    float *part = a.partials + ((head0 + h) * a.S + split) * (D + 2);
+    if (dd == 0) {
+      publish(part + 0, M);
+      publish(part + 1, L);
+    }
+    publish(part + 2 + dd, O);
+  }
+
+  // ---- the last workgroup of this (b, g) merges all chunks
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's partials and scores have landed
+  __syncthreads();
+  if (tid == 0) s_last = (atomicAdd(&a.counters[bg], 1u) == static_cast<unsigned>(a.S - 1));
+  __syncthreads();
+  if (!s_last) return;
+  merge_splits<D, G, 256>(a, head0, bg, s_M, s_L);
+}
+
+template <typename KT, int D>
+hipError_t launch_short(const DecodeArgs &a, hipStream_t s) {
+  const dim3 grid(a.B * a.Hkv * a.S), block(256);
+  switch (a.Hq / a.Hkv) {
+    case 1: decode_short_kernel<KT, D, 1><<<grid, block, 0, s>>>(a); break;
+    case 2: decode_short_kernel<KT, D, 2><<<grid, block, 0, s>>>(a); break;
+    case 4: decode_short_kernel<KT, D, 4><<<grid, block, 0, s>>>(a); break;
+    default: decode_short_kernel<KT, D, 8><<<grid, block, 0, s>>>(a); break;
+  }
+  return hipGetLastError();
 }
 
 template <typename KT, int D, int G, bool FUSED>
@@ -578,9 +840,27 @@ DecodeLayout decode_layout(int dtype, int G) {
   return L;
 }
 
+bool decode_short(int len) { return len <= kDecodeShortMax; }
+
+int decode_splits(int dtype, int G, int len) {
+  if (decode_short(len)) return (len + kShortChunk - 1) / kShortChunk;
+  const DecodeLayout L = decode_layout(dtype, G);
+  return (len + L.split - 1) / L.split;
+}
+
+namespace {
+// partials per head: enough for any len <= T_cap in either layout
+size_t partial_slots(int dtype, int G, int T_cap) {
+  const DecodeLayout L = decode_layout(dtype, G);
+  const size_t s_long = (static_cast<size_t>(T_cap) + L.split - 1) / L.split;
+  const int short_len = T_cap < kDecodeShortMax ? T_cap : kDecodeShortMax;
+  const size_t s_short = (static_cast<size_t>(short_len) + kShortChunk - 1) / kShortChunk;
+  return s_long > s_short ? s_long : s_short;
+}
+}  // namespace
+
 size_t decode_workspace_bytes(int dtype, int B, int Hq, int Hkv, int d, int T_cap) {
-  const DecodeLayout L = decode_layout(dtype, Hq / Hkv);
-  const size_t S = (static_cast<size_t>(T_cap) + L.split - 1) / L.split;
+  const size_t S = partial_slots(dtype, Hq / Hkv, T_cap);
   return align256(static_cast<size_t>(B) * Hkv * 4) +
          align256(static_cast<size_t>(B) * Hq * S * (d + 2) * 4) +
          static_cast<size_t>(B) * Hq * T_cap * 4;
@@ -588,8 +868,7 @@ size_t decode_workspace_bytes(int dtype, int B, int Hq, int Hkv, int d, int T_ca
 
 void decode_workspace_carve(void *ws, int dtype, int B, int Hq, int Hkv, int d, int T_cap,
                             uint32_t **counters, float **partials, float **scores) {
-  const DecodeLayout L = decode_layout(dtype, Hq / Hkv);
-  const size_t S = (static_cast<size_t>(T_cap) + L.split - 1) / L.split;
+  const size_t S = partial_slots(dtype, Hq / Hkv, T_cap);
   char *p = static_cast<char *>(ws);
   *counters = reinterpret_cast<uint32_t *>(p);
   p += align256(static_cast<size_t>(B) * Hkv * 4);
@@ -599,6 +878,11 @@ void decode_workspace_carve(void *ws, int dtype, int B, int Hq, int Hkv, int d, 
 }
 
 hipError_t launch_decode(int dtype, const DecodeArgs &a, hipStream_t s) {
+  if (decode_short(a.len)) {
+    if (dtype == 1)
+      return a.d == 128 ? launch_short<bf16_t, 128>(a, s) : launch_short<bf16_t, 64>(a, s);
+    return a.d == 128 ? launch_short<float, 128>(a, s) : launch_short<float, 64>(a, s);
+  }
   if (dtype == 1)
     return a.d == 128 ? launch_d<bf16_t, 128, false>(a, s) : launch_d<bf16_t, 64, false>(a, s);
   return a.d == 128 ? launch_d<float, 128, false>(a, s) : launch_d<float, 64, false>(a, s);

@@ -37,6 +37,12 @@ def test_tiny_decode_f32():
     (16, 2, 1500, 32, 128),    # G=8
     (8, 2, 1, 96, 128),        # a single token
     (4, 1, 513, 40, 64),       # d = 64
+    # past 4096 tokens the split-T kernel runs (the cases above take the short-context one)
+    (8, 2, 5000, 96, 128),     # G=4
+    (4, 4, 4097, 64, 128),     # G=1
+    (8, 4, 4200, 128, 128),    # G=2, k = d
+    (16, 2, 4500, 32, 128),    # G=8
+    (4, 1, 4300, 40, 64),      # d = 64
 ])
 def test_decode_bf16_shapes(Hq, Hkv, T, k, d):
     c = config(2, B=2, Hq=Hq, Hkv=Hkv, T=T, k=k, d=d, d_store=d, d_sel=d)
@@ -47,7 +53,8 @@ def test_decode_bf16_shapes(Hq, Hkv, T, k, d):
     assert_close(r["out"].cpu().double().numpy(), ref, "bf16", f"decode {Hq},{Hkv},{T}")
 
 
-@pytest.mark.parametrize("length", [1, 63, 511, 512, 2047, 2048, 2049, 4100])
+@pytest.mark.parametrize("length", [1, 63, 255, 256, 257, 511, 512, 2047, 2048, 2049, 4096, 4097,
+                                    4100])
 def test_decode_ragged_lengths_f32(length):
     """fp32 storage: tight tolerance across split and wavefront boundaries; T_cap > len."""
     c = config(1, B=1, Hq=4, Hkv=2, d=128, T=length, k=100, d_store=128, d_sel=128)
