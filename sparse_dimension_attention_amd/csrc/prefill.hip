@@ -22,8 +22,8 @@
 //    hands out (lane l < 32: tokens 0-3, 8-11 of a 16-token step; lane l >= 32: tokens 4-7,
 //    12-15), and the V operand is read in that same order.  D holds O^T with lane l owning
 //    query row l%32, so the softmax rescale is one scalar per lane.
-// One workgroup = 4 wavefronts = 4 (query head, 32-position block) pairs of one KV group, so a
-// K'/V tile of 64 tokens is staged once for 4 heads.
+// One workgroup = 8 wavefronts over the query heads of one KV group (256 query rows), so a
+// K'/V tile of 64 tokens is staged in LDS once for all of them.
 #include "aqua_internal.h"
 
 namespace aqua {
@@ -156,12 +156,19 @@ __global__ __launch_bounds__(256) void prefill_select_kernel(const bf16_t *__res
 // ------------------------------------------------------------------ 2. attention
 // A workgroup holds 256 query rows: QB 32-row MFMA blocks per wavefront times NW wavefronts
 // (QB * NW = 8).  The launched form is QB = 1, NW = 8: two wavefronts per SIMD, each owning 32
-// consecutive positions of one head, so one wavefront's softmax can overlap the other's MFMAs;
-// QB = 2, NW = 4 (one wavefront per SIMD, every K'/V operand read feeding two MFMAs) measured
-// slower.  The wavefronts cover the heads of one KV group (or, for G < 4, several position
-// blocks), so each 64-token K'/V tile is staged in LDS once for the 256 rows.  Tiles are
-// double-buffered: the global loads of tile t+1 are in flight while tile t is computed, and one
-// barrier per tile hands the buffers over.
+// consecutive positions of one head.  The wavefronts cover the heads of one KV group (or, for
+// G < 4, several position blocks), so each 64-token K'/V tile is staged in LDS once for the 256
+// rows.
+//
+// Each wavefront is software-pipelined over 32-token halves of the tiles: the scores S of the
+// next half are computed on the matrix cores while the VALU turns the current half's scores into
+// probabilities, then P V of the current half follows.  A half's scores are thus computed one
+// step before its softmax, so a K' tile is read in two steps (the step of the tile before it and
+// its own): K' tiles rotate through three LDS buffers and V tiles through two, so the buffers
+// written in a step are never ones that a wavefront still in that step reads, and one barrier per
+// tile suffices.  The global loads of the tiles two (K') and one (V) ahead are in flight across
+// the step.  (QB = 2, NW = 4 -- one wavefront per SIMD, every operand read feeding two MFMAs --
+// measured slower: with one wavefront per SIMD the LDS latencies are exposed.)
 //
 // Operands come out of LDS with ds_read_b64_tr_b16, which within each 16-lane group reads a
 // 4-row x 16-column block of 16-bit elements (lane s of the group supplying the address of row
@@ -195,52 +202,48 @@ __device__ __forceinline__ bf16x8_t lds_tr_pair(const bf16_t *p0, const bf16_t *
   return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// QB: 32-row query blocks per wavefront; NW: wavefronts per workgroup (QB * NW = 8, so a
-// workgroup always holds 256 query rows).
+// QB: 32-row query blocks per wavefront; NW: wavefronts per workgroup (QB * NW = 8).
 template <int QB, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(PrefillArgs a) {
-  constexpr int NT = NW * 64;      // threads
-  constexpr int CPT = 1024 / NT;   // 16-byte chunks of K' (and of V) staged per thread per tile
-  constexpr int ROWS = 32 * QB;    // query rows per wavefront
-  __shared__ __align__(16) bf16_t sK[2][KBUF];  // K' tile, [dim][token]
-  __shared__ __align__(16) bf16_t sV[2][VBUF];  // V tile, [token][dim]
+  constexpr int ROWS = 32 * QB, NT = NW * 64, CPT = 1024 / NT;
+  __shared__ __align__(16) bf16_t sK[3][KBUF];  // K' tiles, [dim][token]
+  __shared__ __align__(16) bf16_t sV[2][VBUF];  // V tiles, [token][dim]
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int G = a.Hq / a.Hkv;
-  const int WPH = NW / a.qh;    // wavefronts per head: consecutive ROWS-position blocks
-  const int nsub = G / a.qh;    // head subsets per KV group
+  const int WPH = NW / a.qh;
+  const int nsub = G / a.qh;
   const int ncombo = a.B * a.Hkv * nsub;
-  // consecutive workgroup ids go round-robin over the XCDs: keep one (b, group) per id residue
-  // so that the workgroups sharing a K'/V stream share an L2; latest positions first
   const int combo = blockIdx.x % ncombo;
   const int qblk = a.nqb - 1 - blockIdx.x / ncombo;
   const int sub = combo % nsub;
   const int bg = combo / nsub;
   const int b = bg / a.Hkv, g = bg - b * a.Hkv;
   const int head = g * G + sub * a.qh + (w % a.qh);
-  const int pb = qblk * WPH + w / a.qh;  // this wavefront's block of ROWS positions
-  const int kend = a.pos0 + min((qblk + 1) * WPH * ROWS, a.Lq);  // keys [0, kend) for the group
+  const int pb = qblk * WPH + w / a.qh;
+  const int kend = a.pos0 + min((qblk + 1) * WPH * ROWS, a.Lq);
   const int ntile = (kend + KT - 1) / KT;
+  const int pos_first_wg = a.pos0 + min(qblk * WPH * ROWS, a.Lq - 1);
+  // tiles [0, n_pipe) are visible to every row of the workgroup and have a successor: they take
+  // the step without causal masking
+  const int n_pipe = min((pos_first_wg + 1) / KT, ntile - 1);
 
-  // ---- the wavefront's query rows (B operand of S^T), one 16-dim step per register group
-  int pos[QB];
+  int pos[QB], pos_blk[QB];
   u32x4_t qreg[QB][8];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int rl = min(pb * ROWS + qb * 32 + (lane & 31), a.Lq - 1);
     pos[qb] = a.pos0 + rl;
+    pos_blk[qb] = a.pos0 + min(pb * ROWS + qb * 32, a.Lq - 1);
     const bf16_t *qr = a.qm + ((static_cast<size_t>(b) * a.Hq + head) * a.Lq + rl) * 128 +
                        8 * (lane >> 5);
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      qreg[qb][m] = *reinterpret_cast<const u32x4_t *>(qr + 16 * m);
-      asm volatile("" : "+a"(qreg[qb][m]));  // MFMA B operands only: keep them in AGPRs
-    }
+    for (int m = 0; m < 8; ++m) qreg[qb][m] = *reinterpret_cast<const u32x4_t *>(qr + 16 * m);
   }
-  const int pos_first = a.pos0 + min(pb * ROWS, a.Lq - 1);  // earliest row of the wavefront
 
-  // ---- staging through buffer loads: the descriptors' sizes end K' at d_store dims and V at
-  // kend tokens, and reads past a size return zeros (never multiply unwritten V by a zero weight)
+  // staging through buffer loads: the descriptors' sizes end K' at d_store dims and V at kend
+  // tokens, and reads past a size return zeros (unwritten V is never multiplied by a zero weight;
+  // the loads of tiles past the last one read zeros or unused K' and are never consumed)
   const __amdgpu_buffer_rsrc_t rK = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<bf16_t *>(a.kp + static_cast<size_t>(bg) * a.d_store * a.T_cap), (short)0,
       a.d_store * a.T_cap * 2, 0x00020000);
@@ -250,28 +253,35 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(PrefillArgs a)
   const int kdim = tid >> 3, kpart = tid & 7;   // K' rows kdim + (NT/8) i, 8 tokens at 8 kpart
   const int vtok = tid >> 4, vpart = tid & 15;  // V rows vtok + (NT/16) i, 8 dims at 8 vpart
   u32x4_t stK[CPT], stV[CPT];
-  auto load_tile = [&](int t0) {
+  auto load_K = [&](int t) {
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
+    for (int i = 0; i < CPT; ++i)
       stK[i] = __builtin_amdgcn_raw_buffer_load_b128(
-          rK, (kdim + (NT / 8) * i) * a.T_cap * 2 + 16 * kpart, t0 * 2, 0);
-      stV[i] = __builtin_amdgcn_raw_buffer_load_b128(
-          rV, (vtok + (NT / 16) * i) * 256 + 16 * vpart, t0 * 256, 0);
-    }
+          rK, (kdim + (NT / 8) * i) * a.T_cap * 2 + 16 * kpart, t * KT * 2, 0);
   };
-  auto store_tile = [&](int buf) {
+  auto load_V = [&](int t) {
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      *reinterpret_cast<u32x4_t *>(&sK[buf][(kdim + (NT / 8) * i) * KROW + 8 * kpart]) = stK[i];
-      *reinterpret_cast<u32x4_t *>(&sV[buf][(vtok + (NT / 16) * i) * VROW + 8 * vpart]) = stV[i];
-    }
+    for (int i = 0; i < CPT; ++i)
+      stV[i] = __builtin_amdgcn_raw_buffer_load_b128(
+          rV, (vtok + (NT / 16) * i) * 256 + 16 * vpart, t * KT * 256, 0);
+  };
+  auto store_K = [&](bf16_t *dst) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i)
+      *reinterpret_cast<u32x4_t *>(&dst[(kdim + (NT / 8) * i) * KROW + 8 * kpart]) = stK[i];
+  };
+  auto store_V = [&](bf16_t *dst) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i)
+      *reinterpret_cast<u32x4_t *>(&dst[(vtok + (NT / 16) * i) * VROW + 8 * vpart]) = stV[i];
+  };
+  auto barrier = [&]() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // LDS traffic done; global loads stay in flight
+    __builtin_amdgcn_s_barrier();
   };
 
-  // per-lane parts of the transposed-read addresses (see the comment at the top of this part)
   const int g16 = (lane >> 4) & 3, s16 = lane & 15;
-  // K': row (dim) 16 m + 8 (g16 / 2) + 4 j + s16 / 4, column (token) 32 tb + 16 (g16 % 2) + 4 (s16 % 4)
   const int k_off = (8 * (g16 >> 1) + (s16 >> 2)) * KROW + 16 * (g16 & 1) + 4 * (s16 & 3);
-  // V: row (token) 32 tb + 16 s + 4 (g16 / 2) + 8 j + s16 / 4, column (dim) 32 db + 16 (g16 % 2) + 4 (s16 % 4)
   const int v_off = (4 * (g16 >> 1) + (s16 >> 2)) * VROW + 16 * (g16 & 1) + 4 * (s16 & 3);
 
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -290,101 +300,139 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(PrefillArgs a)
     l_i[qb] = 0.0f;
   }
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int t = 0; t < ntile; ++t) {
-    const int buf = t & 1, t0 = t * KT;
-    if (t + 1 < ntile) load_tile(t0 + KT);
-    const bf16_t *kt = sK[buf] + k_off;
-    const bf16_t *vt = sV[buf] + v_off;
-
+  // S^T of 32 tokens (half tb of the tile in kt) for both query blocks
+  auto s_half = [&](const bf16_t *kt, int tb, f32x16_t (&s)[QB]) {
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {  // 32-token halves of the tile, one after the other
-      // ---- S^T = K'^T Q'^T for the 32 tokens x QB query blocks
-      f32x16_t acc_s[QB];
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[qb][r] = 0.0f;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const bf16_t *p = kt + k_off + 16 * m * KROW + 32 * tb;
+      const bf16x8_t av = lds_tr_pair(p, p + 4 * KROW);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc_s[qb][r] = 0.0f;
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const bf16_t *p = kt + 16 * m * KROW + 32 * tb;
-        const bf16x8_t av = lds_tr_pair(p, p + 4 * KROW);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          acc_s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              av, __builtin_bit_cast(bf16x8_t, qreg[qb][m]), acc_s[qb], 0, 0, 0);
-      }
-
-      // ---- causal mask, online softmax (log2 units), probabilities as bf16 B operands
-      const int tok0 = t0 + 32 * tb;
-      uint32_t pk[QB][2][4];  // [qb][16-token step][packed pair]
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        if (tok0 + 31 > pos_first + 32 * qb) {  // the block reaches past some row's position
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int tok = tok0 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            if (tok > pos[qb]) acc_s[qb][r] = -INFINITY;
-          }
-        }
-        float mx = acc_s[qb][0];
-#pragma unroll
-        for (int r = 1; r < 16; ++r) mx = __builtin_fmaxf(mx, acc_s[qb][r]);
-        {  // lanes l and l ^ 32 hold the two halves of a row's scores
-          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx),
-                                                           __float_as_uint(mx), false, false);
-          mx = __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-        }
-        // the running max moves only when a score exceeds it by more than the slack, so the
-        // probabilities stay <= 2^slack and the rescale of O is rare after the first block
-        const bool grow = mx > m_i[qb] + RESCALE_SLACK;
-        if (__ballot(grow)) {
-          const float m_new = grow ? mx : m_i[qb];
-          const float alpha = __builtin_amdgcn_exp2f(m_i[qb] - m_new);
-          l_i[qb] *= alpha;
-#pragma unroll
-          for (int db = 0; db < 4; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc_o[qb][db][r] *= alpha;
-          m_i[qb] = m_new;
-        }
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-#pragma unroll
-          for (int x = 0; x < 4; ++x) {
-            const int r0 = 8 * s + 2 * x;
-            pk[qb][s][x] = pack_bf16x2(__builtin_amdgcn_exp2f(acc_s[qb][r0] - m_i[qb]),
-                                       __builtin_amdgcn_exp2f(acc_s[qb][r0 + 1] - m_i[qb]));
-            // the row sum takes the rounded weights, the ones P V multiplies
-            l_i[qb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[qb][s][x]),
-                                                      ones, l_i[qb], false);
-          }
-      }
-
-      // ---- O^T += V^T P^T over the 32 tokens
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const bf16_t *p = vt + (32 * tb + 16 * s) * VROW + 32 * db;
-          const bf16x8_t av = lds_tr_pair(p, p + 8 * VROW);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) {
-            const u32x4_t bv = {pk[qb][s][0], pk[qb][s][1], pk[qb][s][2], pk[qb][s][3]};
-            acc_o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                av, __builtin_bit_cast(bf16x8_t, bv), acc_o[qb][db], 0, 0, 0);
-          }
-        }
+        s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            av, __builtin_bit_cast(bf16x8_t, qreg[qb][m]), s[qb], 0, 0, 0);
     }
+  };
+  auto mask_half = [&](int tok0, f32x16_t (&s)[QB]) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+      if (tok0 + 31 > pos_blk[qb]) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int tok = tok0 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          if (tok > pos[qb]) s[qb][r] = -INFINITY;
+        }
+      }
+  };
+  // running max with slack: O and l are rescaled only when a score passes max + slack
+  auto rescale = [&](f32x16_t (&s)[QB]) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float mx = s[qb][0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = __builtin_fmaxf(mx, s[qb][r]);
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                       false, false);
+      mx = __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      const bool grow = mx > m_i[qb] + RESCALE_SLACK;
+      if (__ballot(grow)) {
+        const float m_new = grow ? mx : m_i[qb];
+        const float alpha = __builtin_amdgcn_exp2f(m_i[qb] - m_new);
+        l_i[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc_o[qb][db][r] *= alpha;
+        m_i[qb] = m_new;
+      }
+    }
+  };
+  // probabilities as bf16 B operands: pk[qb][16-token step][pair]; the row sum takes the
+  // rounded weights, the ones P V multiplies
+  uint32_t pk[QB][2][4];
+  auto probs = [&](f32x16_t (&s)[QB]) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int ss = 0; ss < 2; ++ss)
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const int r0 = 8 * ss + 2 * x;
+          pk[qb][ss][x] = pack_bf16x2(__builtin_amdgcn_exp2f(s[qb][r0] - m_i[qb]),
+                                      __builtin_amdgcn_exp2f(s[qb][r0 + 1] - m_i[qb]));
+          l_i[qb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[qb][ss][x]),
+                                                    ones, l_i[qb], false);
+        }
+  };
+  auto pv_half = [&](const bf16_t *vt, int tb) {
+#pragma unroll
+    for (int ss = 0; ss < 2; ++ss)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const bf16_t *p = vt + v_off + (32 * tb + 16 * ss) * VROW + 32 * db;
+        const bf16x8_t av = lds_tr_pair(p, p + 8 * VROW);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const u32x4_t bv = {pk[qb][ss][0], pk[qb][ss][1], pk[qb][ss][2], pk[qb][ss][3]};
+          acc_o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              av, __builtin_bit_cast(bf16x8_t, bv), acc_o[qb][db], 0, 0, 0);
+        }
+      }
+  };
 
-    if (t + 1 < ntile) store_tile(buf ^ 1);  // that buffer was last read before the previous barrier
-    __syncthreads();
+  // K' tiles rotate through three buffers (tile t in sK[t % 3]): a tile is read in two steps
+  // (its first half's scores in the step before its own), so the buffer written in step t must
+  // be one that no wavefront still in step t reads.  V tiles alternate between two.
+  f32x16_t sa[QB], sb[QB];  // scores of the current tile's first and second 32 tokens
+  auto step = [&](int t, int c0, int c1, int c2, bool masked, bool has_next) {
+    const bf16_t *vt = sV[t & 1];
+    if (masked) mask_half(t * KT, sa);
+    rescale(sa);
+    s_half(sK[c0], 1, sb);
+    probs(sa);
+    pv_half(vt, 0);
+    if (masked) mask_half(t * KT + 32, sb);
+    rescale(sb);
+    if (has_next) s_half(sK[c1], 0, sa);
+    probs(sb);
+    pv_half(vt, 1);
+    store_K(sK[c2]);
+    store_V(sV[(t + 1) & 1]);
+    load_K(t + 3);
+    load_V(t + 2);
+    barrier();
+  };
+
+  load_K(0);
+  load_V(0);
+  store_K(sK[0]);
+  store_V(sV[0]);
+  load_K(1);
+  store_K(sK[1]);
+  load_K(2);
+  load_V(1);
+  barrier();
+  s_half(sK[0], 0, sa);
+
+  int t = 0, c0 = 0, c1 = 1, c2 = 2;
+  for (; t < n_pipe; ++t) {
+    step(t, c0, c1, c2, false, true);
+    const int c = c0;
+    c0 = c1;
+    c1 = c2;
+    c2 = c;
+  }
+  for (; t < ntile; ++t) {  // the last tiles: causal masking, and a tile without successor
+    step(t, c0, c1, c2, true, t + 1 < ntile);
+    const int c = c0;
+    c0 = c1;
+    c1 = c2;
+    c2 = c;
   }
 
-  // ---- normalise and write: lane l owns query row l % 32, dims db*32 + 8(r/4) + 4(l/32) + r%4
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int rl = pb * ROWS + qb * 32 + (lane & 31);
@@ -443,12 +491,7 @@ hipError_t launch_prefill(const void *kp, const void *v, int B, int Hq, int Hkv,
   const int rows_per_wg = 256 / a.qh;  // 256 query rows per workgroup over qh heads
   a.nqb = (Lq + rows_per_wg - 1) / rows_per_wg;
   const int grid = a.nqb * (G / a.qh) * B * Hkv;
-#ifdef AQUA_PREFILL_QB
-  constexpr int QB = AQUA_PREFILL_QB;
-#else
-  constexpr int QB = 1;
-#endif
-  prefill_attn_kernel<QB, 8 / QB><<<dim3(grid), dim3(64 * (8 / QB)), 0, s>>>(a);
+  prefill_attn_kernel<1, 8><<<dim3(grid), dim3(512), 0, s>>>(a);
   return hipGetLastError();
 }
 
