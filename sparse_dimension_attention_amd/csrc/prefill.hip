@@ -160,15 +160,17 @@ __global__ __launch_bounds__(256) void prefill_select_kernel(const bf16_t *__res
 // G < 4, several position blocks), so each 64-token K'/V tile is staged in LDS once for the 256
 // rows.
 //
-// Each wavefront is software-pipelined over 32-token halves of the tiles: the scores S of the
-// next half are computed on the matrix cores while the VALU turns the current half's scores into
-// probabilities, then P V of the current half follows.  A half's scores are thus computed one
-// step before its softmax, so a K' tile is read in two steps (the step of the tile before it and
-// its own): K' tiles rotate through three LDS buffers and V tiles through two, so the buffers
-// written in a step are never ones that a wavefront still in that step reads, and one barrier per
-// tile suffices.  The global loads of the tiles two (K') and one (V) ahead are in flight across
-// the step.  (QB = 2, NW = 4 -- one wavefront per SIMD, every operand read feeding two MFMAs --
-// measured slower: with one wavefront per SIMD the LDS latencies are exposed.)
+// Each wavefront is software-pipelined over the tiles: the scores S of the next tile are computed
+// on the matrix cores while the VALU turns the current tile's scores into probabilities, and P V
+// of the current tile follows.  So step t reads K' tile t+1 and V tile t; each kind rotates
+// through two LDS buffers, and the tiles written in step t (K' t+2, V t+1) replace ones last read
+// before the previous barrier: one barrier per tile.  The global loads of the tiles two (K') and
+// one (V) ahead are in flight across the step.  Scores come out of the MFMA already relative to
+// the row's running max m (the first MFMA of each accumulation chain starts from C = -m), so the
+// softmax needs no subtraction; m is checked once per tile, at the end of the step that computed
+// its scores, and moves only past a slack (lazy rescale of O and the row sum).  (QB = 2, NW = 4 --
+// one wavefront per SIMD, every operand read feeding two MFMAs -- measured slower: with one
+// wavefront per SIMD the LDS latencies are exposed.)
 //
 // Operands come out of LDS with ds_read_b64_tr_b16, which within each 16-lane group reads a
 // 4-row x 16-column block of 16-bit elements (lane s of the group supplying the address of row
@@ -206,7 +208,7 @@ __device__ __forceinline__ bf16x8_t lds_tr_pair(const bf16_t *p0, const bf16_t *
 template <int QB, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(PrefillArgs a) {
   constexpr int ROWS = 32 * QB, NT = NW * 64, CPT = 1024 / NT;
-  __shared__ __align__(16) bf16_t sK[3][KBUF];  // K' tiles, [dim][token]
+  __shared__ __align__(16) bf16_t sK[2][KBUF];  // K' tiles, [dim][token]
   __shared__ __align__(16) bf16_t sV[2][VBUF];  // V tiles, [token][dim]
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -293,19 +295,14 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(PrefillArgs a)
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc_o[qb][db][r] = 0.0f;
-  float m_i[QB], l_i[QB];
+  float m_i[QB], l_i[QB];  // running max (set from the first tile) and row sum
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m_i[qb] = -INFINITY;
-    l_i[qb] = 0.0f;
-  }
+  for (int qb = 0; qb < QB; ++qb) l_i[qb] = 0.0f;
 
   // S^T of 32 tokens (half tb of the tile in kt) for both query blocks
+  // scores relative to the running max: the chain's first MFMA adds them to C = -m
+  f32x16_t negm[QB];
   auto s_half = [&](const bf16_t *kt, int tb, f32x16_t (&s)[QB]) {
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[qb][r] = 0.0f;
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
       const bf16_t *p = kt + k_off + 16 * m * KROW + 32 * tb;
@@ -313,7 +310,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(PrefillArgs a)
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
         s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            av, __builtin_bit_cast(bf16x8_t, qreg[qb][m]), s[qb], 0, 0, 0);
+            av, __builtin_bit_cast(bf16x8_t, qreg[qb][m]), m == 0 ? negm[qb] : s[qb], 0, 0, 0);
     }
   };
   auto mask_half = [&](int tok0, f32x16_t (&s)[QB]) {
@@ -327,33 +324,44 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(PrefillArgs a)
         }
       }
   };
-  // running max with slack: O and l are rescaled only when a score passes max + slack
-  auto rescale = [&](f32x16_t (&s)[QB]) {
+  // s0, s1 hold a tile's scores relative to m.  A row whose maximum passes the slack moves m up
+  // by that maximum: O and l are rescaled, the tile's scores and -m shift with it.
+  auto rescale = [&](f32x16_t (&s0)[QB], f32x16_t (&s1)[QB]) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      float mx = s[qb][0];
+      float mx = __builtin_fmaxf(s0[qb][0], s0[qb][1]);
 #pragma unroll
-      for (int r = 1; r < 16; ++r) mx = __builtin_fmaxf(mx, s[qb][r]);
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
-                                                       false, false);
-      mx = __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-      const bool grow = mx > m_i[qb] + RESCALE_SLACK;
-      if (__ballot(grow)) {
-        const float m_new = grow ? mx : m_i[qb];
-        const float alpha = __builtin_amdgcn_exp2f(m_i[qb] - m_new);
+      for (int r = 2; r < 16; r += 2)
+        mx = __builtin_fmaxf(__builtin_fmaxf(mx, s0[qb][r]), s0[qb][r + 1]);
+#pragma unroll
+      for (int r = 0; r < 16; r += 2)
+        mx = __builtin_fmaxf(__builtin_fmaxf(mx, s1[qb][r]), s1[qb][r + 1]);
+      if (__ballot(mx > RESCALE_SLACK)) {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx),
+                                                         __float_as_uint(mx), false, false);
+        mx = __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        const float dm = mx > RESCALE_SLACK ? mx : 0.0f;
+        const float alpha = __builtin_amdgcn_exp2f(-dm);
         l_i[qb] *= alpha;
 #pragma unroll
         for (int db = 0; db < 4; ++db)
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc_o[qb][db][r] *= alpha;
-        m_i[qb] = m_new;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          s0[qb][r] -= dm;
+          s1[qb][r] -= dm;
+        }
+        m_i[qb] += dm;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) negm[qb][r] = -m_i[qb];
       }
     }
   };
   // probabilities as bf16 B operands: pk[qb][16-token step][pair]; the row sum takes the
   // rounded weights, the ones P V multiplies
-  uint32_t pk[QB][2][4];
-  auto probs = [&](f32x16_t (&s)[QB]) {
+  uint32_t pk[QB][4][4];
+  auto probs = [&](f32x16_t (&s)[QB], int h) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -361,10 +369,10 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(PrefillArgs a)
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
           const int r0 = 8 * ss + 2 * x;
-          pk[qb][ss][x] = pack_bf16x2(__builtin_amdgcn_exp2f(s[qb][r0] - m_i[qb]),
-                                      __builtin_amdgcn_exp2f(s[qb][r0 + 1] - m_i[qb]));
-          l_i[qb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[qb][ss][x]),
-                                                    ones, l_i[qb], false);
+          pk[qb][2 * h + ss][x] = pack_bf16x2(__builtin_amdgcn_exp2f(s[qb][r0]),
+                                              __builtin_amdgcn_exp2f(s[qb][r0 + 1]));
+          l_i[qb] = __builtin_amdgcn_fdot2_f32_bf16(
+              __builtin_bit_cast(bf16x2_t, pk[qb][2 * h + ss][x]), ones, l_i[qb], false);
         }
   };
   auto pv_half = [&](const bf16_t *vt, int tb) {
@@ -376,30 +384,36 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(PrefillArgs a)
         const bf16x8_t av = lds_tr_pair(p, p + 8 * VROW);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-          const u32x4_t bv = {pk[qb][ss][0], pk[qb][ss][1], pk[qb][ss][2], pk[qb][ss][3]};
+          const uint32_t *pq = pk[qb][2 * tb + ss];
+          const u32x4_t bv = {pq[0], pq[1], pq[2], pq[3]};
           acc_o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
               av, __builtin_bit_cast(bf16x8_t, bv), acc_o[qb][db], 0, 0, 0);
         }
       }
   };
 
-  // K' tiles rotate through three buffers (tile t in sK[t % 3]): a tile is read in two steps
-  // (its first half's scores in the step before its own), so the buffer written in step t must
-  // be one that no wavefront still in step t reads.  V tiles alternate between two.
-  f32x16_t sa[QB], sb[QB];  // scores of the current tile's first and second 32 tokens
-  auto step = [&](int t, int c0, int c1, int c2, bool masked, bool has_next) {
+  // One step per tile: the next tile's scores run on the matrix cores while the VALU turns the
+  // current tile's into probabilities and P V follows; the next tile's max is checked at the end
+  // of the step, next to the barrier.  K' tile t+1 and V tile t are read in step t.
+  f32x16_t a0[QB], a1[QB], b0[QB], b1[QB];
+  auto step = [&](int t, f32x16_t (&s0)[QB], f32x16_t (&s1)[QB], f32x16_t (&x0)[QB],
+                  f32x16_t (&x1)[QB], bool masked, bool has_next, bool check_next) {
     const bf16_t *vt = sV[t & 1];
-    if (masked) mask_half(t * KT, sa);
-    rescale(sa);
-    s_half(sK[c0], 1, sb);
-    probs(sa);
+    if (has_next) {
+      s_half(sK[(t + 1) & 1], 0, x0);
+      s_half(sK[(t + 1) & 1], 1, x1);
+    }
+    if (masked) {
+      mask_half(t * KT, s0);
+      mask_half(t * KT + 32, s1);
+      rescale(s0, s1);
+    }
+    probs(s0, 0);
+    probs(s1, 1);
     pv_half(vt, 0);
-    if (masked) mask_half(t * KT + 32, sb);
-    rescale(sb);
-    if (has_next) s_half(sK[c1], 0, sa);
-    probs(sb);
     pv_half(vt, 1);
-    store_K(sK[c2]);
+    if (check_next) rescale(x0, x1);
+    store_K(sK[t & 1]);
     store_V(sV[(t + 1) & 1]);
     load_K(t + 3);
     load_V(t + 2);
@@ -415,22 +429,45 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(PrefillArgs a)
   load_K(2);
   load_V(1);
   barrier();
-  s_half(sK[0], 0, sa);
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) negm[qb][r] = 0.0f;
+  s_half(sK[0], 0, a0);
+  s_half(sK[0], 1, a1);
+  mask_half(0, a0);
+  mask_half(32, a1);
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {  // every row sees token 0: its max is finite
+    float mx = a0[qb][0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = __builtin_fmaxf(mx, a0[qb][r]);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, a1[qb][r]);
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                     false, false);
+    m_i[qb] = __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      a0[qb][r] -= m_i[qb];
+      a1[qb][r] -= m_i[qb];
+      negm[qb][r] = -m_i[qb];
+    }
+  }
+  barrier();  // sK[0] is rewritten in the first step
 
-  int t = 0, c0 = 0, c1 = 1, c2 = 2;
-  for (; t < n_pipe; ++t) {
-    step(t, c0, c1, c2, false, true);
-    const int c = c0;
-    c0 = c1;
-    c1 = c2;
-    c2 = c;
+  int t = 0;
+  for (; t + 2 <= n_pipe; t += 2) {
+    step(t, a0, a1, b0, b1, false, true, true);
+    step(t + 1, b0, b1, a0, a1, false, true, t + 2 < n_pipe);
   }
   for (; t < ntile; ++t) {  // the last tiles: causal masking, and a tile without successor
-    step(t, c0, c1, c2, true, t + 1 < ntile);
-    const int c = c0;
-    c0 = c1;
-    c1 = c2;
-    c2 = c;
+    step(t, a0, a1, b0, b1, true, t + 1 < ntile, false);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      a0[qb] = b0[qb];
+      a1[qb] = b1[qb];
+    }
   }
 
 #pragma unroll
