@@ -180,22 +180,30 @@ def bench_prefill(dev, reps: int):
 
     run(None)
     torch.cuda.synchronize()
-    per_rep = []
+    # the whole prefill (8 chunk calls back to back) between two events, per rep; then one rep
+    # with events around every call for the per-chunk breakdown
+    totals = []
     for _ in range(reps):
-        ev = []
-        run(ev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        run(None)
+        e1.record()
         torch.cuda.synchronize()
-        per_rep.append([a.elapsed_time(b) for a, b in ev])
-    totals = [sum(r) for r in per_rep]
-    med = int(np.argsort(totals)[len(totals) // 2])
-    ms = totals[med]
+        totals.append(e0.elapsed_time(e1))
+    ev = []
+    run(ev)
+    torch.cuda.synchronize()
+    per_chunk = [a.elapsed_time(b) for a, b in ev]
+    ms = float(np.median(totals))
     flops = Hq * 4 * d * T * (T + 1) / 2 * B
     tflops = flops / (ms * 1e-3) / 1e12
     return {"workload": c["name"], "chunks": T // chunk, "chunk": chunk, "ms": ms,
-            "per_chunk_ms": per_rep[med], "reps": reps,
+            "ms_reps": totals, "per_chunk_ms": per_chunk, "reps": reps,
             "flops_executed_useful": flops, "tflops": tflops,
             "frac_bf16_mfma_peak": tflops / BF16_MFMA_PEAK_TFLOPS,
-            "timing": "HIP events around each aqua_prefill_chunk on the launch stream; median rep"}
+            "timing": "HIP events around the 8 aqua_prefill_chunk calls on the launch stream, "
+                      "median of reps; per_chunk_ms from events around each call in one more "
+                      "pass"}
 
 
 def bench_h2o(dev, reps: int):

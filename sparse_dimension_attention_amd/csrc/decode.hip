@@ -382,10 +382,10 @@ void decode_kernel(DecodeArgs a) {
     for (int j = 0; j < TPL; ++j) acc[h][j] = 0.0f;
 
   // Software pipeline over batches of kUnroll rows, two register sets A and B in turn: the
-  // loads of batch i + 1 are issued before the arithmetic of batch i.  Every load is
-  // unconditional (past the end it re-reads the last batch, which hits in cache), so the
-  // wait before each batch's arithmetic is exactly "one batch still in flight"; only the
-  // arithmetic of a missing odd batch is skipped, by a uniform branch.
+  // loads of batch i + 1 are issued before the arithmetic of batch i.  Inside the loop every
+  // load is unconditional, so the wait before each batch's arithmetic is exactly "one batch
+  // still in flight"; the last one or two batches are peeled off so that nothing is fetched
+  // past the end (a re-read there would go back to memory: the loads are non-temporal).
 #define AQUA_K_LOAD(BUF, BATCH)                                                          \
   _Pragma("unroll") for (int i = 0; i < kUnroll; ++i) BUF[i] = load16(                   \
       kbase + static_cast<size_t>(s_dl[min(BATCH, nbat - 1) * kUnroll + i]) * a.T_cap)
@@ -403,14 +403,26 @@ void decode_kernel(DecodeArgs a) {
   if (wave_live && nbat > 0) {
     uint4 kA[kUnroll], kB[kUnroll];
     AQUA_K_LOAD(kA, 0);
-    for (int bi = 0; bi < nbat; bi += 2) {
+    int bi = 0;
+    for (; bi + 2 < nbat; bi += 2) {
       progress_priority(bi, nbat + WT / (TPI * kUnroll));
       AQUA_K_LOAD(kB, bi + 1);
       __builtin_amdgcn_sched_barrier(0);
       AQUA_K_FMA(kA, bi);
       AQUA_K_LOAD(kA, bi + 2);
       __builtin_amdgcn_sched_barrier(0);
-      if (bi + 1 < nbat) { AQUA_K_FMA(kB, bi + 1); }
+      AQUA_K_FMA(kB, bi + 1);
+    }
+    // the last one or two batches: nothing more to prefetch
+    progress_priority(bi, nbat + WT / (TPI * kUnroll));
+    if (bi + 1 < nbat) {
+      AQUA_K_LOAD(kB, bi + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      AQUA_K_FMA(kA, bi);
+      __builtin_amdgcn_sched_barrier(0);
+      AQUA_K_FMA(kB, bi + 1);
+    } else {
+      AQUA_K_FMA(kA, bi);
     }
   }
 #undef AQUA_K_LOAD
@@ -516,14 +528,25 @@ void decode_kernel(DecodeArgs a) {
   if (vbat > 0) {
     uint4 vA[kUnroll], vB[kUnroll];
     AQUA_V_LOAD(vA, 0);
-    for (int bi = 0; bi < vbat; bi += 2) {
+    int bi = 0;
+    for (; bi + 2 < vbat; bi += 2) {
       progress_priority(nbat + bi, nbat + WT / (TPI * kUnroll));
       AQUA_V_LOAD(vB, bi + 1);
       __builtin_amdgcn_sched_barrier(0);
       AQUA_V_FMA(vA, bi);
       AQUA_V_LOAD(vA, bi + 2);
       __builtin_amdgcn_sched_barrier(0);
-      if (bi + 1 < vbat) { AQUA_V_FMA(vB, bi + 1); }
+      AQUA_V_FMA(vB, bi + 1);
+    }
+    progress_priority(nbat + bi, nbat + WT / (TPI * kUnroll));
+    if (bi + 1 < vbat) {
+      AQUA_V_LOAD(vB, bi + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      AQUA_V_FMA(vA, bi);
+      __builtin_amdgcn_sched_barrier(0);
+      AQUA_V_FMA(vB, bi + 1);
+    } else {
+      AQUA_V_FMA(vA, bi);
     }
   }
 #undef AQUA_V_LOAD

@@ -136,3 +136,19 @@ def test_prefill_llama8b_t16384_sampled():
     got = np.stack([out[b, h, p].cpu().double().numpy() for b, h, p in rows])
     assert_close(got, ref, "bf16", "prefill T16384")
     assert torch.isfinite(out).all()
+
+
+@pytest.mark.parametrize("d_sel,k", [(128, 96), (128, 5), (96, 40), (128, 127), (128, 128)])
+def test_prefill_selection_ties(d_sel, k):
+    """Many exact ties in |q'| (P = I, so q' = q: magnitudes from a tiny set, both signs, +-0;
+    bf16 has no fp32 denormals to offer beyond its own): the prefill masks must be the oracle's
+    selection of the GPU's q' (ties to the lower index), and the outputs still match."""
+    c = config(4, B=1, Hq=8, Hkv=2, T=300, k=k)
+    inp = make_prefill_inputs(c)
+    rng = np.random.default_rng(11)
+    vals = np.array([0.0, -0.0, 1.0, -1.0, 0.5, -0.5, 0.25, -0.25, 2.0], dtype=np.float32)
+    inp["q"] = torch.from_numpy(rng.choice(vals, size=tuple(inp["q"].shape))).to(torch.bfloat16)
+    inp["P"] = torch.eye(128)
+    out, qp, mask = _run_chunks(inp, c, 128, d_store=d_sel, d_sel=d_sel, k=k)
+    rows = [(0, h, p) for h in range(8) for p in range(0, 300, 13)]
+    _check(inp, c, out, qp, mask, rows, d_sel, k, d_store=d_sel)
