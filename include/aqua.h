@@ -169,6 +169,29 @@ aqua_status aqua_h2o_victim(float *mass, int32_t *slot_pos, int32_t B, int32_t H
                             int32_t n_slots, int32_t t_new, int32_t recent, int32_t *victim,
                             void *stream);
 
+/* One whole H2O decode step in one launch (H2O combined with AQUA: abstract; blog "Key
+ * Advantages"; the online step of the digest's 技术框架 and the blog's "How AQUA Works" over the
+ * kept tokens).  Equivalent, bit for bit, to
+ *   aqua_h2o_victim(mass, slot_pos, B, Hkv, T_cap, t_new, recent, victim) +
+ *   aqua_project_keys(c, k_new, v_new, P, 1, victim) +
+ *   aqua_select_dims(q, ..., d_sel, k, q_proj, mask) +
+ *   aqua_decode(c, Hq, q_proj, mask, scale, mass, out, ...)
+ * for a compact cache whose every slot holds a token (c->len == c->T_cap <= 4096): the new
+ * token at position t_new replaces the evicted slot (if any: victim is -1 when no slot is
+ * older than the recent window, and then the new token is not cached), every query head selects
+ * its dims and attends over all slots, and every slot's mass grows by the group's weights (the
+ * replaced slot's mass restarts at 0 first).  c->len does not change.
+ *   q, k_new, v_new, P, d_sel, k, scale: as aqua_decode_step (k_new/v_new [B][Hkv][d_head]).
+ *   mass    : device fp32 [B][Hkv][T_cap] (read and written).
+ *   slot_pos: device int32 [B][Hkv][T_cap] (read and written).
+ *   victim  : out device int32 [B][Hkv].
+ *   out, q_proj_out, mask_out, ws, ws_bytes: as aqua_decode_step (the same workspace size). */
+aqua_status aqua_h2o_step(aqua_cache *c, int32_t Hq, const void *q, const void *k_new,
+                          const void *v_new, const float *P, int32_t d_sel, int32_t k,
+                          float scale, float *mass, int32_t *slot_pos, int32_t t_new,
+                          int32_t recent, int32_t *victim, float *out, float *q_proj_out,
+                          uint32_t *mask_out, void *ws, size_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -26,7 +26,7 @@ _STATUS_NAMES = {0: "AQUA_OK", 1: "AQUA_ERR_NULL", 2: "AQUA_ERR_SHAPE", 3: "AQUA
 
 EXPORTS = ("aqua_version", "aqua_last_error", "aqua_project_keys", "aqua_select_dims",
            "aqua_decode_workspace", "aqua_decode", "aqua_decode_step", "aqua_prefill_workspace",
-           "aqua_prefill_chunk", "aqua_h2o_victim")
+           "aqua_prefill_chunk", "aqua_h2o_victim", "aqua_h2o_step")
 
 
 class AquaError(RuntimeError):
@@ -67,6 +67,8 @@ def load_library() -> ctypes.CDLL:
         "aqua_prefill_chunk": ([cp, I32, P, I32, I32, P, I32, I32, ctypes.c_float, P, P, P, P,
                                 SZ, P], ctypes.c_int),
         "aqua_h2o_victim": ([P, P, I32, I32, I32, I32, I32, P, P], ctypes.c_int),
+        "aqua_h2o_step": ([cp, I32, P, P, P, P, I32, I32, ctypes.c_float, P, P, I32, I32, P, P, P,
+                           P, P, SZ, P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -176,3 +178,14 @@ def aqua_h2o_victim(mass, slot_pos, t_new: int, recent: int, victim, stream=None
     _check(load_library().aqua_h2o_victim(_ptr(mass), _ptr(slot_pos), int(B), int(Hkv),
                                           int(n_slots), int(t_new), int(recent), _ptr(victim),
                                           _stream(stream)))
+
+
+def aqua_h2o_step(cache: aqua_cache, Hq: int, q, k_new, v_new, P, d_sel: int, k: int,
+                  scale: float, mass, slot_pos, t_new: int, recent: int, victim, out, ws,
+                  q_proj_out=None, mask_out=None, stream=None):
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(load_library().aqua_h2o_step(ctypes.byref(cache), int(Hq), _ptr(q), _ptr(k_new),
+                                        _ptr(v_new), _ptr(P), int(d_sel), int(k), float(scale),
+                                        _ptr(mass), _ptr(slot_pos), int(t_new), int(recent),
+                                        _ptr(victim), _ptr(out), _ptr(q_proj_out),
+                                        _ptr(mask_out), _ptr(ws), nbytes, _stream(stream)))

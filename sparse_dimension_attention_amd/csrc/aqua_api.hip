@@ -274,3 +274,69 @@ aqua_status aqua_h2o_victim(float *mass, int32_t *slot_pos, int32_t B, int32_t H
 }
 
 }  // extern "C"
+
+aqua_status aqua_h2o_step(aqua_cache *c, int32_t Hq, const void *q, const void *k_new,
+                          const void *v_new, const float *P, int32_t d_sel, int32_t k,
+                          float scale, float *mass, int32_t *slot_pos, int32_t t_new,
+                          int32_t recent, int32_t *victim, float *out, float *q_proj_out,
+                          uint32_t *mask_out, void *ws, size_t ws_bytes, void *stream) {
+  g_err[0] = 0;
+  if (aqua_status st = check_cache(c)) return st;
+  if (aqua_status st = check_heads(c, Hq)) return st;
+  if (!q || !k_new || !v_new || !P || !mass || !slot_pos || !victim || !out)
+    return fail(AQUA_ERR_NULL, "q, k_new, v_new, P, mass, slot_pos, victim and out are required");
+  if (!ws) return fail(AQUA_ERR_WORKSPACE, "workspace is NULL");
+  if (c->len != c->T_cap)
+    return fail(AQUA_ERR_SHAPE, "len=%d: every slot of the compact cache must hold a token "
+                "(len == T_cap=%d)", c->len, c->T_cap);
+  if (c->len > aqua::kDecodeShortMax)
+    return fail(AQUA_ERR_SHAPE, "%d slots: the fused H2O step takes at most %d", c->len,
+                aqua::kDecodeShortMax);
+  if (!(1 <= k && k <= d_sel && d_sel <= c->d_store))
+    return fail(AQUA_ERR_SHAPE, "need 1 <= k (%d) <= d_sel (%d) <= d_store (%d)", k, d_sel,
+                c->d_store);
+  if (t_new < 0 || recent < 0)
+    return fail(AQUA_ERR_SHAPE, "t_new=%d and recent=%d must be >= 0", t_new, recent);
+  if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(P) ||
+      !aligned16(out) || !aligned16(ws) || !aligned16(mass) ||
+      (q_proj_out && !aligned16(q_proj_out)) || (mask_out && !aligned16(mask_out)))
+    return fail(AQUA_ERR_ALIGN, "all buffers must be 16-byte aligned");
+  const size_t need =
+      aqua::decode_workspace_bytes(c->dtype, c->B, Hq, c->Hkv, c->d_head, c->T_cap);
+  if (ws_bytes < need)
+    return fail(AQUA_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, need);
+
+  aqua::DecodeArgs a{};
+  a.kp = c->kp;
+  a.v = c->v;
+  a.kp_w = c->kp;
+  a.v_w = c->v;
+  a.mass = mass;
+  a.out = out;
+  aqua::decode_workspace_carve(ws, c->dtype, c->B, Hq, c->Hkv, c->d_head, c->T_cap,
+                               &a.counters, &a.partials, &a.scores);
+  a.B = c->B;
+  a.Hq = Hq;
+  a.Hkv = c->Hkv;
+  a.d = c->d_head;
+  a.d_store = c->d_store;
+  a.T_cap = c->T_cap;
+  a.len = c->len;
+  a.S = aqua::decode_splits(c->dtype, Hq / c->Hkv, c->len);
+  a.qscale = scale * 1.4426950408889634f;
+  a.q_raw = q;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.P = P;
+  a.q_proj_out = q_proj_out;
+  a.mask_out = mask_out;
+  a.d_sel = d_sel;
+  a.k = k;
+  aqua::H2OArgs h{};
+  h.slot_pos = slot_pos;
+  h.victim = victim;
+  h.t_new = t_new;
+  h.recent = recent;
+  return hip_status(aqua::launch_h2o_step(c->dtype, a, h, static_cast<hipStream_t>(stream)),
+                    "aqua_h2o_step launch");
+}

@@ -108,6 +108,65 @@ __device__ __forceinline__ void wave_topk_threshold(const float (&x)[E], int d_s
   }
 }
 
+// ------------------------------------------------------------------ H2O eviction rule
+// Among the slots of one (b, g) holding a position <= limit (t_new - recent), the one ranked lowest
+// by (mass descending, position ascending): the minimum of the 64-bit key (mass bits,
+// 0x7fffffff - position), mass >= 0 so that its fp32 bits order like the value; equal keys go
+// to the lower slot.  Called by every thread of a 256-thread workgroup (it holds barriers);
+// returns the slot, or -1 if no slot qualifies, in every thread.
+__device__ __forceinline__ void h2o_keep_min(uint64_t &key, int &slot, uint64_t k2, int s2) {
+  if (k2 < key || (k2 == key && s2 < slot)) {
+    key = k2;
+    slot = s2;
+  }
+}
+
+__device__ __forceinline__ int h2o_pick_victim(const float *mass, const int32_t *pos, int n_slots,
+                                               int limit) {
+  __shared__ uint64_t s_key[4];
+  __shared__ int s_slot[4];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  uint64_t key = ~0ull;
+  int slot = 0x7fffffff;
+  constexpr int BATCH = 16;  // slots per thread whose loads are in flight together
+  for (int s0 = tid; s0 < n_slots; s0 += 256 * BATCH) {
+    float mv[BATCH];
+    int pv[BATCH];
+#pragma unroll
+    for (int i = 0; i < BATCH; ++i) {  // unconditional loads (clamped), validity applied below
+      const int s = min(s0 + 256 * i, n_slots - 1);
+      pv[i] = pos[s];
+      mv[i] = mass[s];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < BATCH; ++i)
+      if (s0 + 256 * i >= n_slots) pv[i] = -1;
+#pragma unroll
+    for (int i = 0; i < BATCH; ++i)
+      if (pv[i] >= 0 && pv[i] <= limit)
+        h2o_keep_min(key, slot,
+                     (static_cast<uint64_t>(__float_as_uint(mv[i])) << 32) |
+                         static_cast<uint32_t>(0x7fffffff - pv[i]),
+                     s0 + 256 * i);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const uint64_t k2 = __shfl_xor(key, off, 64);
+    const int s2 = __shfl_xor(slot, off, 64);
+    h2o_keep_min(key, slot, k2, s2);
+  }
+  if (lane == 0) {
+    s_key[w] = key;
+    s_slot[w] = slot;
+  }
+  __syncthreads();
+  key = s_key[0];
+  slot = s_slot[0];
+  for (int x = 1; x < 4; ++x) h2o_keep_min(key, slot, s_key[x], s_slot[x]);
+  return key == ~0ull ? -1 : slot;
+}
+
 // ------------------------------------------------------------------ launch parameter blocks
 struct DecodeArgs {
   const void *kp;        // [B][Hkv][d_store][T_cap]
@@ -131,6 +190,14 @@ struct DecodeArgs {
   uint32_t *mask_out;    // [B][Hq][d/32] or nullptr
   void *kp_w, *v_w;      // the cache, written at column len - 1
   int d_sel, k;
+};
+
+// Fused H2O step only: the compact cache's slot positions, the step's position and window, and
+// where the evicted slot is reported.
+struct H2OArgs {
+  int32_t *slot_pos;  // [B][Hkv][n_slots], n_slots = T_cap = len
+  int32_t *victim;    // [B][Hkv]
+  int t_new, recent;
 };
 
 struct DecodeLayout {
@@ -157,6 +224,7 @@ hipError_t launch_project_keys(int dtype, const void *k_raw, const void *v_raw, 
                                const int32_t *slots, void *kp, void *v, hipStream_t s);
 hipError_t launch_decode(int dtype, const DecodeArgs &a, hipStream_t s);
 hipError_t launch_decode_step(int dtype, const DecodeArgs &a, hipStream_t s);
+hipError_t launch_h2o_step(int dtype, const DecodeArgs &a, const H2OArgs &h, hipStream_t s);
 size_t prefill_workspace_bytes(int B, int Hq, int Lq);
 hipError_t launch_prefill(const void *kp, const void *v, int B, int Hq, int Hkv, int d_store,
                           int T_cap, const void *q, int Lq, int pos0, const float *P, int d_sel,

@@ -96,12 +96,28 @@ struct DecodeSmem {
 
 // The last workgroup of a (b, g): merge the S partials (m, l, o) of every head into the output
 // and, in mass mode, add every token's normalised probability (summed over the group's heads)
-// to its mass.  The partials and scores were written by other workgroups, possibly on other
-// XCDs, so they are read past the non-coherent caches; each thread issues up to 8 such loads
-// at once, so that the merge costs a few memory round trips rather than one per split.
+// to its mass (slot `restart`, if any, starts again from 0).  The partials and scores were
+// written by other workgroups, possibly on other XCDs, so they are read past the non-coherent
+// caches; each thread issues up to 8 such loads at once, so that the merge costs a few memory
+// round trips rather than one per split.
 template <int D, int G, int NT>
-__device__ void merge_splits(const DecodeArgs &a, size_t head0, int bg, float *s_M, float *s_L) {
+__device__ void merge_splits(const DecodeArgs &a, size_t head0, int bg, float *s_M, float *s_L,
+                             int restart = -1) {
   constexpr int CH = 8;
+  // mass mode: the first batch of scores and masses is loaded before the partials, so that the
+  // two sets of round trips overlap
+  float *mass = a.mass ? a.mass + static_cast<size_t>(bg) * a.T_cap : nullptr;
+  float sc[CH][G], mv[CH];
+  auto load_batch = [&](int t0) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int t = min(t0 + c * NT, a.len - 1);
+#pragma unroll
+      for (int h = 0; h < G; ++h) sc[c][h] = coherent_load(a.scores + (head0 + h) * a.T_cap + t);
+      mv[c] = mass[t];
+    }
+  };
+  if (mass) load_batch(threadIdx.x);
   for (int e = threadIdx.x; e < G * D; e += NT) {
     const int h = e / D, dd = e - h * D;
     const float *part = a.partials + (head0 + h) * a.S * (D + 2);
@@ -119,9 +135,9 @@ __device__ void merge_splits(const DecodeArgs &a, size_t head0, int bg, float *s
 #pragma unroll
       for (int c = 0; c < CH; ++c)
         if (s0 + c < a.S) Mc = fmaxf(Mc, ms[c]);
-      const float sc = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(M - Mc);
-      O *= sc;
-      L *= sc;
+      const float rs = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(M - Mc);
+      O *= rs;
+      L *= rs;
 #pragma unroll
       for (int c = 0; c < CH; ++c) {
         const float al = (s0 + c >= a.S || ms[c] == -INFINITY)
@@ -138,17 +154,10 @@ __device__ void merge_splits(const DecodeArgs &a, size_t head0, int bg, float *s
       s_L[h] = L;
     }
   }
-  if (a.mass) {
+  if (mass) {
     __syncthreads();
-    float *mass = a.mass + static_cast<size_t>(bg) * a.T_cap;
     for (int t0 = threadIdx.x; t0 < a.len; t0 += NT * CH) {
-      float sc[CH][G];
-#pragma unroll
-      for (int c = 0; c < CH; ++c) {
-        const int t = min(t0 + c * NT, a.len - 1);
-#pragma unroll
-        for (int h = 0; h < G; ++h) sc[c][h] = coherent_load(a.scores + (head0 + h) * a.T_cap + t);
-      }
+      if (t0 != static_cast<int>(threadIdx.x)) load_batch(t0);
 #pragma unroll
       for (int c = 0; c < CH; ++c) {
         const int t = t0 + c * NT;
@@ -156,12 +165,123 @@ __device__ void merge_splits(const DecodeArgs &a, size_t head0, int bg, float *s
           float add = 0.0f;
 #pragma unroll
           for (int h = 0; h < G; ++h) add += __builtin_amdgcn_exp2f(sc[c][h] - s_M[h]) / s_L[h];
-          mass[t] += add;
+          mass[t] = (t == restart ? 0.0f : mv[c]) + add;  // a restarted slot's mass begins at 0
         }
       }
     }
   }
   if (threadIdx.x == 0) atomicExch(&a.counters[bg], 0u);
+}
+
+// Fused prologue shared by the fused decode step and the fused H2O step: stage P in LDS, project
+// the group's G query rows and, when with_key, the new token's key (q'_h[i] = sum_j q_h[j] P[j][i]
+// in fp32, j ascending: the arithmetic of select_kernel and of the key projection, so the results
+// are those of the separate calls bit for bit), keep the key's stored (rounded) K' and raw V in
+// LDS, and select every head's top-k dims into mask words.  split0 writes q_proj_out / mask_out.
+// LDS: sP [D][D], sq [G+1][D], s_qp [G+1][D], s_mw [G][D/32], s_knew and s_vnew [D].
+// after_staging() runs once P and the rows are on their way to LDS (the caller issues its own
+// loads there).  Ends with a workgroup barrier.
+template <typename KT, int D, int G, int NT, typename F>
+__device__ __forceinline__ void fused_project_select(const DecodeArgs &a, size_t head0, int bg,
+                                                     bool with_key, bool split0, float *sP,
+                                                     float (*sq)[D], float (*s_qp)[D],
+                                                     uint32_t (*s_mw)[D / 32], float *s_knew,
+                                                     float *s_vnew, F &&after_staging) {
+  constexpr int NWORD = D / 32;
+  constexpr int E = D / 64;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // the raw rows' loads first, so that they are in flight with P's; then the LDS stores
+  constexpr int QPT = (G * D + NT - 1) / NT;  // raw query elements per thread
+  constexpr int NV = D * D / (NT * 4);        // 16-byte pieces of P per thread
+  const KT *qr = static_cast<const KT *>(a.q_raw) + head0 * D;
+  const size_t at = static_cast<size_t>(bg) * D + min(tid, D - 1);
+  float qv[QPT];
+#pragma unroll
+  for (int r = 0; r < QPT; ++r) qv[r] = load_elem<KT>(qr + min(tid + r * NT, G * D - 1));
+  const float kn = load_elem<KT>(static_cast<const KT *>(a.k_new) + at);
+  const float vn = load_elem<KT>(static_cast<const KT *>(a.v_new) + at);
+  constexpr int CH = NV < 16 ? NV : 16;  // P pieces per batch of loads
+#pragma unroll
+  for (int v0 = 0; v0 < NV; v0 += CH) {
+    float4 st[CH];
+#pragma unroll
+    for (int v = 0; v < CH; ++v)
+      st[v] = *reinterpret_cast<const float4 *>(&a.P[((v0 + v) * NT + tid) * 4]);
+#pragma unroll
+    for (int v = 0; v < CH; ++v)
+      *reinterpret_cast<float4 *>(&sP[((v0 + v) * NT + tid) * 4]) = st[v];
+  }
+#pragma unroll
+  for (int r = 0; r < QPT; ++r)
+    if (tid + r * NT < G * D) sq[(tid + r * NT) / D][(tid + r * NT) % D] = qv[r];
+  if (with_key && tid < D) {
+    sq[G][tid] = kn;
+    s_vnew[tid] = vn;
+  }
+  after_staging();  // the caller's loads go out while the projection runs
+  __syncthreads();
+  // q'_h[i] = sum_j q_h[j] P[j][i] (fp32, j ascending); thread -> dim i, rows r0, r0+NT/D, ...
+  // The j loop is fully unrolled and branch-free (rows past the last are computed on a
+  // clamped row and discarded), so the LDS reads of later j are issued ahead of the fmas.
+  {
+    constexpr int RSTEP = NT / D;
+    constexpr int RPT = (G + 1 + RSTEP - 1) / RSTEP;
+    const int nrows = G + (with_key ? 1 : 0);
+    const int i = tid % D, r0 = tid / D;
+    float acc[RPT];
+    int row[RPT];
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+      acc[r] = 0.0f;
+      row[r] = min(r0 + r * RSTEP, G);
+    }
+#pragma unroll 8
+    for (int j = 0; j < D; j += 4) {
+      float p[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) p[c] = sP[(j + c) * D + i];
+#pragma unroll
+      for (int r = 0; r < RPT; ++r) {
+        const float4 q4 = *reinterpret_cast<const float4 *>(&sq[row[r]][j]);  // broadcast
+        acc[r] = fmaf(q4.x, p[0], acc[r]);
+        acc[r] = fmaf(q4.y, p[1], acc[r]);
+        acc[r] = fmaf(q4.z, p[2], acc[r]);
+        acc[r] = fmaf(q4.w, p[3], acc[r]);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < RPT; ++r)
+      if (r0 + r * RSTEP < nrows) s_qp[r0 + r * RSTEP][i] = acc[r];
+  }
+  __syncthreads();
+  if (with_key && tid < D) {
+    // the new token's K' as it will be stored (rounded once); the caller writes it to the cache
+    // only after its own reads of that column are done
+    const KT kq = store_elem<KT>(s_qp[G][tid]);
+    s_knew[tid] = load_elem<KT>(&kq);
+  }
+  for (int h = w; h < G; h += NT / 64) {
+    float x[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) x[e] = s_qp[h][lane + 64 * e];
+    bool sel[E];
+    wave_topk_threshold<E>(x, a.d_sel, a.k, sel);
+    uint64_t sb[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) sb[e] = __ballot(sel[e]);
+    if (lane < NWORD) {
+      const uint64_t bb = (lane >> 1) ? sb[E - 1] : sb[0];
+      const uint32_t word =
+          (lane & 1) ? static_cast<uint32_t>(bb >> 32) : static_cast<uint32_t>(bb);
+      s_mw[h][lane] = word;
+      if (split0 && a.mask_out) a.mask_out[(head0 + h) * NWORD + lane] = word;
+    }
+    if (split0 && a.q_proj_out) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) a.q_proj_out[(head0 + h) * D + lane + 64 * e] = x[e];
+    }
+  }
+  __syncthreads();
 }
 
 // Two workgroups share each CU, and the issue arbiter favours older wavefronts: left alone, the
@@ -216,95 +336,11 @@ void decode_kernel(DecodeArgs a) {
   const bool owner = FUSED && split == (a.len - 1) / SPLIT;
 
   // ---- fused prologue: project the group's queries (and the new key), select their dims
-  if constexpr (FUSED) {
-    float *sP = reinterpret_cast<float *>(smem);
-    float(*sq)[D] = reinterpret_cast<float(*)[D]>(smem + D * D * 4);
-    {
-      // P into LDS in chunks of CH 16-byte loads per thread (each chunk one L2 round trip)
-      constexpr int NV = D * D / (NT * 4);
-      constexpr int CH = NV < 16 ? NV : 16;
-#pragma unroll
-      for (int v0 = 0; v0 < NV; v0 += CH) {
-        float4 st[CH];
-#pragma unroll
-        for (int v = 0; v < CH; ++v)
-          st[v] = *reinterpret_cast<const float4 *>(&a.P[((v0 + v) * NT + tid) * 4]);
-#pragma unroll
-        for (int v = 0; v < CH; ++v)
-          *reinterpret_cast<float4 *>(&sP[((v0 + v) * NT + tid) * 4]) = st[v];
-      }
-    }
-    const KT *qr = static_cast<const KT *>(a.q_raw) + head0 * D;
-    for (int e = tid; e < G * D; e += NT) sq[e / D][e % D] = load_elem<KT>(qr + e);
-    if (owner && tid < D) {
-      const size_t at = static_cast<size_t>(bg) * D + tid;
-      sq[G][tid] = load_elem<KT>(static_cast<const KT *>(a.k_new) + at);
-      s_vnew[tid] = load_elem<KT>(static_cast<const KT *>(a.v_new) + at);
-    }
-    __syncthreads();
-    // q'_h[i] = sum_j q_h[j] P[j][i] (fp32, j ascending); thread -> dim i, rows r0, r0+NT/D, ...
-    // The j loop is fully unrolled and branch-free (rows past the last are computed on a
-    // clamped row and discarded), so the LDS reads of later j are issued ahead of the fmas.
-    {
-      constexpr int RSTEP = NT / D;
-      constexpr int RPT = (G + 1 + RSTEP - 1) / RSTEP;
-      const int nrows = G + (owner ? 1 : 0);
-      const int i = tid % D, r0 = tid / D;
-      float acc[RPT];
-      int row[RPT];
-#pragma unroll
-      for (int r = 0; r < RPT; ++r) {
-        acc[r] = 0.0f;
-        row[r] = min(r0 + r * RSTEP, G);
-      }
-#pragma unroll 8
-      for (int j = 0; j < D; j += 4) {
-        float p[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) p[c] = sP[(j + c) * D + i];
-#pragma unroll
-        for (int r = 0; r < RPT; ++r) {
-          const float4 q4 = *reinterpret_cast<const float4 *>(&sq[row[r]][j]);  // broadcast
-          acc[r] = fmaf(q4.x, p[0], acc[r]);
-          acc[r] = fmaf(q4.y, p[1], acc[r]);
-          acc[r] = fmaf(q4.z, p[2], acc[r]);
-          acc[r] = fmaf(q4.w, p[3], acc[r]);
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < RPT; ++r)
-        if (r0 + r * RSTEP < nrows) s_qp[r0 + r * RSTEP][i] = acc[r];
-    }
-    __syncthreads();
-    if (owner && tid < D) {
-      // the new token's K' as it will be stored (rounded once); it reaches the cache only after
-      // this workgroup's K' loads are done (they cover the same 16-byte chunk)
-      const KT kq = store_elem<KT>(s_qp[G][tid]);
-      s_knew[tid] = load_elem<KT>(&kq);
-    }
-    for (int h = w; h < G; h += NW) {
-      float x[E];
-#pragma unroll
-      for (int e = 0; e < E; ++e) x[e] = s_qp[h][lane + 64 * e];
-      bool sel[E];
-      wave_topk_threshold<E>(x, a.d_sel, a.k, sel);
-      uint64_t sb[E];
-#pragma unroll
-      for (int e = 0; e < E; ++e) sb[e] = __ballot(sel[e]);
-      if (lane < NWORD) {
-        const uint64_t bb = (lane >> 1) ? sb[E - 1] : sb[0];
-        const uint32_t word =
-            (lane & 1) ? static_cast<uint32_t>(bb >> 32) : static_cast<uint32_t>(bb);
-        s_mw[h][lane] = word;
-        if (split == 0 && a.mask_out) a.mask_out[(head0 + h) * NWORD + lane] = word;
-      }
-      if (split == 0 && a.q_proj_out) {
-#pragma unroll
-        for (int e = 0; e < E; ++e) a.q_proj_out[(head0 + h) * D + lane + 64 * e] = x[e];
-      }
-    }
-    __syncthreads();
-  }
+  if constexpr (FUSED)
+    fused_project_select<KT, D, G, NT>(a, head0, bg, owner, split == 0,
+                                       reinterpret_cast<float *>(smem),
+                                       reinterpret_cast<float(*)[D]>(smem + D * D * 4), s_qp,
+                                       s_mw, s_knew, s_vnew, [] {});
 
   // ---- union of the group's masks, restricted to stored dims (uniform per workgroup)
   auto mask_word = [&](int h, int wd) -> uint32_t {
@@ -617,23 +653,43 @@ void decode_kernel(DecodeArgs a) {
 // With few tokens (a compact H2O cache of 1280 slots, a prompt's first steps) the split-T layout
 // above gives one workgroup per KV group, whose wavefronts each walk the whole union U of K'
 // rows one batch after another: latency, not bandwidth.  Here a workgroup takes 256 tokens and
-// its 4 wavefronts split U instead (wavefront w reads rows w, w + 4, ...; every load of a
-// wavefront is in flight at once), add their partial scores in LDS, and then split the tokens
-// (64 each) for the softmax and the V pass.  Partials, the last-workgroup merge and the mass
-// update are as above.
+// its 4 wavefronts split the stored dims (wavefront w reads dims w, w + 4, ..., a dim that no
+// head selected weighing 0).  Every K' and V load of the workgroup is issued first, so that the
+// reads of the masks and q' (in the H2O form: the eviction and the selection) overlap them; the
+// partial scores are added in LDS, then the tokens are split (64 per wavefront) for the softmax
+// and the V pass.
+// Partials, the last-workgroup merge and the mass update are as above.
+//
+// H2O form (the fused H2O step: one launch per decode step over a compact H2O cache whose every
+// slot holds a token): eviction, the new token's K' and V, the group's selection and the
+// mass-mode attention.  Each workgroup picks the victim itself (h2o_pick_victim on the masses as
+// they stand: only the group's last workgroup writes them, after every other one has read them)
+// and projects and selects the group's queries (fused_project_select).  The workgroup whose chunk
+// holds the victim slot also projects the new key, and inside its chunk the slot's cached K' and
+// V are replaced by the new token's (from LDS) in the partial scores and the V pass, so every
+// number is the one the separate calls (aqua_h2o_victim, aqua_project_keys with slots,
+// aqua_select_dims, aqua_decode in mass mode) compute.  That workgroup writes the new K' and V
+// into the slot after its own reads of it; the group's last workgroup merges, sets the slot's
+// position and restarts its mass from 0 before adding this step's weights.
 constexpr int kShortChunk = 256;
 
-template <typename KT, int D, int G>
-__global__ __launch_bounds__(256) void decode_short_kernel(DecodeArgs a) {
+template <typename KT, int D, int G, bool H2O>
+__device__ __forceinline__ void short_attend(const DecodeArgs &a, const H2OArgs &hh) {
+  constexpr int NT = 256;
   constexpr int NWORD = D / 32;
   constexpr int TPL = 4;                  // tokens per lane per K' row load
   constexpr int EPL = 16 / sizeof(KT);    // V elements per lane per 16-byte load
   constexpr int LPT = D / EPL;            // lanes per V row
   constexpr int TPI = 64 / LPT;           // V rows per wavefront load
-  constexpr int RW = (D + 3) / 4;         // most K' rows a wavefront reads
+  constexpr int RW = D / 4;               // most K' rows a wavefront reads
+  constexpr int NL = 64 / TPI;            // V loads per lane
   typedef typename std::conditional<sizeof(KT) == 2, uint2, uint4>::type kvec;
-  __shared__ int s_dl[D];
-  __shared__ float s_qw[D][G];
+  __shared__ __align__(16) float sP[H2O ? D * D : 1];
+  __shared__ __align__(16) float sq[H2O ? G + 1 : 1][D];
+  __shared__ float s_qp[H2O ? G + 1 : 1][D];
+  __shared__ uint32_t s_mw[H2O ? G : 1][NWORD];
+  __shared__ float s_knew[H2O ? D : 1], s_vnew[H2O ? D : 1];
+  __shared__ float s_qw[D][G];                 // head weights of every stored dim (0: unselected)
   __shared__ float s_part[4][kShortChunk][G];  // partial scores; then the probabilities
   __shared__ float s_o[4][G][D];
   __shared__ float s_wm[4][G], s_wl[4][G], s_M[G], s_L[G];
@@ -643,81 +699,107 @@ __global__ __launch_bounds__(256) void decode_short_kernel(DecodeArgs a) {
   const int bg = blockIdx.x / a.S, split = blockIdx.x - bg * a.S;
   const int b = bg / a.Hkv, g = bg - b * a.Hkv;
   const size_t head0 = static_cast<size_t>(b) * a.Hq + static_cast<size_t>(g) * G;
+  const size_t slot0 = static_cast<size_t>(bg) * a.T_cap;
   const int t0 = split * kShortChunk;
 
-  // ---- union of the group's masks (stored dims only), as a list of rows with head weights
-  uint32_t U[NWORD];
-  int nU = 0;
+  // ---- K' of this chunk, wavefront w's stored dims, every load in flight at once
+  const int tl = min(t0 + TPL * lane, a.T_cap - TPL);  // stays inside the row; masked below
+  const KT *kbase =
+      static_cast<const KT *>(a.kp) + static_cast<size_t>(bg) * a.d_store * a.T_cap + tl;
+  const int nw = a.d_store > w ? (a.d_store - w + 3) / 4 : 0;  // rows of this wavefront
+  kvec kr[RW];
+  auto load_k = [&]() {
 #pragma unroll
-  for (int wd = 0; wd < NWORD; ++wd) {
-    uint32_t u = 0;
-#pragma unroll
-    for (int h = 0; h < G; ++h) u |= a.mask[(head0 + h) * NWORD + wd];
-    const int lo = wd * 32;
-    if (a.d_store <= lo) u = 0;
-    else if (a.d_store < lo + 32) u &= (1u << (a.d_store - lo)) - 1u;
-    U[wd] = u;
-    nU += __popc(u);
-  }
-  if (tid < D) {
-    const int wd = tid >> 5, bit = tid & 31;
-    uint32_t uw = 0;
-    int pos = 0;
-#pragma unroll
-    for (int x = 0; x < NWORD; ++x) {
-      if (x < wd) pos += __popc(U[x]);
-      if (x == wd) uw = U[x];
+    for (int i = 0; i < RW; ++i) {  // rows past nw re-read a stored row (never used)
+      const int dim = i < nw ? w + 4 * i : min(w, a.d_store - 1);
+      kr[i] = *reinterpret_cast<const kvec *>(kbase + static_cast<size_t>(dim) * a.T_cap);
     }
-    if ((uw >> bit) & 1u) {
-      pos += __popc(uw & ((1u << bit) - 1u));
-      s_dl[pos] = tid;
+  };
+
+  // ---- V of the wavefront's 64 tokens (t0 + 64 w ..).  K' and V loads go out here, or in the
+  // H2O form once the prologue's own loads are on their way (held across those, their registers
+  // would make the compiler issue P's loads one at a time)
+  const int sub = lane / LPT, cl = lane - sub * LPT;
+  const int last = a.len - 1;
+  const KT *vbase = static_cast<const KT *>(a.v) + slot0 * D + cl * EPL;
+  uint4 vr[NL];
+  auto load_v = [&]() {
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const uint32_t mw = a.mask[(head0 + h) * NWORD + wd];
-        s_qw[pos][h] = ((mw >> bit) & 1u) ? a.q_proj[(head0 + h) * D + tid] * a.qscale : 0.0f;
+    for (int i = 0; i < NL; ++i) {  // rows past the last token re-read it (their p is 0)
+      const int t = min(t0 + 64 * w + i * TPI + sub, last);
+      vr[i] = load16(vbase + static_cast<size_t>(t) * D);
+    }
+  };
+  if constexpr (!H2O) {
+    load_k();
+    load_v();
+  }
+
+  int victim = -1;
+  if constexpr (H2O) {
+    victim = h2o_pick_victim(a.mass + slot0, hh.slot_pos + slot0, a.len, hh.t_new - hh.recent);
+    if (split == 0 && tid == 0) hh.victim[bg] = victim;
+  }
+  const bool owner = H2O && victim >= t0 && victim < t0 + kShortChunk;  // false if victim is -1
+  if constexpr (H2O)
+    fused_project_select<KT, D, G, NT>(a, head0, bg, owner, split == 0, sP, sq, s_qp, s_mw,
+                                       s_knew, s_vnew, [&] {
+                                         load_k();
+                                         load_v();
+                                       });
+
+  // ---- every stored dim's weight per head: q'_i * scale * log2 e where the head selected it
+  if (tid < a.d_store) {
+    const int wd = tid >> 5, bit = tid & 31;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      uint32_t mw;
+      float qv;
+      if constexpr (H2O) {
+        mw = s_mw[h][wd];
+        qv = s_qp[h][tid];
+      } else {
+        mw = a.mask[(head0 + h) * NWORD + wd];
+        qv = a.q_proj[(head0 + h) * D + tid];
       }
+      s_qw[tid][h] = ((mw >> bit) & 1u) ? qv * a.qscale : 0.0f;
     }
   }
   __syncthreads();
 
-  // ---- partial scores: wavefront w takes rows w, w + 4, ... of the list, all loads at once
-  const int tl = min(t0 + TPL * lane, a.T_cap - TPL);  // stays inside the row; masked below
-  const KT *kbase = static_cast<const KT *>(a.kp) + static_cast<size_t>(bg) * a.d_store * a.T_cap + tl;
-  const int nw = nU > w ? (nU - w + 3) / 4 : 0;  // rows of this wavefront
+  // ---- partial scores (the victim slot, in the owner's chunk, takes the new token's K')
+  const int vj = owner ? victim - tl : -1;  // the victim's token among this lane's four
   float acc[G][TPL];
 #pragma unroll
   for (int h = 0; h < G; ++h)
 #pragma unroll
     for (int j = 0; j < TPL; ++j) acc[h][j] = 0.0f;
-  {
-    kvec kr[RW];
 #pragma unroll
-    for (int i = 0; i < RW; ++i) {  // rows past nw re-read row w (their weight is 0)
-      const int u = i < nw ? w + 4 * i : w;
-      kr[i] = nw > 0 ? *reinterpret_cast<const kvec *>(kbase + static_cast<size_t>(s_dl[u]) * a.T_cap)
-                     : kvec{};
-    }
+  for (int i = 0; i < RW; ++i) {
+    if (i < nw) {  // uniform over the wavefront
+      float kv[TPL];
+      if constexpr (sizeof(KT) == 2) {
+        kv[0] = bf16_lo(kr[i].x); kv[1] = bf16_hi(kr[i].x);
+        kv[2] = bf16_lo(kr[i].y); kv[3] = bf16_hi(kr[i].y);
+      } else {
+        kv[0] = __uint_as_float(kr[i].x); kv[1] = __uint_as_float(kr[i].y);
+        kv[2] = __uint_as_float(kr[i].z); kv[3] = __uint_as_float(kr[i].w);
+      }
+      const int dim = w + 4 * i;
+      if constexpr (H2O) {
 #pragma unroll
-    for (int i = 0; i < RW; ++i) {
-      if (i < nw) {  // uniform over the wavefront
-        float kv[TPL];
-        if constexpr (sizeof(KT) == 2) {
-          kv[0] = bf16_lo(kr[i].x); kv[1] = bf16_hi(kr[i].x);
-          kv[2] = bf16_lo(kr[i].y); kv[3] = bf16_hi(kr[i].y);
-        } else {
-          kv[0] = __uint_as_float(kr[i].x); kv[1] = __uint_as_float(kr[i].y);
-          kv[2] = __uint_as_float(kr[i].z); kv[3] = __uint_as_float(kr[i].w);
-        }
-        const int u = w + 4 * i;
+        for (int j = 0; j < TPL; ++j)
+          if (j == vj) kv[j] = s_knew[dim];
+      }
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float qw = s_qw[u][h];
+      for (int h = 0; h < G; ++h) {
+        const float qw = s_qw[dim][h];
 #pragma unroll
-          for (int j = 0; j < TPL; ++j) acc[h][j] = fmaf(qw, kv[j], acc[h][j]);
-        }
+        for (int j = 0; j < TPL; ++j) acc[h][j] = fmaf(qw, kv[j], acc[h][j]);
       }
     }
   }
+
 #pragma unroll
   for (int j = 0; j < TPL; ++j)
 #pragma unroll
@@ -739,34 +821,28 @@ __global__ __launch_bounds__(256) void decode_short_kernel(DecodeArgs a) {
     s_part[0][lt][h] = p;  // only this wavefront reads its own tokens' slots
   }
 
-  // ---- o = sum_t p_t V_t over the wavefront's 64 tokens, all loads at once
-  const int sub = lane / LPT, cl = lane - sub * LPT;
-  const int last = a.len - 1;
-  const KT *vbase = static_cast<const KT *>(a.v) + static_cast<size_t>(bg) * a.T_cap * D + cl * EPL;
+  // ---- o = sum_t p_t V_t over the wavefront's 64 tokens (the victim slot: the new V)
   float o[G][EPL];
 #pragma unroll
   for (int h = 0; h < G; ++h)
 #pragma unroll
     for (int e = 0; e < EPL; ++e) o[h][e] = 0.0f;
-  {
-    constexpr int NL = 64 / TPI;
-    uint4 vr[NL];
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {  // rows past the last token re-read it (their p is 0)
-      const int t = min(t0 + 64 * w + i * TPI + sub, last);
-      vr[i] = load16(vbase + static_cast<size_t>(t) * D);
-    }
+  for (int i = 0; i < NL; ++i) {
+    float vv[EPL];
+    Vec<KT>::unpack(vr[i], vv);
+    if constexpr (H2O) {
+      if (owner && min(t0 + 64 * w + i * TPI + sub, last) == victim) {
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      float vv[EPL];
-      Vec<KT>::unpack(vr[i], vv);
-      const int r = 64 * w + i * TPI + sub;
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float p = s_part[0][r][h];
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) o[h][e] = fmaf(p, vv[e], o[h][e]);
+        for (int e = 0; e < EPL; ++e) vv[e] = s_vnew[cl * EPL + e];
       }
+    }
+    const int r = 64 * w + i * TPI + sub;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float p = s_part[0][r][h];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[h][e] = fmaf(p, vv[e], o[h][e]);
     }
   }
 #pragma unroll
@@ -791,7 +867,7 @@ __global__ __launch_bounds__(256) void decode_short_kernel(DecodeArgs a) {
     }
   }
   __syncthreads();
-  for (int e = tid; e < G * D; e += 256) {
+  for (int e = tid; e < G * D; e += NT) {
     const int h = e / D, dd = e - h * D;
     float M = -INFINITY;
 #pragma unroll
@@ -811,26 +887,56 @@ __global__ __launch_bounds__(256) void decode_short_kernel(DecodeArgs a) {
     }
     publish(part + 2 + dd, O);
   }
+  if constexpr (H2O) {
+    // the new token into the victim slot: this workgroup's reads of the slot are consumed
+    if (owner && tid < D) {
+      if (tid < a.d_store)
+        static_cast<KT *>(a.kp_w)[(static_cast<size_t>(bg) * a.d_store + tid) * a.T_cap +
+                                  victim] = store_elem<KT>(s_knew[tid]);
+      static_cast<KT *>(a.v_w)[(slot0 + victim) * D + tid] =
+          static_cast<const KT *>(a.v_new)[static_cast<size_t>(bg) * D + tid];
+    }
+  }
 
-  // ---- the last workgroup of this (b, g) merges all chunks
-  __builtin_amdgcn_s_waitcnt(0);  // this thread's partials and scores have landed
+  // ---- the last workgroup of this (b, g) merges all chunks (and updates the masses)
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's partials, scores and cache writes have landed
   __syncthreads();
   if (tid == 0) s_last = (atomicAdd(&a.counters[bg], 1u) == static_cast<unsigned>(a.S - 1));
   __syncthreads();
   if (!s_last) return;
-  merge_splits<D, G, 256>(a, head0, bg, s_M, s_L);
+  if (H2O && victim >= 0 && tid == 0) hh.slot_pos[slot0 + victim] = hh.t_new;
+  merge_splits<D, G, NT>(a, head0, bg, s_M, s_L, victim);
 }
 
-template <typename KT, int D>
-hipError_t launch_short(const DecodeArgs &a, hipStream_t s) {
+template <typename KT, int D, int G>
+__global__ __launch_bounds__(256) void decode_short_kernel(DecodeArgs a) {
+  short_attend<KT, D, G, false>(a, H2OArgs{});
+}
+
+// The H2O form holds P in LDS (one workgroup per CU), so each wavefront may take a whole SIMD's
+// registers: its K' loads, P's and the victim's then all stay in flight together.
+template <typename KT, int D, int G>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void h2o_step_kernel(DecodeArgs a, H2OArgs hh) {
+  short_attend<KT, D, G, true>(a, hh);
+}
+
+template <typename KT, int D, int G, bool H2O>
+hipError_t launch_short_g(const DecodeArgs &a, const H2OArgs &h, hipStream_t s) {
   const dim3 grid(a.B * a.Hkv * a.S), block(256);
-  switch (a.Hq / a.Hkv) {
-    case 1: decode_short_kernel<KT, D, 1><<<grid, block, 0, s>>>(a); break;
-    case 2: decode_short_kernel<KT, D, 2><<<grid, block, 0, s>>>(a); break;
-    case 4: decode_short_kernel<KT, D, 4><<<grid, block, 0, s>>>(a); break;
-    default: decode_short_kernel<KT, D, 8><<<grid, block, 0, s>>>(a); break;
-  }
+  if constexpr (H2O) h2o_step_kernel<KT, D, G><<<grid, block, 0, s>>>(a, h);
+  else decode_short_kernel<KT, D, G><<<grid, block, 0, s>>>(a);
   return hipGetLastError();
+}
+
+template <typename KT, int D, bool H2O>
+hipError_t launch_short(const DecodeArgs &a, const H2OArgs &h, hipStream_t s) {
+  switch (a.Hq / a.Hkv) {
+    case 1: return launch_short_g<KT, D, 1, H2O>(a, h, s);
+    case 2: return launch_short_g<KT, D, 2, H2O>(a, h, s);
+    case 4: return launch_short_g<KT, D, 4, H2O>(a, h, s);
+    default: return launch_short_g<KT, D, 8, H2O>(a, h, s);
+  }
 }
 
 template <typename KT, int D, int G, bool FUSED>
@@ -902,9 +1008,12 @@ void decode_workspace_carve(void *ws, int dtype, int B, int Hq, int Hkv, int d, 
 
 hipError_t launch_decode(int dtype, const DecodeArgs &a, hipStream_t s) {
   if (decode_short(a.len)) {
+    const H2OArgs none{};
     if (dtype == 1)
-      return a.d == 128 ? launch_short<bf16_t, 128>(a, s) : launch_short<bf16_t, 64>(a, s);
-    return a.d == 128 ? launch_short<float, 128>(a, s) : launch_short<float, 64>(a, s);
+      return a.d == 128 ? launch_short<bf16_t, 128, false>(a, none, s)
+                        : launch_short<bf16_t, 64, false>(a, none, s);
+    return a.d == 128 ? launch_short<float, 128, false>(a, none, s)
+                      : launch_short<float, 64, false>(a, none, s);
   }
   if (dtype == 1)
     return a.d == 128 ? launch_d<bf16_t, 128, false>(a, s) : launch_d<bf16_t, 64, false>(a, s);
@@ -915,6 +1024,14 @@ hipError_t launch_decode_step(int dtype, const DecodeArgs &a, hipStream_t s) {
   if (dtype == 1)
     return a.d == 128 ? launch_d<bf16_t, 128, true>(a, s) : launch_d<bf16_t, 64, true>(a, s);
   return a.d == 128 ? launch_d<float, 128, true>(a, s) : launch_d<float, 64, true>(a, s);
+}
+
+hipError_t launch_h2o_step(int dtype, const DecodeArgs &a, const H2OArgs &h, hipStream_t s) {
+  if (dtype == 1)
+    return a.d == 128 ? launch_short<bf16_t, 128, true>(a, h, s)
+                      : launch_short<bf16_t, 64, true>(a, h, s);
+  return a.d == 128 ? launch_short<float, 128, true>(a, h, s)
+                    : launch_short<float, 64, true>(a, h, s);
 }
 
 }  // namespace aqua

@@ -1,7 +1,8 @@
 """H2O decoding over a compact AQUA-Memory cache (AQUA combined with H2O heavy-hitter eviction:
 abstract of arXiv 2509.11155; edgentiq blog, "Key Advantages").
 
-Each (b, g) keeps ``heavy + recent`` slots.  A step is four libaqua calls on one stream:
+Each (b, g) keeps ``heavy + recent`` slots.  A step is four libaqua calls on one stream (or the
+single launch ``aqua_h2o_step``, which computes the same thing):
 
 1. ``aqua_h2o_victim``: evict the non-recent slot ranked lowest by (mass desc, position asc) and
    claim it for the new position (its mass restarts at 0);
@@ -70,12 +71,19 @@ class H2OCache:
         return self.ws
 
     def step(self, q, k_new, v_new, P, t_new: int, d_sel: int, k: int, scale: float, out,
-             q_proj, mask, stream=None):
+             q_proj, mask, stream=None, fused: bool = False):
         """One decode step for the token at position ``t_new``.
         q ``[B][Hq][d]``, k_new/v_new ``[B][Hkv][d]`` (raw, the cache's dtype); out ``[B][Hq][d]``
-        fp32; q_proj ``[B][Hq][d]`` fp32 and mask ``[B][Hq][d/32]`` int32 are written."""
+        fp32; q_proj ``[B][Hq][d]`` fp32 and mask ``[B][Hq][d/32]`` int32 are written.
+        ``fused`` runs the step as the single launch ``aqua_h2o_step`` (the same results, bit for
+        bit, as the four calls below)."""
         Hq = q.shape[1]
         ws = self.workspace(Hq)
+        if fused:
+            A.aqua_h2o_step(self.cache, Hq, q, k_new, v_new, P, d_sel, k, scale, self.mass,
+                            self.slot_pos, t_new, self.recent, self.victim, out, ws,
+                            q_proj_out=q_proj, mask_out=mask, stream=stream)
+            return
         A.aqua_h2o_victim(self.mass, self.slot_pos, t_new, self.recent, self.victim, stream)
         A.aqua_project_keys(self.cache, k_new, v_new, P, 1, slots=self.victim, stream=stream)
         A.aqua_select_dims(q, P, d_sel, k, q_proj, mask, stream=stream)

@@ -30,7 +30,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 10
+    assert len(names) == 11
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(aq.EXPORTS)

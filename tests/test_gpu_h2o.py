@@ -164,3 +164,35 @@ def test_h2o_llama8b_t32768_64_steps():
     """The heavy-hitter workload: 32768-token context, 1024 heavy + 256 recent slots, AQUA-Memory
     (96 stored dims, top-64 of them), 64 steps."""
     _run(config(5))
+
+
+@pytest.mark.parametrize("over", [
+    dict(T=320, heavy=40, recent=24, steps=48, dtype="f32"),   # every step evicts
+    dict(Hq=16, Hkv=2, T=700, heavy=96, recent=32, steps=40),  # G = 8
+    dict(Hq=8, Hkv=8, T=900, heavy=200, recent=56, steps=24),  # G = 1, 256 slots: one chunk
+    dict(steps=16),                                            # the 32768-token workload
+])
+def test_h2o_fused_step_equals_separate_calls(over):
+    """aqua_h2o_step against the four calls (victim, slot append, selection, mass-mode decode)
+    from two copies of the same state: every output and every piece of state equal, bit for
+    bit, after every step (the separate calls are checked against the oracle above)."""
+    c = config(5, **over)
+    inp = make_h2o_inputs(c)
+    st, _, _, _, P, _ = _seed(inp, c)
+    st2 = H2OCache(st.kp.clone(), st.v.clone(), st.slot_pos.clone(), st.mass.clone(), st.heavy,
+                   st.recent)
+    B, Hq, d = c["B"], c["Hq"], c["d"]
+    bufs = [(torch.empty(B, Hq, d, device=DEV), torch.empty(B, Hq, d, device=DEV),
+             torch.empty(B, Hq, d // 32, dtype=torch.int32, device=DEV)) for _ in range(2)]
+    scale = 1 / math.sqrt(d)
+    for s in range(c["steps"]):
+        args = (inp["q_steps"][s].to(DEV), inp["k_steps"][s].to(DEV), inp["v_steps"][s].to(DEV),
+                P, c["T"] + s, c["d_sel"], c["k"], scale)
+        st.step(*args, *bufs[0])
+        st2.step(*args, *bufs[1], fused=True)
+        torch.cuda.synchronize()
+        for name, x, y in (("out", bufs[0][0], bufs[1][0]), ("q'", bufs[0][1], bufs[1][1]),
+                           ("mask", bufs[0][2], bufs[1][2]), ("victim", st.victim, st2.victim),
+                           ("slot_pos", st.slot_pos, st2.slot_pos), ("mass", st.mass, st2.mass),
+                           ("K'", st.kp, st2.kp), ("V", st.v, st2.v)):
+            assert torch.equal(x, y), f"step {s}: {name} differs"
