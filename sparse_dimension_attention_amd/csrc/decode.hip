@@ -173,6 +173,16 @@ __device__ void merge_splits(const DecodeArgs &a, size_t head0, int bg, float *s
   if (threadIdx.x == 0) atomicExch(&a.counters[bg], 0u);
 }
 
+// A workgroup barrier that orders LDS traffic only: unlike __syncthreads, whose fence waits
+// for every outstanding global load too, it lets loads issued earlier stay in flight.  The
+// empty asm statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt left at their maxima
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Fused prologue shared by the fused decode step and the fused H2O step: stage P in LDS, project
 // the group's G query rows and, when with_key, the new token's key (q'_h[i] = sum_j q_h[j] P[j][i]
 // in fp32, j ascending: the arithmetic of select_kernel and of the key projection, so the results
@@ -180,7 +190,8 @@ __device__ void merge_splits(const DecodeArgs &a, size_t head0, int bg, float *s
 // LDS, and select every head's top-k dims into mask words.  split0 writes q_proj_out / mask_out.
 // LDS: sP [D][D], sq [G+1][D], s_qp [G+1][D], s_mw [G][D/32], s_knew and s_vnew [D].
 // after_staging() runs once P and the rows are on their way to LDS (the caller issues its own
-// loads there).  Ends with a workgroup barrier.
+// loads there; the barriers here order LDS only, so those loads stay in flight).  Ends with a
+// workgroup barrier.
 template <typename KT, int D, int G, int NT, typename F>
 __device__ __forceinline__ void fused_project_select(const DecodeArgs &a, size_t head0, int bg,
                                                      bool with_key, bool split0, float *sP,
@@ -219,7 +230,7 @@ __device__ __forceinline__ void fused_project_select(const DecodeArgs &a, size_t
     s_vnew[tid] = vn;
   }
   after_staging();  // the caller's loads go out while the projection runs
-  __syncthreads();
+  lds_barrier();
   // q'_h[i] = sum_j q_h[j] P[j][i] (fp32, j ascending); thread -> dim i, rows r0, r0+NT/D, ...
   // The j loop is fully unrolled and branch-free (rows past the last are computed on a
   // clamped row and discarded), so the LDS reads of later j are issued ahead of the fmas.
@@ -253,7 +264,7 @@ __device__ __forceinline__ void fused_project_select(const DecodeArgs &a, size_t
     for (int r = 0; r < RPT; ++r)
       if (r0 + r * RSTEP < nrows) s_qp[r0 + r * RSTEP][i] = acc[r];
   }
-  __syncthreads();
+  lds_barrier();
   if (with_key && tid < D) {
     // the new token's K' as it will be stored (rounded once); the caller writes it to the cache
     // only after its own reads of that column are done
@@ -281,7 +292,7 @@ __device__ __forceinline__ void fused_project_select(const DecodeArgs &a, size_t
       for (int e = 0; e < E; ++e) a.q_proj_out[(head0 + h) * D + lane + 64 * e] = x[e];
     }
   }
-  __syncthreads();
+  lds_barrier();
 }
 
 // Two workgroups share each CU, and the issue arbiter favours older wavefronts: left alone, the
