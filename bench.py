@@ -21,7 +21,10 @@ Two further workloads are measured beside the headline and reported in the same 
  * h2o: 64 heavy-hitter decode steps over a compact AQUA-Memory cache of 1024 heavy + 256
    recent slots (32768-token context, 96 stored dims, top-64), each step = eviction, slot
    append, selection and mass-mode decode; timed from a Python loop and as a replayed HIP graph
-   of the 64 steps (launch-bound: about 4.6 MB per step, cache-resident).
+   of the 64 steps (launch-bound: about 4.6 MB per step, cache-resident);
+ * long_decode: decode over a 131072-token context (B=1) at k = 128, 96, 64, 32 (GB/s and the
+   speedup over k=128), and the same step over shorter prefixes of that context (T = 256 ..
+   131072), where the gain of fewer kept dims over k=128 sets in.
 """
 from __future__ import annotations
 
@@ -206,6 +209,96 @@ def bench_prefill(dev, reps: int):
                       "pass"}
 
 
+def bench_long_decode(dev, steps: int, warmup: int):
+    """Decode over a long context (B=1, 32 query heads, 8 KV heads, T=131072 bf16) at each k of
+    {128, 96, 64, 32}, and the same step over shorter prefixes of that context (T from 256 up),
+    to locate the context length past which fewer kept dims pay off.
+
+    Per (T, k): the whole step as one launch (aqua_decode_step: new key appended, 32 queries
+    projected and selected, split-T attention) and the decode kernel alone (aqua_decode on the
+    step's masks), each between HIP events on its stream (median of K launches).
+    Algorithmic bytes of the kernel: the K' rows of each group's mask union and all of V over T
+    tokens, q' and masks in, fp32 out."""
+    c = config(3)
+    B, Hq, Hkv, d, T = c["B"], c["Hq"], c["Hkv"], c["d"], c["T"]
+    G = Hq // Hkv
+    inp = make_decode_inputs(c, workers=16)
+    P = inp["P"].to(dev)
+    T_cap = T + CAP_SLACK
+    kp = torch.empty(B, Hkv, d, T_cap, dtype=torch.bfloat16, device=dev)
+    v = torch.empty(B, Hkv, T_cap, d, dtype=torch.bfloat16, device=dev)
+    cache = aq.make_cache(kp, v, 0)
+    aq.aqua_project_keys(cache, inp["k"].to(dev), inp["v"].to(dev), P, T)
+    q = inp["q"].to(dev)
+    k_new = inp["k"][:, :, T - 1].contiguous().to(dev)
+    v_new = inp["v"][:, :, T - 1].contiguous().to(dev)
+    del inp
+    qp = torch.empty(B * Hq, d, device=dev)
+    mask = torch.empty(B, Hq, d // 32, dtype=torch.int32, device=dev)
+    out = torch.empty(B, Hq, d, device=dev)
+    ws = torch.zeros(aq.aqua_decode_workspace(cache, Hq), dtype=torch.uint8, device=dev)
+    scale = 1.0 / math.sqrt(d)
+    cd = dict(c)
+
+    def measure(Tn: int, k: int):
+        # the step appends token Tn-1 (it overwrites that column with the same token's K', V)
+        def step():
+            cache.len = Tn - 1
+            aq.aqua_decode_step(cache, Hq, q, k_new, v_new, P, d, k, scale, out, ws,
+                                q_proj_out=qp.view(B, Hq, d), mask_out=mask)
+
+        def events(fn):
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(steps)]
+            for e0, e1 in ev:
+                e0.record()
+                fn()
+                e1.record()
+            torch.cuda.synchronize()
+            return statistics.median(a.elapsed_time(b) for a, b in ev) * 1e3
+
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        bare_us = (time.perf_counter() - t0) * 1e6 / steps
+        step_us = events(step)
+        cache.len = Tn
+        k_us = events(lambda: aq.aqua_decode(cache, Hq, qp, mask.view(B * Hq, d // 32), scale,
+                                             out, ws))
+        U = union_rows(mask.cpu().numpy(), B, Hkv, G, d, d)
+        nbytes = decode_bytes(U, cd, Tn)
+        return {"step_us": step_us, "step_us_bare": bare_us, "kernel_us": k_us,
+                "mean_union_rows": float(U.mean()), "bytes": nbytes,
+                "kernel_gbs": nbytes / (k_us * 1e-6) / 1e9}
+
+    ks = (128, 96, 64, 32)
+    long = {k: measure(T, k) for k in ks}
+    base = long[128]
+    for k in ks:
+        long[k]["speedup_step_vs_k128"] = base["step_us"] / long[k]["step_us"]
+        long[k]["speedup_kernel_vs_k128"] = base["kernel_us"] / long[k]["kernel_us"]
+        long[k]["ideal_speedup_vs_k128"] = base["bytes"] / long[k]["bytes"]
+    sweep = {}
+    for Tn in (256, 1024, 4096, 16384, 65536):
+        r = {k: measure(Tn, k) for k in ks}
+        sweep[Tn] = {k: {"step_us": r[k]["step_us"], "kernel_us": r[k]["kernel_us"],
+                         "speedup_step_vs_k128": r[128]["step_us"] / r[k]["step_us"]}
+                     for k in ks}
+    sweep[T] = {k: {"step_us": long[k]["step_us"], "kernel_us": long[k]["kernel_us"],
+                    "speedup_step_vs_k128": long[k]["speedup_step_vs_k128"]} for k in ks}
+    return {"workload": c["name"], "T": T, "T_cap": T_cap, "steps": steps, "warmup": warmup,
+            "by_k": {str(k): long[k] for k in ks},
+            "t_sweep": {str(t): {str(k): x for k, x in r.items()} for t, r in sweep.items()},
+            "timing": "step_us: median over K steps of HIP events around each aqua_decode_step "
+                      "launch on its stream (step_us_bare: K bare calls between two "
+                      "synchronizations, host-bound at short contexts); kernel_us: the same "
+                      "for aqua_decode alone on the step's masks"}
+
+
 def bench_h2o(dev, reps: int):
     """64 heavy-hitter decode steps over a compact AQUA-Memory cache."""
     from sparse_dimension_attention_amd.h2o import H2OCache
@@ -307,7 +400,7 @@ def main():
                     help="run one step implementation only, untimed (for counter runs)")
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the prefill and H2O workloads")
-    ap.add_argument("--secondary-only", choices=("prefill", "h2o"), default=None,
+    ap.add_argument("--secondary-only", choices=("prefill", "h2o", "long"), default=None,
                     help="run only that workload and print its record (for profiler runs)")
     ap.add_argument("--secondary-reps", type=int, default=5)
     args = ap.parse_args()
@@ -326,8 +419,12 @@ def main():
 
     dev = torch.device("cuda:0")
     if args.secondary_only:
-        fn = bench_prefill if args.secondary_only == "prefill" else bench_h2o
-        print(json.dumps({args.secondary_only: fn(dev, args.secondary_reps)}))
+        if args.secondary_only == "long":
+            r = bench_long_decode(dev, min(args.steps, 50), min(args.warmup, 10))
+        else:
+            fn = bench_prefill if args.secondary_only == "prefill" else bench_h2o
+            r = fn(dev, args.secondary_reps)
+        print(json.dumps({args.secondary_only: r}))
         return
     c = config(2)
     B, Hq, Hkv, d, T, k = c["B"], c["Hq"], c["Hkv"], c["d"], c["T"], c["k"]
@@ -444,6 +541,8 @@ def main():
         rec["prefill"] = bench_prefill(dev, args.secondary_reps)
         torch.cuda.empty_cache()
         rec["h2o"] = bench_h2o(dev, args.secondary_reps)
+        torch.cuda.empty_cache()
+        rec["long_decode"] = bench_long_decode(dev, min(args.steps, 50), min(args.warmup, 10))
     if not args.no_cpu:
         rec["cpu_baseline"] = cpu_baseline(c, args.cpu_groups, args.cpu_reps)
     print(json.dumps(rec))

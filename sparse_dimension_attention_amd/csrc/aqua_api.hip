@@ -188,7 +188,6 @@ aqua_status aqua_decode_step(aqua_cache *c, int32_t Hq, const void *q, const voi
   if (ws_bytes < need)
     return fail(AQUA_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, need);
 
-  const aqua::DecodeLayout L = aqua::decode_layout(c->dtype, Hq / c->Hkv);
   aqua::DecodeArgs a{};
   a.kp = c->kp;
   a.v = c->v;
@@ -205,7 +204,7 @@ aqua_status aqua_decode_step(aqua_cache *c, int32_t Hq, const void *q, const voi
   a.d_store = c->d_store;
   a.T_cap = c->T_cap;
   a.len = c->len + 1;
-  a.S = (a.len + L.split - 1) / L.split;
+  a.S = aqua::decode_splits(c->dtype, Hq / c->Hkv, a.len);
   a.qscale = scale * 1.4426950408889634f;
   a.q_raw = q;
   a.k_new = k_new;

@@ -26,6 +26,8 @@
 // LDS, projects its group's raw queries (and, in the workgroup that holds the new position, the
 // new key), selects every head's top-k dims with wave_topk_threshold, appends the new token's
 // K' and V to the cache, and attends over the cached tokens plus the new one, taken from LDS.
+// Up to the short-context length the fused step runs on the short kernel instead (256-token
+// workgroups, the same prologue), as the fused H2O step does.
 #include <type_traits>
 
 #include "aqua_internal.h"
@@ -118,40 +120,64 @@ __device__ void merge_splits(const DecodeArgs &a, size_t head0, int bg, float *s
     }
   };
   if (mass) load_batch(threadIdx.x);
-  for (int e = threadIdx.x; e < G * D; e += NT) {
-    const int h = e / D, dd = e - h * D;
-    const float *part = a.partials + (head0 + h) * a.S * (D + 2);
-    float ms[CH], M = -INFINITY, O = 0.0f, L = 0.0f;
-    for (int s0 = 0; s0 < a.S; s0 += CH) {  // running (M, L, O) over chunks of CH splits
-      float ls[CH], os[CH];
+  // A thread merges EB of its output elements side by side, CP splits per batch of loads, so
+  // that a long context's many splits take few round trips (S = 64 at 131072 tokens: 4).
+  constexpr int EPT = (G * D + NT - 1) / NT;  // output elements per thread
+  constexpr int EB = EPT < 2 ? EPT : 2;
+  constexpr int CP = 16;
+  for (int e0 = threadIdx.x; e0 < G * D; e0 += EB * NT) {
+    int hh[EB], dd[EB];
+    const float *part[EB];
+    float M[EB], O[EB], L[EB];
 #pragma unroll
-      for (int c = 0; c < CH; ++c) {
-        const int sp = min(s0 + c, a.S - 1);  // past the last split: re-read it, weight 0
-        ms[c] = coherent_load(part + sp * (D + 2));
-        ls[c] = coherent_load(part + sp * (D + 2) + 1);
-        os[c] = coherent_load(part + sp * (D + 2) + 2 + dd);
-      }
-      float Mc = M;
-#pragma unroll
-      for (int c = 0; c < CH; ++c)
-        if (s0 + c < a.S) Mc = fmaxf(Mc, ms[c]);
-      const float rs = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(M - Mc);
-      O *= rs;
-      L *= rs;
-#pragma unroll
-      for (int c = 0; c < CH; ++c) {
-        const float al = (s0 + c >= a.S || ms[c] == -INFINITY)
-                             ? 0.0f
-                             : __builtin_amdgcn_exp2f(ms[c] - Mc);
-        L = fmaf(al, ls[c], L);
-        O = fmaf(al, os[c], O);
-      }
-      M = Mc;
+    for (int j = 0; j < EB; ++j) {
+      const int e = min(e0 + j * NT, G * D - 1);  // past the end: a copy of the last, unstored
+      hh[j] = e / D;
+      dd[j] = e - hh[j] * D;
+      part[j] = a.partials + (head0 + hh[j]) * a.S * (D + 2);
+      M[j] = -INFINITY;
+      O[j] = 0.0f;
+      L[j] = 0.0f;
     }
-    a.out[(head0 + h) * D + dd] = O / L;
-    if (dd == 0) {
-      s_M[h] = M;
-      s_L[h] = L;
+    for (int s0 = 0; s0 < a.S; s0 += CP) {  // running (M, L, O) over chunks of CP splits
+      float ms[EB][CP], ls[EB][CP], os[EB][CP];
+#pragma unroll
+      for (int j = 0; j < EB; ++j)
+#pragma unroll
+        for (int c = 0; c < CP; ++c) {
+          const int sp = min(s0 + c, a.S - 1);  // past the last split: re-read it, weight 0
+          ms[j][c] = coherent_load(part[j] + sp * (D + 2));
+          ls[j][c] = coherent_load(part[j] + sp * (D + 2) + 1);
+          os[j][c] = coherent_load(part[j] + sp * (D + 2) + 2 + dd[j]);
+        }
+#pragma unroll
+      for (int j = 0; j < EB; ++j) {
+        float Mc = M[j];
+#pragma unroll
+        for (int c = 0; c < CP; ++c)
+          if (s0 + c < a.S) Mc = fmaxf(Mc, ms[j][c]);
+        const float rs = (M[j] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(M[j] - Mc);
+        O[j] *= rs;
+        L[j] *= rs;
+#pragma unroll
+        for (int c = 0; c < CP; ++c) {
+          const float al = (s0 + c >= a.S || ms[j][c] == -INFINITY)
+                               ? 0.0f
+                               : __builtin_amdgcn_exp2f(ms[j][c] - Mc);
+          L[j] = fmaf(al, ls[j][c], L[j]);
+          O[j] = fmaf(al, os[j][c], O[j]);
+        }
+        M[j] = Mc;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < EB; ++j) {
+      if (e0 + j * NT >= G * D) break;
+      a.out[(head0 + hh[j]) * D + dd[j]] = O[j] / L[j];
+      if (dd[j] == 0) {
+        s_M[hh[j]] = M[j];
+        s_L[hh[j]] = L[j];
+      }
     }
   }
   if (mass) {
@@ -684,8 +710,14 @@ void decode_kernel(DecodeArgs a) {
 // position and restarts its mass from 0 before adding this step's weights.
 constexpr int kShortChunk = 256;
 
-template <typename KT, int D, int G, bool H2O>
+// plain: aqua_decode.  step: aqua_decode_step at a short length, the H2O form's prologue with
+// the new token going to column len - 1 (in place of a victim) and no slot bookkeeping.
+enum ShortMode { kShortPlain, kShortStep, kShortH2O };
+
+template <typename KT, int D, int G, int MODE>
 __device__ __forceinline__ void short_attend(const DecodeArgs &a, const H2OArgs &hh) {
+  constexpr bool FUSED = MODE != kShortPlain;
+  constexpr bool H2O = MODE == kShortH2O;
   constexpr int NT = 256;
   constexpr int NWORD = D / 32;
   constexpr int TPL = 4;                  // tokens per lane per K' row load
@@ -695,11 +727,11 @@ __device__ __forceinline__ void short_attend(const DecodeArgs &a, const H2OArgs 
   constexpr int RW = D / 4;               // most K' rows a wavefront reads
   constexpr int NL = 64 / TPI;            // V loads per lane
   typedef typename std::conditional<sizeof(KT) == 2, uint2, uint4>::type kvec;
-  __shared__ __align__(16) float sP[H2O ? D * D : 1];
-  __shared__ __align__(16) float sq[H2O ? G + 1 : 1][D];
-  __shared__ float s_qp[H2O ? G + 1 : 1][D];
-  __shared__ uint32_t s_mw[H2O ? G : 1][NWORD];
-  __shared__ float s_knew[H2O ? D : 1], s_vnew[H2O ? D : 1];
+  __shared__ __align__(16) float sP[FUSED ? D * D : 1];
+  __shared__ __align__(16) float sq[FUSED ? G + 1 : 1][D];
+  __shared__ float s_qp[FUSED ? G + 1 : 1][D];
+  __shared__ uint32_t s_mw[FUSED ? G : 1][NWORD];
+  __shared__ float s_knew[FUSED ? D : 1], s_vnew[FUSED ? D : 1];
   __shared__ float s_qw[D][G];                 // head weights of every stored dim (0: unselected)
   __shared__ float s_part[4][kShortChunk][G];  // partial scores; then the probabilities
   __shared__ float s_o[4][G][D];
@@ -728,7 +760,7 @@ __device__ __forceinline__ void short_attend(const DecodeArgs &a, const H2OArgs 
   };
 
   // ---- V of the wavefront's 64 tokens (t0 + 64 w ..).  K' and V loads go out here, or in the
-  // H2O form once the prologue's own loads are on their way (held across those, their registers
+  // fused forms once the prologue's own loads are on their way (held across those, their registers
   // would make the compiler issue P's loads one at a time)
   const int sub = lane / LPT, cl = lane - sub * LPT;
   const int last = a.len - 1;
@@ -741,18 +773,20 @@ __device__ __forceinline__ void short_attend(const DecodeArgs &a, const H2OArgs 
       vr[i] = load16(vbase + static_cast<size_t>(t) * D);
     }
   };
-  if constexpr (!H2O) {
+  if constexpr (!FUSED) {
     load_k();
     load_v();
   }
 
-  int victim = -1;
+  int victim = -1;  // the column the new token goes to
   if constexpr (H2O) {
     victim = h2o_pick_victim(a.mass + slot0, hh.slot_pos + slot0, a.len, hh.t_new - hh.recent);
     if (split == 0 && tid == 0) hh.victim[bg] = victim;
+  } else if constexpr (FUSED) {
+    victim = a.len - 1;
   }
-  const bool owner = H2O && victim >= t0 && victim < t0 + kShortChunk;  // false if victim is -1
-  if constexpr (H2O)
+  const bool owner = FUSED && victim >= t0 && victim < t0 + kShortChunk;  // false if victim is -1
+  if constexpr (FUSED)
     fused_project_select<KT, D, G, NT>(a, head0, bg, owner, split == 0, sP, sq, s_qp, s_mw,
                                        s_knew, s_vnew, [&] {
                                          load_k();
@@ -766,7 +800,7 @@ __device__ __forceinline__ void short_attend(const DecodeArgs &a, const H2OArgs 
     for (int h = 0; h < G; ++h) {
       uint32_t mw;
       float qv;
-      if constexpr (H2O) {
+      if constexpr (FUSED) {
         mw = s_mw[h][wd];
         qv = s_qp[h][tid];
       } else {
@@ -797,7 +831,7 @@ __device__ __forceinline__ void short_attend(const DecodeArgs &a, const H2OArgs 
         kv[2] = __uint_as_float(kr[i].z); kv[3] = __uint_as_float(kr[i].w);
       }
       const int dim = w + 4 * i;
-      if constexpr (H2O) {
+      if constexpr (FUSED) {
 #pragma unroll
         for (int j = 0; j < TPL; ++j)
           if (j == vj) kv[j] = s_knew[dim];
@@ -842,7 +876,7 @@ __device__ __forceinline__ void short_attend(const DecodeArgs &a, const H2OArgs 
   for (int i = 0; i < NL; ++i) {
     float vv[EPL];
     Vec<KT>::unpack(vr[i], vv);
-    if constexpr (H2O) {
+    if constexpr (FUSED) {
       if (owner && min(t0 + 64 * w + i * TPI + sub, last) == victim) {
 #pragma unroll
         for (int e = 0; e < EPL; ++e) vv[e] = s_vnew[cl * EPL + e];
@@ -898,7 +932,7 @@ __device__ __forceinline__ void short_attend(const DecodeArgs &a, const H2OArgs 
     }
     publish(part + 2 + dd, O);
   }
-  if constexpr (H2O) {
+  if constexpr (FUSED) {
     // the new token into the victim slot: this workgroup's reads of the slot are consumed
     if (owner && tid < D) {
       if (tid < a.d_store)
@@ -916,37 +950,44 @@ __device__ __forceinline__ void short_attend(const DecodeArgs &a, const H2OArgs 
   __syncthreads();
   if (!s_last) return;
   if (H2O && victim >= 0 && tid == 0) hh.slot_pos[slot0 + victim] = hh.t_new;
-  merge_splits<D, G, NT>(a, head0, bg, s_M, s_L, victim);
+  merge_splits<D, G, NT>(a, head0, bg, s_M, s_L, H2O ? victim : -1);
 }
 
 template <typename KT, int D, int G>
 __global__ __launch_bounds__(256) void decode_short_kernel(DecodeArgs a) {
-  short_attend<KT, D, G, false>(a, H2OArgs{});
+  short_attend<KT, D, G, kShortPlain>(a, H2OArgs{});
 }
 
-// The H2O form holds P in LDS (one workgroup per CU), so each wavefront may take a whole SIMD's
-// registers: its K' loads, P's and the victim's then all stay in flight together.
+// The fused forms hold P in LDS (one workgroup per CU), so each wavefront may take a whole
+// SIMD's registers: its K' loads, P's and the victim's then all stay in flight together.
+template <typename KT, int D, int G>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void decode_step_short_kernel(DecodeArgs a) {
+  short_attend<KT, D, G, kShortStep>(a, H2OArgs{});
+}
+
 template <typename KT, int D, int G>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void h2o_step_kernel(DecodeArgs a, H2OArgs hh) {
-  short_attend<KT, D, G, true>(a, hh);
+  short_attend<KT, D, G, kShortH2O>(a, hh);
 }
 
-template <typename KT, int D, int G, bool H2O>
+template <typename KT, int D, int G, int MODE>
 hipError_t launch_short_g(const DecodeArgs &a, const H2OArgs &h, hipStream_t s) {
   const dim3 grid(a.B * a.Hkv * a.S), block(256);
-  if constexpr (H2O) h2o_step_kernel<KT, D, G><<<grid, block, 0, s>>>(a, h);
+  if constexpr (MODE == kShortH2O) h2o_step_kernel<KT, D, G><<<grid, block, 0, s>>>(a, h);
+  else if constexpr (MODE == kShortStep) decode_step_short_kernel<KT, D, G><<<grid, block, 0, s>>>(a);
   else decode_short_kernel<KT, D, G><<<grid, block, 0, s>>>(a);
   return hipGetLastError();
 }
 
-template <typename KT, int D, bool H2O>
+template <typename KT, int D, int MODE>
 hipError_t launch_short(const DecodeArgs &a, const H2OArgs &h, hipStream_t s) {
   switch (a.Hq / a.Hkv) {
-    case 1: return launch_short_g<KT, D, 1, H2O>(a, h, s);
-    case 2: return launch_short_g<KT, D, 2, H2O>(a, h, s);
-    case 4: return launch_short_g<KT, D, 4, H2O>(a, h, s);
-    default: return launch_short_g<KT, D, 8, H2O>(a, h, s);
+    case 1: return launch_short_g<KT, D, 1, MODE>(a, h, s);
+    case 2: return launch_short_g<KT, D, 2, MODE>(a, h, s);
+    case 4: return launch_short_g<KT, D, 4, MODE>(a, h, s);
+    default: return launch_short_g<KT, D, 8, MODE>(a, h, s);
   }
 }
 
@@ -1017,32 +1058,32 @@ void decode_workspace_carve(void *ws, int dtype, int B, int Hq, int Hkv, int d, 
   *scores = reinterpret_cast<float *>(p);
 }
 
+template <int MODE>
+hipError_t launch_short_mode(int dtype, const DecodeArgs &a, const H2OArgs &h, hipStream_t s) {
+  if (dtype == 1)
+    return a.d == 128 ? launch_short<bf16_t, 128, MODE>(a, h, s)
+                      : launch_short<bf16_t, 64, MODE>(a, h, s);
+  return a.d == 128 ? launch_short<float, 128, MODE>(a, h, s)
+                    : launch_short<float, 64, MODE>(a, h, s);
+}
+
 hipError_t launch_decode(int dtype, const DecodeArgs &a, hipStream_t s) {
-  if (decode_short(a.len)) {
-    const H2OArgs none{};
-    if (dtype == 1)
-      return a.d == 128 ? launch_short<bf16_t, 128, false>(a, none, s)
-                        : launch_short<bf16_t, 64, false>(a, none, s);
-    return a.d == 128 ? launch_short<float, 128, false>(a, none, s)
-                      : launch_short<float, 64, false>(a, none, s);
-  }
+  if (decode_short(a.len)) return launch_short_mode<kShortPlain>(dtype, a, H2OArgs{}, s);
   if (dtype == 1)
     return a.d == 128 ? launch_d<bf16_t, 128, false>(a, s) : launch_d<bf16_t, 64, false>(a, s);
   return a.d == 128 ? launch_d<float, 128, false>(a, s) : launch_d<float, 64, false>(a, s);
 }
 
+// a.S must be decode_splits(dtype, G, a.len): the short kernel's chunk count at short lengths
 hipError_t launch_decode_step(int dtype, const DecodeArgs &a, hipStream_t s) {
+  if (decode_short(a.len)) return launch_short_mode<kShortStep>(dtype, a, H2OArgs{}, s);
   if (dtype == 1)
     return a.d == 128 ? launch_d<bf16_t, 128, true>(a, s) : launch_d<bf16_t, 64, true>(a, s);
   return a.d == 128 ? launch_d<float, 128, true>(a, s) : launch_d<float, 64, true>(a, s);
 }
 
 hipError_t launch_h2o_step(int dtype, const DecodeArgs &a, const H2OArgs &h, hipStream_t s) {
-  if (dtype == 1)
-    return a.d == 128 ? launch_short<bf16_t, 128, true>(a, h, s)
-                      : launch_short<bf16_t, 64, true>(a, h, s);
-  return a.d == 128 ? launch_short<float, 128, true>(a, h, s)
-                    : launch_short<float, 64, true>(a, h, s);
+  return launch_short_mode<kShortH2O>(dtype, a, h, s);
 }
 
 }  // namespace aqua

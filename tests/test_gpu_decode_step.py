@@ -66,10 +66,12 @@ def test_step_matches_oracle(B, Hq, Hkv, T, k, d, dtype):
     assert np.array_equal(storage_to_f64(r["v"])[:, :, T - 1], storage_to_f64(inp["v"][:, :, T - 1]))
 
 
-def test_step_equals_separate_calls():
+@pytest.mark.parametrize("T", [5000, 4096, 1500])
+def test_step_equals_separate_calls(T):
     """q', masks and the cache are bit-identical to project + select + decode; outputs agree to
-    fp32 summation order."""
-    c = config(2, B=4, Hq=32, Hkv=8, T=5000)
+    fp32 summation order (split-T kernel, T > 4096), or bit for bit (short kernel: the new token
+    takes its place in the same sums)."""
+    c = config(2, B=4, Hq=32, Hkv=8, T=T)
     inp = make_decode_inputs(c)
     T, d, k, B, Hq = c["T"], c["d"], c["k"], c["B"], c["Hq"]
     r = _step(inp, c, T)
@@ -88,23 +90,28 @@ def test_step_equals_separate_calls():
     assert torch.equal(mask.reshape(B, Hq, d // 32), r["mask"])
     assert torch.equal(kp[..., :T], r["kp"][..., :T])
     assert torch.equal(v[:, :, :T], r["v"][:, :, :T])
-    assert torch.allclose(out, r["out"], rtol=1e-5, atol=1e-7)
+    if T <= 4096:
+        assert torch.equal(out, r["out"])
+    else:
+        assert torch.allclose(out, r["out"], rtol=1e-5, atol=1e-7)
 
 
-def test_step_sequence_appends():
-    """Several steps in a row on one cache and workspace: each appends and attends correctly."""
-    c = config(2, B=2, Hq=8, Hkv=2, T=2600)
+@pytest.mark.parametrize("T0", [2045, 4093])
+def test_step_sequence_appends(T0):
+    """Several steps in a row on one cache and workspace: each appends and attends correctly
+    (across a 256-token chunk and 2048-token split boundary, and across the switch from the
+    short kernel to the split-T kernel after 4096 tokens)."""
+    c = config(2, B=2, Hq=8, Hkv=2, T=T0 + 8)
     inp = make_decode_inputs(c)
     B, Hq, d, k = c["B"], c["Hq"], c["d"], c["k"]
-    T0 = 2045
-    kp, v = new_cache(B, c["Hkv"], d, d, 2624, "bf16")
+    kp, v = new_cache(B, c["Hkv"], d, d, (T0 + 8 + 63) // 64 * 64, "bf16")
     cache = aq.make_cache(kp, v, 0)
     P = inp["P"].to(DEV)
     aq.aqua_project_keys(cache, inp["k"][:, :, :T0].contiguous().to(DEV),
                          inp["v"][:, :, :T0].contiguous().to(DEV), P, T0)
     ws = torch.zeros(aq.aqua_decode_workspace(cache, Hq), dtype=torch.uint8, device=DEV)
     q = inp["q"].to(DEV)
-    for t in range(T0, T0 + 6):  # crosses the 2048-token split boundary
+    for t in range(T0, T0 + 6):
         out = torch.full((B, Hq, d), float("nan"), device=DEV)
         mask = torch.empty(B, Hq, d // 32, dtype=torch.int32, device=DEV)
         aq.aqua_decode_step(cache, Hq, q, inp["k"][:, :, t].contiguous().to(DEV),
@@ -135,3 +142,20 @@ def test_step_mass_mode():
             add += p
         got = mass[0, g].cpu().double().numpy()
         assert np.max(np.abs(got - add)) <= 1e-3 * add.max()
+
+
+@pytest.mark.parametrize("k", [96, 32])
+def test_step_long_context_sampled(k):
+    """B=1, T=131072 (64 splits per KV group; the new token lands in the last one), with a spare
+    capacity of 256 tokens; every mask checked, sampled heads against the oracle."""
+    c = config(3, k=k)
+    T, d = c["T"], c["d"]
+    inp = make_decode_inputs(c, workers=8)
+    r = _step(inp, c, T, T_cap=T + 256)
+    m = unpack_mask(r["mask"], d)
+    assert np.array_equal(m, O.select(r["qp"].cpu().double().numpy(), d, k))
+    heads = [(0, 0), (0, 13), (0, 31)]
+    ref = oracle_decode(inp, c, m, heads=heads)
+    got = r["out"].cpu().double().numpy()
+    for b, h in heads:
+        assert_close(got[b, h], ref[b, h], "bf16", f"k={k} head {h}")
