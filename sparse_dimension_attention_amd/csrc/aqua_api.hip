@@ -149,8 +149,7 @@ aqua_status aqua_decode(const aqua_cache *c, int32_t Hq, const float *q_proj,
   a.mask = mask;
   a.mass = mass;
   a.out = out;
-  aqua::decode_workspace_carve(ws, c->dtype, c->B, Hq, c->Hkv, c->d_head, c->T_cap,
-                               &a.counters, &a.partials, &a.scores);
+  aqua::decode_workspace_carve(ws, c->dtype, c->B, Hq, c->Hkv, c->d_head, c->T_cap, a);
   a.B = c->B;
   a.Hq = Hq;
   a.Hkv = c->Hkv;
@@ -195,8 +194,7 @@ aqua_status aqua_decode_step(aqua_cache *c, int32_t Hq, const void *q, const voi
   a.v_w = c->v;
   a.mass = mass;
   a.out = out;
-  aqua::decode_workspace_carve(ws, c->dtype, c->B, Hq, c->Hkv, c->d_head, c->T_cap,
-                               &a.counters, &a.partials, &a.scores);
+  aqua::decode_workspace_carve(ws, c->dtype, c->B, Hq, c->Hkv, c->d_head, c->T_cap, a);
   a.B = c->B;
   a.Hq = Hq;
   a.Hkv = c->Hkv;
@@ -312,8 +310,7 @@ aqua_status aqua_h2o_step(aqua_cache *c, int32_t Hq, const void *q, const void *
   a.v_w = c->v;
   a.mass = mass;
   a.out = out;
-  aqua::decode_workspace_carve(ws, c->dtype, c->B, Hq, c->Hkv, c->d_head, c->T_cap,
-                               &a.counters, &a.partials, &a.scores);
+  aqua::decode_workspace_carve(ws, c->dtype, c->B, Hq, c->Hkv, c->d_head, c->T_cap, a);
   a.B = c->B;
   a.Hq = Hq;
   a.Hkv = c->Hkv;

@@ -176,6 +176,8 @@ struct DecodeArgs {
   float *mass;           // [B][Hkv][T_cap] or nullptr
   float *out;            // [B][Hq][d]
   uint32_t *counters;    // [B*Hkv], zero between calls
+  uint32_t *run_counters;  // [B*Hkv][run_stride]: per run of splits (two-level merge), zero
+  int run_stride;
   float *partials;       // [B][Hq][S][d+2]  (m, l, o[d]) in log2 units
   float *scores;         // [B][Hq][T_cap]   log2-domain scores (mass mode only)
   int B, Hq, Hkv, d, d_store, T_cap, len;
@@ -215,7 +217,7 @@ bool decode_short(int len);
 int decode_splits(int dtype, int G, int len);  // partials per head that aqua_decode writes
 size_t decode_workspace_bytes(int dtype, int B, int Hq, int Hkv, int d, int T_cap);
 void decode_workspace_carve(void *ws, int dtype, int B, int Hq, int Hkv, int d, int T_cap,
-                            uint32_t **counters, float **partials, float **scores);
+                            DecodeArgs &a);
 
 hipError_t launch_select(const void *q, int qdt, int N, int d, const float *P, int d_sel, int k,
                          float *q_proj, uint32_t *mask, int16_t *idx, hipStream_t s);

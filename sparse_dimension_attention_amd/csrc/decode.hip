@@ -96,15 +96,108 @@ struct DecodeSmem {
   static constexpr int BYTES = OFF_ML + 2 * G * 4 + 16;
 };
 
-// The last workgroup of a (b, g): merge the S partials (m, l, o) of every head into the output
-// and, in mass mode, add every token's normalised probability (summed over the group's heads)
-// to its mass (slot `restart`, if any, starts again from 0).  The partials and scores were
-// written by other workgroups, possibly on other XCDs, so they are read past the non-coherent
-// caches; each thread issues up to 8 such loads at once, so that the merge costs a few memory
-// round trips rather than one per split.
+// Merging split partials (m, l, o), written by other workgroups, possibly on other XCDs, so read
+// past the non-coherent caches.  merge_partials combines `count` partials of each of the group's
+// heads, at split slots first, first + stride, ...: a thread merges EB of its output elements
+// side by side, CP splits per batch of loads, so that a merge costs a few memory round trips
+// rather than one per split.  dst < 0: the result goes to the output (and its (M, L) to s_M,
+// s_L); dst >= 0: it is stored back as a partial in slot dst (an intermediate level; slot dst may
+// be one of those read, so every read is done before the first store).
+template <int D, int G, int NT>
+__device__ void merge_partials(const DecodeArgs &a, size_t head0, int first, int count,
+                               int stride, int dst, float *s_M, float *s_L) {
+  constexpr int EPT = (G * D + NT - 1) / NT;  // output elements per thread
+  constexpr int EB = EPT < 2 ? EPT : 2;
+  constexpr int NIT = (EPT + EB - 1) / EB;
+  constexpr int CP = 16;
+  float rM[NIT][EB], rL[NIT][EB], rO[NIT][EB];
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int e0 = threadIdx.x + it * EB * NT;
+    int dd[EB];
+    const float *part[EB];
+    float M[EB], O[EB], L[EB];
+#pragma unroll
+    for (int j = 0; j < EB; ++j) {
+      const int e = min(e0 + j * NT, G * D - 1);  // past the end: a copy of the last, unstored
+      const int h = e / D;
+      dd[j] = e - h * D;
+      part[j] = a.partials + (head0 + h) * a.S * (D + 2);
+      M[j] = -INFINITY;
+      O[j] = 0.0f;
+      L[j] = 0.0f;
+    }
+    for (int c0 = 0; c0 < count; c0 += CP) {  // running (M, L, O) over batches of CP partials
+      float ms[EB][CP], ls[EB][CP], os[EB][CP];
+#pragma unroll
+      for (int j = 0; j < EB; ++j)
+#pragma unroll
+        for (int c = 0; c < CP; ++c) {
+          // past the last partial: re-read it, weight 0
+          const int sp = first + min(c0 + c, count - 1) * stride;
+          ms[j][c] = coherent_load(part[j] + sp * (D + 2));
+          ls[j][c] = coherent_load(part[j] + sp * (D + 2) + 1);
+          os[j][c] = coherent_load(part[j] + sp * (D + 2) + 2 + dd[j]);
+        }
+#pragma unroll
+      for (int j = 0; j < EB; ++j) {
+        float Mc = M[j];
+#pragma unroll
+        for (int c = 0; c < CP; ++c)
+          if (c0 + c < count) Mc = fmaxf(Mc, ms[j][c]);
+        const float rs = (M[j] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(M[j] - Mc);
+        O[j] *= rs;
+        L[j] *= rs;
+#pragma unroll
+        for (int c = 0; c < CP; ++c) {
+          const float al = (c0 + c >= count || ms[j][c] == -INFINITY)
+                               ? 0.0f
+                               : __builtin_amdgcn_exp2f(ms[j][c] - Mc);
+          L[j] = fmaf(al, ls[j][c], L[j]);
+          O[j] = fmaf(al, os[j][c], O[j]);
+        }
+        M[j] = Mc;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < EB; ++j) {
+      rM[it][j] = M[j];
+      rL[it][j] = L[j];
+      rO[it][j] = O[j];
+    }
+  }
+  if (dst >= 0) __syncthreads();  // every read of the slots is done (dst is uniform)
+#pragma unroll
+  for (int it = 0; it < NIT; ++it)
+#pragma unroll
+    for (int j = 0; j < EB; ++j) {
+      const int e = threadIdx.x + it * EB * NT + j * NT;
+      if (e >= G * D) continue;
+      const int h = e / D, dd = e - h * D;
+      if (dst < 0) {
+        a.out[(head0 + h) * D + dd] = rO[it][j] / rL[it][j];
+        if (dd == 0) {
+          s_M[h] = rM[it][j];
+          s_L[h] = rL[it][j];
+        }
+      } else {
+        float *part = a.partials + ((head0 + h) * a.S + dst) * (D + 2);
+        if (dd == 0) {
+          publish(part + 0, rM[it][j]);
+          publish(part + 1, rL[it][j]);
+        }
+        publish(part + 2 + dd, rO[it][j]);
+      }
+    }
+}
+
+// The last workgroup of a (b, g): merge the group's partials (count of them, at slots 0,
+// stride, 2 stride, ...) into the output and, in mass mode, add every token's normalised
+// probability (summed over the group's heads) to its mass (slot `restart`, if any, starts again
+// from 0); then reset the group's counter.
 template <int D, int G, int NT>
 __device__ void merge_splits(const DecodeArgs &a, size_t head0, int bg, float *s_M, float *s_L,
-                             int restart = -1) {
+                             int restart, int count, int stride) {
   constexpr int CH = 8;
   // mass mode: the first batch of scores and masses is loaded before the partials, so that the
   // two sets of round trips overlap
@@ -120,66 +213,7 @@ __device__ void merge_splits(const DecodeArgs &a, size_t head0, int bg, float *s
     }
   };
   if (mass) load_batch(threadIdx.x);
-  // A thread merges EB of its output elements side by side, CP splits per batch of loads, so
-  // that a long context's many splits take few round trips (S = 64 at 131072 tokens: 4).
-  constexpr int EPT = (G * D + NT - 1) / NT;  // output elements per thread
-  constexpr int EB = EPT < 2 ? EPT : 2;
-  constexpr int CP = 16;
-  for (int e0 = threadIdx.x; e0 < G * D; e0 += EB * NT) {
-    int hh[EB], dd[EB];
-    const float *part[EB];
-    float M[EB], O[EB], L[EB];
-#pragma unroll
-    for (int j = 0; j < EB; ++j) {
-      const int e = min(e0 + j * NT, G * D - 1);  // past the end: a copy of the last, unstored
-      hh[j] = e / D;
-      dd[j] = e - hh[j] * D;
-      part[j] = a.partials + (head0 + hh[j]) * a.S * (D + 2);
-      M[j] = -INFINITY;
-      O[j] = 0.0f;
-      L[j] = 0.0f;
-    }
-    for (int s0 = 0; s0 < a.S; s0 += CP) {  // running (M, L, O) over chunks of CP splits
-      float ms[EB][CP], ls[EB][CP], os[EB][CP];
-#pragma unroll
-      for (int j = 0; j < EB; ++j)
-#pragma unroll
-        for (int c = 0; c < CP; ++c) {
-          const int sp = min(s0 + c, a.S - 1);  // past the last split: re-read it, weight 0
-          ms[j][c] = coherent_load(part[j] + sp * (D + 2));
-          ls[j][c] = coherent_load(part[j] + sp * (D + 2) + 1);
-          os[j][c] = coherent_load(part[j] + sp * (D + 2) + 2 + dd[j]);
-        }
-#pragma unroll
-      for (int j = 0; j < EB; ++j) {
-        float Mc = M[j];
-#pragma unroll
-        for (int c = 0; c < CP; ++c)
-          if (s0 + c < a.S) Mc = fmaxf(Mc, ms[j][c]);
-        const float rs = (M[j] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(M[j] - Mc);
-        O[j] *= rs;
-        L[j] *= rs;
-#pragma unroll
-        for (int c = 0; c < CP; ++c) {
-          const float al = (s0 + c >= a.S || ms[j][c] == -INFINITY)
-                               ? 0.0f
-                               : __builtin_amdgcn_exp2f(ms[j][c] - Mc);
-          L[j] = fmaf(al, ls[j][c], L[j]);
-          O[j] = fmaf(al, os[j][c], O[j]);
-        }
-        M[j] = Mc;
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < EB; ++j) {
-      if (e0 + j * NT >= G * D) break;
-      a.out[(head0 + hh[j]) * D + dd[j]] = O[j] / L[j];
-      if (dd[j] == 0) {
-        s_M[hh[j]] = M[j];
-        s_L[hh[j]] = L[j];
-      }
-    }
-  }
+  merge_partials<D, G, NT>(a, head0, 0, count, stride, -1, s_M, s_L);
   if (mass) {
     __syncthreads();
     for (int t0 = threadIdx.x; t0 < a.len; t0 += NT * CH) {
@@ -197,6 +231,45 @@ __device__ void merge_splits(const DecodeArgs &a, size_t head0, int bg, float *s
     }
   }
   if (threadIdx.x == 0) atomicExch(&a.counters[bg], 0u);
+}
+
+// Past kMergeFan * 2 splits per group the merge takes two levels: the last workgroup of each run
+// of kMergeFan consecutive splits (a counter per run) merges the run into its first slot, and the
+// last of those merges the runs' results.  Both levels are one round of loads, and the first
+// overlaps with the workgroups still streaming.
+constexpr int kMergeFan = 8;
+
+// Ends a split's work once its partials are published: the group's last workgroup merges.
+// Returns in every workgroup; s_last is a workgroup-shared flag.
+template <int D, int G, int NT>
+__device__ __forceinline__ void finish_split(const DecodeArgs &a, size_t head0, int bg,
+                                             int split, int *s_last, float *s_M, float *s_L,
+                                             int restart) {
+  const int tid = threadIdx.x;
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's partials, scores and cache writes have landed
+  __syncthreads();
+  if (a.S > 2 * kMergeFan) {
+    const int run = split / kMergeFan, first = run * kMergeFan;
+    const int cnt = min(kMergeFan, a.S - first);
+    const int nrun = (a.S + kMergeFan - 1) / kMergeFan;
+    uint32_t *rc = a.run_counters + static_cast<size_t>(bg) * a.run_stride + run;
+    if (tid == 0) *s_last = (atomicAdd(rc, 1u) == static_cast<unsigned>(cnt - 1));
+    __syncthreads();
+    if (!*s_last) return;
+    merge_partials<D, G, NT>(a, head0, first, cnt, 1, first, s_M, s_L);
+    if (tid == 0) atomicExch(rc, 0u);
+    __builtin_amdgcn_s_waitcnt(0);  // the run's result has landed
+    __syncthreads();
+    if (tid == 0) *s_last = (atomicAdd(&a.counters[bg], 1u) == static_cast<unsigned>(nrun - 1));
+    __syncthreads();
+    if (!*s_last) return;
+    merge_splits<D, G, NT>(a, head0, bg, s_M, s_L, restart, nrun, kMergeFan);
+    return;
+  }
+  if (tid == 0) *s_last = (atomicAdd(&a.counters[bg], 1u) == static_cast<unsigned>(a.S - 1));
+  __syncthreads();
+  if (!*s_last) return;
+  merge_splits<D, G, NT>(a, head0, bg, s_M, s_L, restart, a.S, 1);
 }
 
 // A workgroup barrier that orders LDS traffic only: unlike __syncthreads, whose fence waits
@@ -420,9 +493,12 @@ void decode_kernel(DecodeArgs a) {
     pos += __popc(uw & ((1u << bit) - 1u));
     // Each workgroup walks the list from its own batch-aligned offset, so that workgroups
     // running at the same time read different K' rows (rows of one group are T_cap apart, and
-    // a lock-step walk would send every workgroup to the same few HBM channels).
+    // a lock-step walk would send every workgroup to the same few HBM channels).  The offset
+    // mixes in the higher bits of the workgroup index: with many splits per group (a long
+    // context at batch 1) workgroups 16 apart would otherwise start on the same batch (measured
+    // at 131072 tokens: 106 us with the plain multiple, 97 us mixed; unchanged at batch 16).
     const int nb = nUp / kUnroll;
-    const int rot = nb ? ((blockIdx.x * 5) % nb) * kUnroll : 0;
+    const int rot = nb ? (((blockIdx.x * 5) ^ (blockIdx.x >> 4)) % nb) * kUnroll : 0;
     if ((uw >> bit) & 1u) {
       const int at = (pos + nUp - rot) % nUp;
       s_dl[at] = tid;
@@ -677,13 +753,7 @@ void decode_kernel(DecodeArgs a) {
   }
 
   // ---- the last workgroup of this (b, g) merges all splits
-  __builtin_amdgcn_s_waitcnt(0);  // this thread's partials and scores have landed
-  __syncthreads();
-  if (tid == 0) s_last = (atomicAdd(&a.counters[bg], 1u) == static_cast<unsigned>(a.S - 1));
-  __syncthreads();
-  if (!s_last) return;
-
-  merge_splits<D, G, NT>(a, head0, bg, s_M, s_L);
+  finish_split<D, G, NT>(a, head0, bg, split, &s_last, s_M, s_L, -1);
 }
 
 // ------------------------------------------------------------------ short contexts
@@ -943,14 +1013,15 @@ __device__ __forceinline__ void short_attend(const DecodeArgs &a, const H2OArgs 
     }
   }
 
-  // ---- the last workgroup of this (b, g) merges all chunks (and updates the masses)
+  // ---- the last workgroup of this (b, g) merges all chunks (and updates the masses); a short
+  // context has at most 16 chunks, one merge level
   __builtin_amdgcn_s_waitcnt(0);  // this thread's partials, scores and cache writes have landed
   __syncthreads();
   if (tid == 0) s_last = (atomicAdd(&a.counters[bg], 1u) == static_cast<unsigned>(a.S - 1));
   __syncthreads();
   if (!s_last) return;
   if (H2O && victim >= 0 && tid == 0) hh.slot_pos[slot0 + victim] = hh.t_new;
-  merge_splits<D, G, NT>(a, head0, bg, s_M, s_L, H2O ? victim : -1);
+  merge_splits<D, G, NT>(a, head0, bg, s_M, s_L, H2O ? victim : -1, a.S, 1);
 }
 
 template <typename KT, int D, int G>
@@ -1040,22 +1111,30 @@ size_t partial_slots(int dtype, int G, int T_cap) {
 }
 }  // namespace
 
+// Workspace: a counter per (b, g), a counter per run of kMergeFan splits of each (b, g), the
+// partials, then the scores (mass mode).
 size_t decode_workspace_bytes(int dtype, int B, int Hq, int Hkv, int d, int T_cap) {
   const size_t S = partial_slots(dtype, Hq / Hkv, T_cap);
+  const size_t runs = (S + kMergeFan - 1) / kMergeFan;
   return align256(static_cast<size_t>(B) * Hkv * 4) +
+         align256(static_cast<size_t>(B) * Hkv * runs * 4) +
          align256(static_cast<size_t>(B) * Hq * S * (d + 2) * 4) +
          static_cast<size_t>(B) * Hq * T_cap * 4;
 }
 
 void decode_workspace_carve(void *ws, int dtype, int B, int Hq, int Hkv, int d, int T_cap,
-                            uint32_t **counters, float **partials, float **scores) {
+                            DecodeArgs &a) {
   const size_t S = partial_slots(dtype, Hq / Hkv, T_cap);
+  const size_t runs = (S + kMergeFan - 1) / kMergeFan;
   char *p = static_cast<char *>(ws);
-  *counters = reinterpret_cast<uint32_t *>(p);
+  a.counters = reinterpret_cast<uint32_t *>(p);
   p += align256(static_cast<size_t>(B) * Hkv * 4);
-  *partials = reinterpret_cast<float *>(p);
+  a.run_counters = reinterpret_cast<uint32_t *>(p);
+  a.run_stride = static_cast<int>(runs);
+  p += align256(static_cast<size_t>(B) * Hkv * runs * 4);
+  a.partials = reinterpret_cast<float *>(p);
   p += align256(static_cast<size_t>(B) * Hq * S * (d + 2) * 4);
-  *scores = reinterpret_cast<float *>(p);
+  a.scores = reinterpret_cast<float *>(p);
 }
 
 template <int MODE>

@@ -43,6 +43,9 @@ def test_tiny_decode_f32():
     (8, 4, 4200, 128, 128),    # G=2, k = d
     (16, 2, 4500, 32, 128),    # G=8
     (4, 1, 4300, 40, 64),      # d = 64
+    # past 16 splits per group the merge takes two levels (runs of 8 splits; the last run ragged)
+    (8, 2, 40000, 96, 128),    # G=4: 20 splits of 2048
+    (16, 2, 20000, 32, 128),   # G=8: 20 splits of 1024
 ])
 def test_decode_bf16_shapes(Hq, Hkv, T, k, d):
     c = config(2, B=2, Hq=Hq, Hkv=Hkv, T=T, k=k, d=d, d_store=d, d_sel=d)
@@ -137,11 +140,13 @@ def test_decode_long_context_sampled(k, long_inputs):
         assert_close(got[b, h], ref[b, h], "bf16", f"k={k} head {h}")
 
 
-def test_decode_mass_accumulation():
-    """Mass mode: mass[t] grows by the sum over the group's heads of the softmax weights."""
-    c = config(2, B=2, Hq=8, Hkv=2, T=3000, d_store=96, d_sel=96, k=64)
+@pytest.mark.parametrize("T", [3000, 40000])
+def test_decode_mass_accumulation(T):
+    """Mass mode: mass[t] grows by the sum over the group's heads of the softmax weights (short
+    kernel at 3000 tokens; split-T kernel with the two-level merge at 40000)."""
+    c = config(2, B=2, Hq=8, Hkv=2, T=T, d_store=96, d_sel=96, k=64)
     inp = make_decode_inputs(c)
-    T_cap = 3008
+    T_cap = (T + 8 + 63) // 64 * 64
     mass0 = torch.rand(c["B"], c["Hkv"], T_cap, device=DEV)
     mass = mass0.clone()
     r = run_decode(inp, c, T_cap=T_cap, mass=mass)
