@@ -24,7 +24,10 @@ Two further workloads are measured beside the headline and reported in the same 
    of the 64 steps (launch-bound: about 4.6 MB per step, cache-resident);
  * long_decode: decode over a 131072-token context (B=1) at k = 128, 96, 64, 32 (GB/s and the
    speedup over k=128), and the same step over shorter prefixes of that context (T = 256 ..
-   131072), where the gain of fewer kept dims over k=128 sets in.
+   131072), where the gain of fewer kept dims over k=128 sets in;
+ * memory_cut: AQUA-Memory's static cut (K' stored on 96 or 64 of 128 dims, top-64 or top-48 of
+   them kept) at both decode shapes: decode kernel time, GB/s, KV bytes, speedup over the full
+   cache.
 """
 from __future__ import annotations
 
@@ -299,6 +302,70 @@ def bench_long_decode(dev, steps: int, warmup: int):
                       "for aqua_decode alone on the step's masks"}
 
 
+def bench_memory_cut(dev, steps: int, warmup: int):
+    """AQUA-Memory's static cut without eviction at the two decode shapes (B=16, T=8192 and B=1,
+    T=131072): only K' dims [0, d_store) are stored, each query keeps its top-k of them, V is
+    stored whole.  Per (d_store, k) in (128, 96), (96, 64), (64, 48): the decode kernel alone
+    (aqua_decode on the selected masks) between HIP events on its stream (median of K launches),
+    its algorithmic bytes (the union's K' rows, all of V, q', masks, output), GB/s, the KV cache
+    bytes per token, and the speedup over the full (128, 96) cache."""
+    cuts = ((128, 96), (96, 64), (64, 48))
+    res = {}
+    for cid in (2, 3):
+        c = config(cid)
+        B, Hq, Hkv, d, T = c["B"], c["Hq"], c["Hkv"], c["d"], c["T"]
+        G = Hq // Hkv
+        inp = make_decode_inputs(c, workers=16)
+        P = inp["P"].to(dev)
+        k_all, v_all = inp["k"].to(dev), inp["v"].to(dev)
+        q = inp["q"].reshape(B * Hq, d).to(dev)
+        del inp
+        T_cap = T + CAP_SLACK
+        scale = 1.0 / math.sqrt(d)
+        rows = {}
+        for d_store, k in cuts:
+            kp = torch.empty(B, Hkv, d_store, T_cap, dtype=torch.bfloat16, device=dev)
+            v = torch.empty(B, Hkv, T_cap, d, dtype=torch.bfloat16, device=dev)
+            cache = aq.make_cache(kp, v, 0)
+            aq.aqua_project_keys(cache, k_all, v_all, P, T)
+            qp = torch.empty(B * Hq, d, device=dev)
+            mask = torch.empty(B * Hq, d // 32, dtype=torch.int32, device=dev)
+            aq.aqua_select_dims(q, P, d_store, k, qp, mask)
+            out = torch.empty(B, Hq, d, device=dev)
+            ws = torch.zeros(aq.aqua_decode_workspace(cache, Hq), dtype=torch.uint8, device=dev)
+            for _ in range(warmup):
+                aq.aqua_decode(cache, Hq, qp, mask, scale, out, ws)
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(steps)]
+            for e0, e1 in ev:
+                e0.record()
+                aq.aqua_decode(cache, Hq, qp, mask, scale, out, ws)
+                e1.record()
+            torch.cuda.synchronize()
+            k_us = statistics.median(a.elapsed_time(b) for a, b in ev) * 1e3
+            cc = dict(c, d_store=d_store)
+            U = union_rows(mask.cpu().numpy().reshape(B, Hq, d // 32), B, Hkv, G, d, d_store)
+            nbytes = decode_bytes(U, cc, T)
+            rows[f"{d_store},{k}"] = {
+                "d_store": d_store, "k": k, "kernel_us": k_us,
+                "mean_union_rows": float(U.mean()), "bytes": nbytes,
+                "kernel_gbs": nbytes / (k_us * 1e-6) / 1e9,
+                "kv_bytes_per_token": B * Hkv * (d_store + d) * 2}
+            del kp, v, cache, ws
+            torch.cuda.empty_cache()
+        base = rows["128,96"]
+        for r in rows.values():
+            r["speedup_vs_full"] = base["kernel_us"] / r["kernel_us"]
+            r["ideal_speedup_vs_full"] = base["bytes"] / r["bytes"]
+            r["kv_memory_vs_full"] = r["kv_bytes_per_token"] / base["kv_bytes_per_token"]
+        res[c["name"]] = rows
+        del k_all, v_all
+        torch.cuda.empty_cache()
+    return {"cuts": res, "steps": steps, "warmup": warmup,
+            "timing": "kernel_us: median over K launches of HIP events around aqua_decode on "
+                      "its stream"}
+
+
 def bench_h2o(dev, reps: int):
     """64 heavy-hitter decode steps over a compact AQUA-Memory cache."""
     from sparse_dimension_attention_amd.h2o import H2OCache
@@ -400,7 +467,8 @@ def main():
                     help="run one step implementation only, untimed (for counter runs)")
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the prefill and H2O workloads")
-    ap.add_argument("--secondary-only", choices=("prefill", "h2o", "long"), default=None,
+    ap.add_argument("--secondary-only", choices=("prefill", "h2o", "long", "memory"),
+                    default=None,
                     help="run only that workload and print its record (for profiler runs)")
     ap.add_argument("--secondary-reps", type=int, default=5)
     args = ap.parse_args()
@@ -421,6 +489,8 @@ def main():
     if args.secondary_only:
         if args.secondary_only == "long":
             r = bench_long_decode(dev, min(args.steps, 50), min(args.warmup, 10))
+        elif args.secondary_only == "memory":
+            r = bench_memory_cut(dev, min(args.steps, 50), min(args.warmup, 10))
         else:
             fn = bench_prefill if args.secondary_only == "prefill" else bench_h2o
             r = fn(dev, args.secondary_reps)
@@ -543,6 +613,8 @@ def main():
         rec["h2o"] = bench_h2o(dev, args.secondary_reps)
         torch.cuda.empty_cache()
         rec["long_decode"] = bench_long_decode(dev, min(args.steps, 50), min(args.warmup, 10))
+        torch.cuda.empty_cache()
+        rec["memory_cut"] = bench_memory_cut(dev, min(args.steps, 50), min(args.warmup, 10))
     if not args.no_cpu:
         rec["cpu_baseline"] = cpu_baseline(c, args.cpu_groups, args.cpu_reps)
     print(json.dumps(rec))

@@ -56,6 +56,26 @@ def test_decode_bf16_shapes(Hq, Hkv, T, k, d):
     assert_close(r["out"].cpu().double().numpy(), ref, "bf16", f"decode {Hq},{Hkv},{T}")
 
 
+@pytest.mark.parametrize("T,d_store,k", [
+    (3000, 96, 64),    # short-context kernel
+    (3000, 64, 48),
+    (9000, 96, 64),    # split-T kernel
+    (9000, 64, 48),
+    (40000, 64, 48),   # two-level merge
+])
+def test_decode_memory_cut(T, d_store, k):
+    """AQUA-Memory's static cut at the decode shape: only K' dims [0, d_store) are stored and each
+    query keeps its top-k of those; V is stored whole."""
+    c = config(2, B=2, Hq=8, Hkv=2, T=T, k=k, d_store=d_store, d_sel=d_store)
+    inp = make_decode_inputs(c)
+    r = run_decode(inp, c)
+    assert r["kp"].shape[2] == d_store
+    m = _check_masks(r, c)
+    assert not m[..., d_store:].any()
+    ref = oracle_decode(inp, c, m)
+    assert_close(r["out"].cpu().double().numpy(), ref, "bf16", f"memory cut {T},{d_store},{k}")
+
+
 @pytest.mark.parametrize("length", [1, 63, 255, 256, 257, 511, 512, 2047, 2048, 2049, 4096, 4097,
                                     4100])
 def test_decode_ragged_lengths_f32(length):
