@@ -27,7 +27,9 @@ Two further workloads are measured beside the headline and reported in the same 
    131072), where the gain of fewer kept dims over k=128 sets in;
  * memory_cut: AQUA-Memory's static cut (K' stored on 96 or 64 of 128 dims, top-64 or top-48 of
    them kept) at both decode shapes: decode kernel time, GB/s, KV bytes, speedup over the full
-   cache.
+   cache;
+ * retention: the output lost at k = 96, 64, 32 with magnitude selection and with first-k
+   slicing, under the generator's P, an SVD-calibrated P and an uncalibrated one.
 """
 from __future__ import annotations
 
@@ -366,6 +368,68 @@ def bench_memory_cut(dev, steps: int, warmup: int):
                       "its stream"}
 
 
+def bench_retention(dev):
+    """How much of the attention output the kept dims retain, magnitude selection against slicing
+    (the pages' ablation: selecting by the projected query's magnitude against keeping the first
+    k dims), under three projections: the generator's own P, a P calibrated by SVD on 16384
+    independent query and key vectors of the same generator (the method's offline phase), and an
+    uncalibrated random orthogonal P.  Loss = relative L2 distance of the decode output at k from
+    the output at k = 128 (exact attention for an orthogonal P) under the same P; B=4, T=4096,
+    Llama-3.1-8B head layout, every step through libaqua on the GPU."""
+    from sparse_dimension_attention_amd.calibrate import calibrate_projection
+    from synth import make_qk_block
+
+    c = config(2, B=4, T=4096)
+    B, Hq, Hkv, d, T = c["B"], c["Hq"], c["Hkv"], c["d"], c["T"]
+    inp = make_decode_inputs(c, workers=16)
+    qc, _ = make_qk_block(c["id"], "calib_q", (0, 0), 8192, d, c["tau"], inp["P64"])
+    kc, _ = make_qk_block(c["id"], "calib_k", (0, 0), 8192, d, c["tau"], inp["P64"])
+    g = torch.Generator().manual_seed(12345)
+    qr, rr = torch.linalg.qr(torch.randn(d, d, dtype=torch.float64, generator=g))
+    projections = {
+        "generator": inp["P"],
+        "calibrated": calibrate_projection(torch.from_numpy(np.concatenate([qc, kc]))),
+        "uncalibrated": (qr * torch.sign(torch.diagonal(rr))).float(),
+    }
+    k_all, v_all = inp["k"].to(dev), inp["v"].to(dev)
+    q = inp["q"].reshape(B * Hq, d).to(dev)
+    scale = 1.0 / math.sqrt(d)
+    kp = torch.empty(B, Hkv, d, T, dtype=torch.bfloat16, device=dev)
+    v = torch.empty(B, Hkv, T, d, dtype=torch.bfloat16, device=dev)
+    qp = torch.empty(B * Hq, d, device=dev)
+    mask = torch.empty(B * Hq, d // 32, dtype=torch.int32, device=dev)
+    out = torch.empty(B, Hq, d, device=dev)
+
+    def first_k(k: int) -> torch.Tensor:
+        m = np.zeros((B * Hq, d), bool)
+        m[:, :k] = True
+        return torch.from_numpy(np.packbits(m, axis=-1, bitorder="little").view(np.int32)
+                                .copy()).to(dev)
+
+    res = {}
+    for name, P in projections.items():
+        P = P.to(dev)
+        cache = aq.make_cache(kp, v, 0)
+        aq.aqua_project_keys(cache, k_all, v_all, P, T)
+        ws = torch.zeros(aq.aqua_decode_workspace(cache, Hq), dtype=torch.uint8, device=dev)
+
+        def run(k: int, static: bool) -> np.ndarray:
+            aq.aqua_select_dims(q, P, d, k, qp, mask)
+            aq.aqua_decode(cache, Hq, qp, first_k(k) if static else mask, scale, out, ws)
+            torch.cuda.synchronize()
+            return out.cpu().double().numpy()
+
+        exact = run(d, False)
+        rows = {}
+        for k in (96, 64, 32):
+            lm = float(np.linalg.norm(run(k, False) - exact) / np.linalg.norm(exact))
+            ls = float(np.linalg.norm(run(k, True) - exact) / np.linalg.norm(exact))
+            rows[str(k)] = {"magnitude": lm, "slicing": ls, "slicing_over_magnitude": ls / lm}
+        res[name] = rows
+    return {"workload": "llama8b_decode_bf16_b4_t4096", "loss": "relative L2 distance of the "
+            "decode output at k from the output at k=128, same P", "by_projection": res}
+
+
 def bench_h2o(dev, reps: int):
     """64 heavy-hitter decode steps over a compact AQUA-Memory cache."""
     from sparse_dimension_attention_amd.h2o import H2OCache
@@ -467,8 +531,8 @@ def main():
                     help="run one step implementation only, untimed (for counter runs)")
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the prefill and H2O workloads")
-    ap.add_argument("--secondary-only", choices=("prefill", "h2o", "long", "memory"),
-                    default=None,
+    ap.add_argument("--secondary-only",
+                    choices=("prefill", "h2o", "long", "memory", "retention"), default=None,
                     help="run only that workload and print its record (for profiler runs)")
     ap.add_argument("--secondary-reps", type=int, default=5)
     args = ap.parse_args()
@@ -491,6 +555,8 @@ def main():
             r = bench_long_decode(dev, min(args.steps, 50), min(args.warmup, 10))
         elif args.secondary_only == "memory":
             r = bench_memory_cut(dev, min(args.steps, 50), min(args.warmup, 10))
+        elif args.secondary_only == "retention":
+            r = bench_retention(dev)
         else:
             fn = bench_prefill if args.secondary_only == "prefill" else bench_h2o
             r = fn(dev, args.secondary_reps)
@@ -615,6 +681,8 @@ def main():
         rec["long_decode"] = bench_long_decode(dev, min(args.steps, 50), min(args.warmup, 10))
         torch.cuda.empty_cache()
         rec["memory_cut"] = bench_memory_cut(dev, min(args.steps, 50), min(args.warmup, 10))
+        torch.cuda.empty_cache()
+        rec["retention"] = bench_retention(dev)
     if not args.no_cpu:
         rec["cpu_baseline"] = cpu_baseline(c, args.cpu_groups, args.cpu_reps)
     print(json.dumps(rec))

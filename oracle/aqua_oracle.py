@@ -14,6 +14,8 @@ Sources (the method is described in prose only; no formula or listing is printed
   [mem]    the same blog post, section "AQUA-Memory" (static dimension cut before caching, then
            dynamic selection within the kept dimensions).
   [h2o]    [abs] and the blog's "Key Advantages" (AQUA combined with H2O token eviction).
+  [off]    [frame] (the offline phase: a projection learned by SVD on a calibration set) and the
+           blog's "How AQUA Works", step 1 (offline projection computation).
 
 Where the pages leave a step open, the reading taken is stated at the function.  Every
 function works in float64 on exactly the values it is given; callers pass the stored
@@ -30,7 +32,7 @@ import numpy as np
 __all__ = [
     "round_to_storage", "project", "project_keys_stored", "select", "sparse_scores", "softmax",
     "attend", "decode", "prefill", "chunked_prefill", "split_partials", "combine_partials",
-    "h2o_seed_mass", "h2o_heavy_set", "h2o_step", "h2o_run",
+    "h2o_seed_mass", "h2o_heavy_set", "h2o_step", "h2o_run", "calibrate",
 ]
 
 
@@ -257,3 +259,22 @@ def h2o_run(P, q_seed, q_steps, K_ctx, V_ctx, k_steps, v_steps, d_sel, k, d_stor
         sets.append(A)
         masses.append(mass.copy())
     return np.stack(outs), sets, masses
+
+
+# ----------------------------------------------------------------------------------------------
+# Offline projection [off]: P from an SVD of a calibration set.  Readings (the pages name only
+# "SVD on a calibration dataset"): the set is the rows of `samples` (the stacked query and key
+# vectors of one head group); P's columns are the right singular vectors in decreasing order of
+# singular value, so that dim i of q' = q P is the i-th most important direction (the order the
+# static memory cut relies on); the SVD leaves each column's sign free, and it is fixed here so
+# that the column's entry of largest magnitude (the first such, on ties) is positive.
+# ----------------------------------------------------------------------------------------------
+def calibrate(samples: np.ndarray) -> np.ndarray:
+    X = np.asarray(samples, dtype=np.float64)
+    # rows of vt: descending singular values (all d of them; fewer samples than d need the full
+    # factorisation for the directions the samples do not reach)
+    _, _, vt = np.linalg.svd(X, full_matrices=X.shape[0] < X.shape[1])
+    P = vt.T.copy()
+    lead = np.argmax(np.abs(P), axis=0)
+    P *= np.sign(P[lead, np.arange(P.shape[1])])
+    return P

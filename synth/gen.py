@@ -37,7 +37,8 @@ CONFIGS = {
             d_store=96, d_sel=96, heavy=1024, recent=256, steps=64, tau=40.0, dtype="bf16"),
 }
 
-_TENSOR_IDS = {"P": 1, "q": 2, "k": 3, "v": 4, "q_step": 5, "k_step": 6, "v_step": 7, "q_seed": 8}
+_TENSOR_IDS = {"P": 1, "q": 2, "k": 3, "v": 4, "q_step": 5, "k_step": 6, "v_step": 7, "q_seed": 8,
+               "calib_q": 9, "calib_k": 10}  # calib_*: samples for the offline projection
 
 
 def config(cid: int, **overrides) -> dict:

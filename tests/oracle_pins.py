@@ -448,4 +448,67 @@ def pin_25_percent():
     assert 1 - c["k"] / c["d"] == 0.25
 
 
+def _orthonormal(rng, n, m):
+    q, r = np.linalg.qr(rng.standard_normal((n, m)))
+    return q * np.sign(np.diag(r))
+
+
+def pin_calibrate_recovers_rotation():
+    """Samples X = A diag(s) R^T with orthonormal A and distinct s have X^T X = R diag(s^2) R^T
+    exactly, so the calibrated P is R column for column up to sign, in decreasing order of s."""
+    rng = _rng(71)
+    d, n = 16, 200
+    R = _orthonormal(rng, d, d)
+    s = np.sort(rng.uniform(0.5, 3.0, d))[::-1]
+    perm = rng.permutation(d)  # the rows of X come in any order of the directions
+    X = _orthonormal(rng, n, d)[:, perm] @ np.diag(s[perm]) @ R[:, perm].T
+    P = O.calibrate(X)
+    assert P.shape == (d, d)
+    assert np.allclose(np.abs(P.T @ R), np.eye(d), atol=1e-10)
+    # the variance of each calibrated coordinate is the matching s^2, in decreasing order
+    assert np.allclose(np.sum((X @ P) ** 2, axis=0), s ** 2, rtol=1e-10)
+    # the sign rule: each column's largest-magnitude entry is positive
+    lead = np.argmax(np.abs(P), axis=0)
+    assert np.all(P[lead, np.arange(d)] > 0)
+
+
+def pin_calibrate_low_rank():
+    """A rank-r calibration set: P is orthogonal, its first r columns span the samples' row space
+    (X P has zero columns past r), and the calibrated coordinates carry all the energy."""
+    rng = _rng(72)
+    d, n, r = 12, 50, 5
+    X = rng.standard_normal((n, r)) @ rng.standard_normal((r, d))
+    P = O.calibrate(X)
+    assert np.allclose(P.T @ P, np.eye(d), atol=1e-12)
+    Y = X @ P
+    assert np.max(np.abs(Y[:, r:])) < 1e-10 * np.max(np.abs(X))
+    assert np.isclose(np.sum(Y ** 2), np.sum(X ** 2), rtol=1e-12)
+    e = np.sum(Y ** 2, axis=0)
+    assert np.all(np.diff(e[:r]) <= 1e-12 * e[0])
+    # fewer samples than dims: still a full orthogonal P, the samples' span first
+    X2 = rng.standard_normal((4, d))
+    P2 = O.calibrate(X2)
+    assert np.allclose(P2.T @ P2, np.eye(d), atol=1e-12)
+    assert np.max(np.abs(X2 @ P2[:, 4:])) < 1e-10 * np.max(np.abs(X2))
+
+
+def pin_calibrate_generator():
+    """On the workload generator's own queries and keys (raw = Z diag(s) P^T, s decreasing), the
+    calibrated P's leading r columns span the generator's leading r directions to within the
+    sampling error of 16384 rows, and (Ky Fan: no r orthonormal directions capture more of the
+    samples' energy than the top r right singular vectors) they capture at least as much energy
+    as the generator's own columns."""
+    from synth import make_qk_block, make_projection
+
+    P64 = make_projection(2, 128)
+    q, _ = make_qk_block(2, "calib_q", (0, 0), 8192, 128, 40.0, P64)
+    k, _ = make_qk_block(2, "calib_k", (0, 0), 8192, 128, 40.0, P64)
+    X = np.concatenate([q, k]).astype(np.float64)
+    P = O.calibrate(X)
+    for r in (16, 32, 64, 96):
+        M = P64[:, :r].T @ P[:, :r]
+        assert np.sum(M ** 2) / r > 0.99, r
+        assert np.sum((X @ P[:, :r]) ** 2) >= np.sum((X @ P64[:, :r]) ** 2), r
+
+
 PINS = {name: fn for name, fn in globals().items() if name.startswith("pin_")}

@@ -76,6 +76,26 @@ def test_decode_memory_cut(T, d_store, k):
     assert_close(r["out"].cpu().double().numpy(), ref, "bf16", f"memory cut {T},{d_store},{k}")
 
 
+@pytest.mark.parametrize("T,k", [(3000, 96), (9000, 32)])
+def test_decode_static_first_k_mask(T, k):
+    """aqua_decode takes any mask: the first-k slicing baseline (dims [0, k) for every query)
+    against the oracle on the same mask."""
+    c = config(2, B=2, Hq=8, Hkv=2, T=T, k=k)
+    inp = make_decode_inputs(c)
+    B, Hq, Hkv, d = c["B"], c["Hq"], c["Hkv"], c["d"]
+    r = run_decode(inp, c)  # builds the cache and q'; its own masks are not used below
+    m = np.zeros((B, Hq, d), bool)
+    m[..., :k] = True
+    words = np.packbits(m.reshape(B * Hq, d), axis=-1, bitorder="little").view(np.int32)
+    mask = torch.from_numpy(words.copy()).to(DEV)
+    out = torch.full((B, Hq, d), float("nan"), device=DEV)
+    ws = torch.zeros_like(r["ws"])
+    aq.aqua_decode(r["cache"], Hq, r["qp"].reshape(B * Hq, d), mask, 1 / math.sqrt(d), out, ws)
+    torch.cuda.synchronize()
+    ref = oracle_decode(inp, c, m)
+    assert_close(out.cpu().double().numpy(), ref, "bf16", f"first-{k} mask, T={T}")
+
+
 @pytest.mark.parametrize("length", [1, 63, 255, 256, 257, 511, 512, 2047, 2048, 2049, 4096, 4097,
                                     4100])
 def test_decode_ragged_lengths_f32(length):

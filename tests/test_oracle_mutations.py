@@ -105,7 +105,26 @@ def _memory_cut_last_dims(K, P, dtype, d_store):
     return _orig["round_to_storage"](_orig["project"](K, P), dtype)[..., -d_store:]
 
 
+def _calibrate_ascending(samples):
+    return _orig["calibrate"](samples)[:, ::-1]
+
+
+def _calibrate_left_vectors(samples):
+    # the left singular vectors' first d rows instead of the right singular vectors
+    X = np.asarray(samples, np.float64)
+    u, _, _ = np.linalg.svd(X, full_matrices=False)
+    d = X.shape[1]
+    return u[:d, :d] if u.shape[0] >= d else np.eye(d)
+
+
+def _calibrate_transposed(samples):
+    return _orig["calibrate"](samples).T
+
+
 MUTANTS = {
+    "calibrate: ascending singular values": ("calibrate", _calibrate_ascending),
+    "calibrate: left singular vectors": ("calibrate", _calibrate_left_vectors),
+    "calibrate: P transposed": ("calibrate", _calibrate_transposed),
     "select: ties to the higher index": ("select", _select_ties_high),
     "select: smallest magnitudes": ("select", _select_smallest),
     "select: signed value, not magnitude": ("select", _select_signed),
