@@ -193,6 +193,7 @@ struct PrefillArgs {
   int B, Hq, Hkv, d_store, T_cap, Lq, pos0;
   int qh;            // query heads per workgroup (min(G, 4))
   int nqb;           // position blocks per (b, group, head subset)
+  int pair;          // 1: a workgroup pairs 32-row block j with block Lq/32 - 1 - j (see below)
 };
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
@@ -222,13 +223,23 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(PrefillArgs a)
   const int bg = combo / nsub;
   const int b = bg / a.Hkv, g = bg - b * a.Hkv;
   const int head = g * G + sub * a.qh + (w % a.qh);
-  const int pb = qblk * WPH + w / a.qh;
-  const int kend = a.pos0 + min((qblk + 1) * WPH * ROWS, a.Lq);
+  // Paired form (two wavefronts per head, ROWS = 32, Lq a multiple of 64): the head's two
+  // wavefronts take 32-row blocks j and Lq / 32 - 1 - j, so every workgroup has about the same
+  // causal work; the wavefront of the early block stops computing after its own last tile and
+  // the other one, alone on its SIMD from then on, runs faster.  Otherwise the workgroup's
+  // wavefronts take consecutive blocks.
+  const int pb = a.pair ? (w / a.qh == 0 ? qblk : a.Lq / ROWS - 1 - qblk)
+                        : qblk * WPH + w / a.qh;
+  const int kend = a.pair ? a.pos0 + a.Lq - qblk * ROWS
+                          : a.pos0 + min((qblk + 1) * WPH * ROWS, a.Lq);
   const int ntile = (kend + KT - 1) / KT;
-  const int pos_first_wg = a.pos0 + min(qblk * WPH * ROWS, a.Lq - 1);
+  const int pos_first_wg =
+      a.pos0 + (a.pair ? qblk * ROWS : min(qblk * WPH * ROWS, a.Lq - 1));
   // tiles [0, n_pipe) are visible to every row of the workgroup and have a successor: they take
   // the step without causal masking
   const int n_pipe = min((pos_first_wg + 1) / KT, ntile - 1);
+  // tiles [0, ntile_w) hold keys this wavefront's rows attend (uniform over the wavefront)
+  const int ntile_w = (a.pos0 + min((pb + 1) * ROWS, a.Lq) + KT - 1) / KT;
 
   int pos[QB], pos_blk[QB];
   u32x4_t qreg[QB][8];
@@ -396,22 +407,28 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(PrefillArgs a)
   // current tile's into probabilities and P V follows; the next tile's max is checked at the end
   // of the step, next to the barrier.  K' tile t+1 and V tile t are read in step t.
   f32x16_t a0[QB], a1[QB], b0[QB], b1[QB];
+  // Past its own last tile a wavefront only helps stage the tiles (masked steps only: every
+  // wavefront holds keys in the unmasked ones).
   auto step = [&](int t, f32x16_t (&s0)[QB], f32x16_t (&s1)[QB], f32x16_t (&x0)[QB],
                   f32x16_t (&x1)[QB], bool masked, bool has_next, bool check_next) {
     const bf16_t *vt = sV[t & 1];
-    if (has_next) {
+    const bool cur = !masked || t < ntile_w;
+    const bool nxt = has_next && (!masked || t + 1 < ntile_w);
+    if (nxt) {
       s_half(sK[(t + 1) & 1], 0, x0);
       s_half(sK[(t + 1) & 1], 1, x1);
     }
-    if (masked) {
-      mask_half(t * KT, s0);
-      mask_half(t * KT + 32, s1);
-      rescale(s0, s1);
+    if (cur) {
+      if (masked) {
+        mask_half(t * KT, s0);
+        mask_half(t * KT + 32, s1);
+        rescale(s0, s1);
+      }
+      probs(s0, 0);
+      probs(s1, 1);
+      pv_half(vt, 0);
+      pv_half(vt, 1);
     }
-    probs(s0, 0);
-    probs(s1, 1);
-    pv_half(vt, 0);
-    pv_half(vt, 1);
     if (check_next) rescale(x0, x1);
     store_K(sK[t & 1]);
     store_V(sV[(t + 1) & 1]);
@@ -460,6 +477,10 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(PrefillArgs a)
   for (; t + 2 <= n_pipe; t += 2) {
     step(t, a0, a1, b0, b1, false, true, true);
     step(t + 1, b0, b1, a0, a1, false, true, t + 2 < n_pipe);
+  }
+  for (; t + 2 < ntile; t += 2) {  // causal masking, both tiles with a successor
+    step(t, a0, a1, b0, b1, true, true, false);
+    step(t + 1, b0, b1, a0, a1, true, true, false);
   }
   for (; t < ntile; ++t) {  // the last tiles: causal masking, and a tile without successor
     step(t, a0, a1, b0, b1, true, t + 1 < ntile, false);
@@ -527,6 +548,7 @@ hipError_t launch_prefill(const void *kp, const void *v, int B, int Hq, int Hkv,
   a.qh = G < 4 ? G : 4;
   const int rows_per_wg = 256 / a.qh;  // 256 query rows per workgroup over qh heads
   a.nqb = (Lq + rows_per_wg - 1) / rows_per_wg;
+  a.pair = (a.qh == 4 && Lq % 64 == 0) ? 1 : 0;  // two 32-row blocks per head and workgroup
   const int grid = a.nqb * (G / a.qh) * B * Hkv;
   prefill_attn_kernel<1, 8><<<dim3(grid), dim3(512), 0, s>>>(a);
   return hipGetLastError();

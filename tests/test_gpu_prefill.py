@@ -15,7 +15,8 @@ pytestmark = pytest.mark.gpu
 
 
 def _run_chunks(inp, c, chunk, T_cap=None, d_store=None, d_sel=None, k=None):
-    """Append each chunk's keys, then prefill its queries.  Returns GPU out, q', masks."""
+    """Append each chunk's keys, then prefill its queries.  Returns GPU out, q', masks.
+    chunk: a chunk length, or the list of chunk lengths."""
     B, Hq, Hkv, d, T = c["B"], c["Hq"], c["Hkv"], c["d"], c["T"]
     d_store = d_store or d
     d_sel = d_sel or d_store
@@ -27,8 +28,11 @@ def _run_chunks(inp, c, chunk, T_cap=None, d_store=None, d_sel=None, k=None):
     out = torch.full((B, Hq, T, d), float("nan"), device=DEV)
     qp = torch.full((B, Hq, T, d), float("nan"), device=DEV)
     mask = torch.zeros(B, Hq, T, d // 32, dtype=torch.int32, device=DEV)
-    for c0 in range(0, T, chunk):
-        L = min(chunk, T - c0)
+    lengths = chunk if isinstance(chunk, (list, tuple)) else \
+        [min(chunk, T - c0) for c0 in range(0, T, chunk)]
+    assert sum(lengths) == T
+    c0 = 0
+    for L in lengths:
         aq.aqua_project_keys(cache, inp["k"][:, :, c0:c0 + L].contiguous().to(DEV),
                              inp["v"][:, :, c0:c0 + L].contiguous().to(DEV), P, L)
         ws = torch.empty(aq.aqua_prefill_workspace(cache, Hq, L), dtype=torch.uint8, device=DEV)
@@ -40,6 +44,7 @@ def _run_chunks(inp, c, chunk, T_cap=None, d_store=None, d_sel=None, k=None):
         out[:, :, c0:c0 + L] = o
         qp[:, :, c0:c0 + L] = qpc
         mask[:, :, c0:c0 + L] = mc
+        c0 += L
     torch.cuda.synchronize()
     return out, qp, mask
 
@@ -80,6 +85,10 @@ def _check(inp, c, out, qp, mask, rows, d_sel, k, d_store=None):
     (4, 4, 333, 128, 64),     # G = 1
     (8, 4, 260, 100, 128),    # G = 2, k = d
     (16, 2, 200, 200, 32),    # G = 8
+    # chunks that are multiples of 64 at G >= 4 take the paired form (blocks j and last - j)
+    (8, 2, 1024, 512, 96),    # two chunks of 16 blocks
+    (16, 2, 640, 128, 64),    # G = 8, five chunks of 4 blocks
+    (8, 2, 512, [32, 128, 256, 96], 96),  # paired chunks starting at 32 and 160
 ])
 def test_prefill_small_all_rows(Hq, Hkv, T, chunk, k):
     c = config(4, B=2, Hq=Hq, Hkv=Hkv, T=T, k=k)
