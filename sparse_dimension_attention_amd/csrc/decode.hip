@@ -18,7 +18,8 @@
 //    row (d = 128 bf16: 16 lanes per token, 4 tokens per wavefront load).
 //  * The workgroup's wavefronts merge their (m, l, o) in LDS; the workgroup writes one partial
 //    per query head.  The last workgroup of a (b, g) to finish (atomic counter in the
-//    workspace) merges all partials of the group, writes the output and resets its counter.
+//    workspace) merges all partials of the group, writes the output and resets its counter;
+//    past 16 splits per group the merge takes two levels (finish_split).
 //  * H2O mass mode additionally stores the raw scores and lets that last workgroup add every
 //    token's normalised probability, summed over the group's heads, to its mass.
 //
