@@ -38,12 +38,18 @@ typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 // q' = q P on bf16 MFMA at fp32 accuracy: q is bf16, and every fp32 entry of P is the exact sum
 // of three bf16 parts (RNE of P, of the remainder, of the remainder's remainder: 8 + 8 + 8
 // significand bits), so q' = q P_hi + q P_mid + q P_lo with every product exact and fp32
-// accumulation.  A workgroup walks blocks of 32 rows; wavefront w computes output columns
-// [32w, 32w + 32) with its parts of P held in registers, writes its q' tile to LDS, and after one
-// barrier each wavefront selects 8 of the 32 rows (one row at a time, lane l holding dims l and
-// l + 64).
+// accumulation.  A workgroup of 8 wavefronts walks blocks of 32 rows; wavefront w computes output
+// columns [16w, 16w + 16) on v_mfma_f32_16x16x32_bf16 (A lane l: row l % 16, k = 8 (l / 16) + e;
+// B lane l: column l % 16, same k; D register r: row 4 (l / 16) + r, column l % 16), its parts of
+// P held in registers, and writes its part of the q' tile to LDS; after one barrier each
+// wavefront selects 4 of the 32 rows (one row at a time, lane l holding dims l and l + 64).  The
+// selection is a latency-bound chain of ballots and scalar steps per row, so the layout keeps
+// the registers low (16 columns' parts of P per wavefront) for four wavefronts per SIMD.
 constexpr int SQS = 128 + 8;  // LDS row stride (floats) of the q' tile
+constexpr int SEL_WAVES = 8;  // wavefronts per selection workgroup
+constexpr int SEL_ROWS_PER_WAVE = 32 / SEL_WAVES;
 
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 
 __device__ __forceinline__ void split3(float p, uint32_t &h, uint32_t &m, uint32_t &l) {
   const uint32_t hm = pack_bf16x2(p, 0.0f);
@@ -54,72 +60,73 @@ __device__ __forceinline__ void split3(float p, uint32_t &h, uint32_t &m, uint32
   l = pack_bf16x2(r2, 0.0f) & 0xffffu;
 }
 
-__global__ __launch_bounds__(256) void prefill_select_kernel(const bf16_t *__restrict__ q, int N,
-                                                             const float *__restrict__ P,
-                                                             int d_sel, int k, float qscale,
-                                                             float *__restrict__ q_proj,
-                                                             uint32_t *__restrict__ mask,
-                                                             bf16_t *__restrict__ qm) {
+__global__ __launch_bounds__(SEL_WAVES * 64) void prefill_select_kernel(
+    const bf16_t *__restrict__ q, int N, const float *__restrict__ P, int d_sel, int k,
+    float qscale, float *__restrict__ q_proj, uint32_t *__restrict__ mask,
+    bf16_t *__restrict__ qm) {
+  constexpr int R = SEL_ROWS_PER_WAVE;
   __shared__ __align__(16) float sQ[2][32 * SQS];
-  __shared__ __align__(16) bf16_t sM[4 * 8 * 128];
+  __shared__ __align__(16) bf16_t sM[SEL_WAVES * R * 128];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int col = 32 * w + (lane & 31);
-  // B operands: P[16 m + 8 (lane / 32) + e][col], e = 0..7, in three bf16 parts
-  u32x4_t bh[8], bm[8], bl[8];
+  const int col = 16 * w + (lane & 15);
+  // B operands: P[32 s + 8 (lane / 16) + e][col], e = 0..7, in three bf16 parts
+  u32x4_t bh[4], bm[4], bl[4];
 #pragma unroll
-  for (int m = 0; m < 8; ++m) {
+  for (int st = 0; st < 4; ++st) {
     uint32_t h[8], mi[8], lo[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e)
-      split3(P[(16 * m + 8 * (lane >> 5) + e) * 128 + col], h[e], mi[e], lo[e]);
-    bh[m] = u32x4_t{h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16, h[6] | h[7] << 16};
-    bm[m] = u32x4_t{mi[0] | mi[1] << 16, mi[2] | mi[3] << 16, mi[4] | mi[5] << 16,
-                    mi[6] | mi[7] << 16};
-    bl[m] = u32x4_t{lo[0] | lo[1] << 16, lo[2] | lo[3] << 16, lo[4] | lo[5] << 16,
-                    lo[6] | lo[7] << 16};
+      split3(P[(32 * st + 8 * (lane >> 4) + e) * 128 + col], h[e], mi[e], lo[e]);
+    bh[st] = u32x4_t{h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16, h[6] | h[7] << 16};
+    bm[st] = u32x4_t{mi[0] | mi[1] << 16, mi[2] | mi[3] << 16, mi[4] | mi[5] << 16,
+                     mi[6] | mi[7] << 16};
+    bl[st] = u32x4_t{lo[0] | lo[1] << 16, lo[2] | lo[3] << 16, lo[4] | lo[5] << 16,
+                     lo[6] | lo[7] << 16};
   }
   const int nblk = (N + 31) / 32;
-  bf16_t *qrows = sM + 8 * 128 * w;  // this wavefront's 8 rows of qm, staged for 16-byte stores
-  // A operands of the first block; each block then loads the next one's before selecting
-  u32x4_t av[8];
+  bf16_t *qrows = sM + R * 128 * w;  // this wavefront's rows of qm, staged for 16-byte stores
+  // A operands of a block (two halves of 16 rows); each block then loads the next one's before
+  // selecting
+  u32x4_t av[2][4];
   auto load_rows = [&](int blk) {
-    const int arow = min(blk * 32 + (lane & 31), N - 1);
-    const bf16_t *qa = q + static_cast<size_t>(arow) * 128 + 8 * (lane >> 5);
 #pragma unroll
-    for (int m = 0; m < 8; ++m) av[m] = *reinterpret_cast<const u32x4_t *>(qa + 16 * m);
+    for (int hf = 0; hf < 2; ++hf) {
+      const int arow = min(blk * 32 + 16 * hf + (lane & 15), N - 1);
+      const bf16_t *qa = q + static_cast<size_t>(arow) * 128 + 8 * (lane >> 4);
+#pragma unroll
+      for (int st = 0; st < 4; ++st) av[hf][st] = *reinterpret_cast<const u32x4_t *>(qa + 32 * st);
+    }
   };
   if (blockIdx.x < nblk) load_rows(blockIdx.x);
   int buf = 0;
   for (int blk = blockIdx.x; blk < nblk; blk += gridDim.x, buf ^= 1) {
     const int r0 = blk * 32;
-    // ---- projection: rows r0 .. r0+31 (clamped), columns [32w, 32w+32)
-    f32x16_t acc_h, acc_l;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      acc_h[r] = 0.0f;
-      acc_l[r] = 0.0f;
-    }
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, av[m]);
-      acc_l = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, bl[m]),
-                                                      acc_l, 0, 0, 0);
-      acc_l = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, bm[m]),
-                                                      acc_l, 0, 0, 0);
-      acc_h = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, bh[m]),
-                                                      acc_h, 0, 0, 0);
-    }
+    // ---- projection: rows r0 .. r0+31 (clamped), columns [16w, 16w+16)
     float *tile = sQ[buf];
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-      tile[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * SQS + col] = acc_h[r] + acc_l[r];
+    for (int hf = 0; hf < 2; ++hf) {
+      f32x4_t acc_h = {0.0f, 0.0f, 0.0f, 0.0f}, acc_l = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, av[hf][st]);
+        acc_l = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, bl[st]),
+                                                        acc_l, 0, 0, 0);
+        acc_l = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, bm[st]),
+                                                        acc_l, 0, 0, 0);
+        acc_h = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, bh[st]),
+                                                        acc_h, 0, 0, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        tile[(16 * hf + 4 * (lane >> 4) + r) * SQS + col] = acc_h[r] + acc_l[r];
+    }
     if (blk + static_cast<int>(gridDim.x) < nblk) load_rows(blk + gridDim.x);
     __syncthreads();
-    // ---- selection: wavefront w takes rows 8w .. 8w+7 of the block
-    const int nrows = min(8, N - (r0 + 8 * w));  // uniform over the wavefront
+    // ---- selection: wavefront w takes rows R w .. R w + R - 1 of the block
+    const int nrows = min(R, N - (r0 + R * w));  // uniform over the wavefront
     for (int rr = 0; rr < nrows; ++rr) {
-      const int row = r0 + 8 * w + rr;
-      const float *tr = tile + (8 * w + rr) * SQS;
+      const int row = r0 + R * w + rr;
+      const float *tr = tile + (R * w + rr) * SQS;
       const float x[2] = {tr[lane], tr[lane + 64]};
       bool sel[2];
       wave_topk_threshold<2>(x, d_sel, k, sel);
@@ -140,14 +147,11 @@ __global__ __launch_bounds__(256) void prefill_select_kernel(const bf16_t *__res
     // the wavefront's rows of qm are contiguous in HBM: 16-byte stores (LDS is in order within
     // a wavefront, so the values written above are read back here)
     if (nrows > 0) {
-      bf16_t *dst = qm + static_cast<size_t>(r0 + 8 * w) * 128;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int c = lane + 64 * h;  // 16-byte chunk: row c / 16
-        if (c < nrows * 16)
-          *reinterpret_cast<u32x4_t *>(dst + 8 * c) =
-              *reinterpret_cast<const u32x4_t *>(qrows + 8 * c);
-      }
+      bf16_t *dst = qm + static_cast<size_t>(r0 + R * w) * 128;
+      const int c = lane;  // 16-byte chunk: row c / 16
+      if (c < nrows * 16)
+        *reinterpret_cast<u32x4_t *>(dst + 8 * c) =
+            *reinterpret_cast<const u32x4_t *>(qrows + 8 * c);
     }
     // the next block writes the other tile; the barrier above it orders this block's reads
   }
@@ -527,7 +531,7 @@ hipError_t launch_prefill(const void *kp, const void *v, int B, int Hq, int Hkv,
   bf16_t *qm = static_cast<bf16_t *>(ws);
   uint32_t *mask = mask_out ? mask_out : reinterpret_cast<uint32_t *>(qm + rows * 128);
   const int nblk = static_cast<int>((rows + 31) / 32);
-  prefill_select_kernel<<<dim3(nblk < 512 ? nblk : 512), dim3(256), 0, s>>>(
+  prefill_select_kernel<<<dim3(nblk < 768 ? nblk : 768), dim3(SEL_WAVES * 64), 0, s>>>(
       static_cast<const bf16_t *>(q), static_cast<int>(rows), P, d_sel, k,
       scale * 1.4426950408889634f, q_proj_out, mask, qm);
   hipError_t e = hipGetLastError();
