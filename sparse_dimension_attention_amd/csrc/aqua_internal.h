@@ -108,6 +108,16 @@ __device__ __forceinline__ void wave_topk_threshold(const float (&x)[E], int d_s
   }
 }
 
+// A workgroup barrier that orders LDS traffic only: unlike __syncthreads, whose fence waits
+// for every outstanding global load too, it lets loads issued earlier stay in flight.  The
+// empty asm statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt left at their maxima
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // ------------------------------------------------------------------ H2O eviction rule
 // Among the slots of one (b, g) holding a position <= limit (t_new - recent), the one ranked lowest
 // by (mass descending, position ascending): the minimum of the 64-bit key (mass bits,

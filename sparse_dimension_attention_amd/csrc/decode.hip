@@ -273,16 +273,6 @@ __device__ __forceinline__ void finish_split(const DecodeArgs &a, size_t head0, 
   merge_splits<D, G, NT>(a, head0, bg, s_M, s_L, restart, a.S, 1);
 }
 
-// A workgroup barrier that orders LDS traffic only: unlike __syncthreads, whose fence waits
-// for every outstanding global load too, it lets loads issued earlier stay in flight.  The
-// empty asm statements keep the compiler from moving memory accesses across it.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt left at their maxima
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 // Fused prologue shared by the fused decode step and the fused H2O step: stage P in LDS, project
 // the group's G query rows and, when with_key, the new token's key (q'_h[i] = sum_j q_h[j] P[j][i]
 // in fp32, j ascending: the arithmetic of select_kernel and of the key projection, so the results

@@ -121,7 +121,7 @@ __global__ __launch_bounds__(SEL_WAVES * 64) void prefill_select_kernel(
         tile[(16 * hf + 4 * (lane >> 4) + r) * SQS + col] = acc_h[r] + acc_l[r];
     }
     if (blk + static_cast<int>(gridDim.x) < nblk) load_rows(blk + gridDim.x);
-    __syncthreads();
+    lds_barrier();  // the next block's rows stay in flight through the selection
     // ---- selection: wavefront w takes rows R w .. R w + R - 1 of the block
     const int nrows = min(R, N - (r0 + R * w));  // uniform over the wavefront
     for (int rr = 0; rr < nrows; ++rr) {
