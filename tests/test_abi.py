@@ -128,3 +128,76 @@ def test_h2o_victim_rejects(lib):
 def test_binding_raises_with_message(lib):
     with pytest.raises(aq.AquaError, match="AQUA_ERR_SHAPE"):
         A._check(_decode(lib, _cache(len=0)))
+
+
+def _prefill(lib, cache, Hq=8, Lq=4, pos0=0, d_sel=128, k=96, q=FAKE, P=FAKE, out=FAKE, ws=FAKE,
+             ws_bytes=1 << 30, q_proj=None):
+    return lib.aqua_prefill_chunk(ctypes.byref(cache), Hq, q, Lq, pos0, P, d_sel, k, 0.1, out,
+                                  q_proj, None, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,args,status", [
+    (dict(dtype=A.AQUA_F32), dict(), A.AQUA_ERR_DTYPE),      # prefill is bf16 only
+    (dict(d_head=64, d_store=64), dict(), A.AQUA_ERR_SHAPE),  # and d_head 128 only
+    (dict(d_store=100), dict(d_sel=96), A.AQUA_ERR_SHAPE),    # d_store a multiple of 16
+    (dict(), dict(Hq=6), A.AQUA_ERR_SHAPE),                   # Hq not a multiple of Hkv
+    (dict(), dict(q=None), A.AQUA_ERR_NULL),
+    (dict(), dict(ws=None), A.AQUA_ERR_WORKSPACE),
+    (dict(), dict(Lq=0), A.AQUA_ERR_SHAPE),
+    (dict(), dict(pos0=-1), A.AQUA_ERR_SHAPE),
+    (dict(), dict(pos0=8, Lq=4), A.AQUA_ERR_CAPACITY),        # pos0 + Lq > len = 10
+    (dict(), dict(k=0), A.AQUA_ERR_SHAPE),
+    (dict(), dict(k=97, d_sel=96), A.AQUA_ERR_SHAPE),         # k > d_sel
+    (dict(d_store=96), dict(d_sel=128), A.AQUA_ERR_SHAPE),    # d_sel > d_store
+    (dict(), dict(out=FAKE + 4), A.AQUA_ERR_ALIGN),
+    (dict(), dict(q_proj=FAKE + 8), A.AQUA_ERR_ALIGN),
+    (dict(), dict(ws_bytes=16), A.AQUA_ERR_WORKSPACE),
+])
+def test_prefill_rejects(lib, kw, args, status):
+    assert _prefill(lib, _cache(**kw), **args) == status
+    assert lib.aqua_last_error().decode() != ""
+
+
+def _step(lib, cache, Hq=8, d_sel=128, k=96, q=FAKE, k_new=FAKE, out=FAKE, ws=FAKE,
+          ws_bytes=1 << 30, mass=None):
+    return lib.aqua_decode_step(ctypes.byref(cache), Hq, q, k_new, FAKE, FAKE, d_sel, k, 0.1,
+                                mass, out, None, None, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,args,status", [
+    (dict(), dict(Hq=6), A.AQUA_ERR_SHAPE),
+    (dict(len=256), dict(), A.AQUA_ERR_CAPACITY),  # no column left for the new token
+    (dict(), dict(k_new=None), A.AQUA_ERR_NULL),
+    (dict(), dict(ws=None), A.AQUA_ERR_WORKSPACE),
+    (dict(), dict(k=0), A.AQUA_ERR_SHAPE),
+    (dict(d_store=96), dict(d_sel=128), A.AQUA_ERR_SHAPE),
+    (dict(), dict(mass=FAKE + 4), A.AQUA_ERR_ALIGN),
+    (dict(), dict(ws_bytes=16), A.AQUA_ERR_WORKSPACE),
+])
+def test_decode_step_rejects(lib, kw, args, status):
+    c = _cache(**kw)
+    assert _step(lib, c, **args) == status
+    assert c.len == kw.get("len", 10)  # a rejected step appends nothing
+
+
+def _h2o_step(lib, cache, Hq=8, k=64, t_new=300, recent=16, mass=FAKE, slot_pos=FAKE,
+              victim=FAKE, ws=FAKE, ws_bytes=1 << 30):
+    return lib.aqua_h2o_step(ctypes.byref(cache), Hq, FAKE, FAKE, FAKE, FAKE, 96, k, 0.1, mass,
+                             slot_pos, t_new, recent, victim, FAKE, None, None, ws, ws_bytes,
+                             None)
+
+
+@pytest.mark.parametrize("kw,args,status", [
+    (dict(len=200), dict(), A.AQUA_ERR_SHAPE),        # the compact cache must be full
+    (dict(T_cap=8192, len=8192), dict(), A.AQUA_ERR_SHAPE),  # more slots than the fused step takes
+    (dict(), dict(mass=None), A.AQUA_ERR_NULL),
+    (dict(), dict(victim=None), A.AQUA_ERR_NULL),
+    (dict(), dict(ws=None), A.AQUA_ERR_WORKSPACE),
+    (dict(), dict(k=97), A.AQUA_ERR_SHAPE),           # k > d_sel = 96
+    (dict(), dict(recent=-1), A.AQUA_ERR_SHAPE),
+    (dict(), dict(mass=FAKE + 4), A.AQUA_ERR_ALIGN),
+    (dict(), dict(ws_bytes=16), A.AQUA_ERR_WORKSPACE),
+])
+def test_h2o_step_rejects(lib, kw, args, status):
+    c = _cache(**dict(dict(d_store=96, T_cap=256, len=256), **kw))
+    assert _h2o_step(lib, c, **args) == status
