@@ -340,8 +340,10 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(PrefillArgs a)
       }
   };
   // s0, s1 hold a tile's scores relative to m.  A row whose maximum passes the slack moves m up
-  // by that maximum: O and l are rescaled, the tile's scores and -m shift with it.
-  auto rescale = [&](f32x16_t (&s0)[QB], f32x16_t (&s1)[QB]) {
+  // by that maximum: O and l are rescaled, the tile's scores and -m shift with it, and so do the
+  // next tile's scores n0, n1 when they were already computed against the old m (shift_next).
+  auto rescale = [&](f32x16_t (&s0)[QB], f32x16_t (&s1)[QB], f32x16_t (&n0)[QB],
+                     f32x16_t (&n1)[QB], bool shift_next) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       float mx = __builtin_fmaxf(s0[qb][0], s0[qb][1]);
@@ -366,6 +368,13 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(PrefillArgs a)
         for (int r = 0; r < 16; ++r) {
           s0[qb][r] -= dm;
           s1[qb][r] -= dm;
+        }
+        if (shift_next) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            n0[qb][r] -= dm;
+            n1[qb][r] -= dm;
+          }
         }
         m_i[qb] += dm;
 #pragma unroll
@@ -426,14 +435,14 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(PrefillArgs a)
       if (masked) {
         mask_half(t * KT, s0);
         mask_half(t * KT + 32, s1);
-        rescale(s0, s1);
+        rescale(s0, s1, x0, x1, nxt);  // x0, x1 were computed against the m before this tile
       }
       probs(s0, 0);
       probs(s1, 1);
       pv_half(vt, 0);
       pv_half(vt, 1);
     }
-    if (check_next) rescale(x0, x1);
+    if (check_next) rescale(x0, x1, x0, x1, false);
     store_K(sK[t & 1]);
     store_V(sV[(t + 1) & 1]);
     load_K(t + 3);

@@ -98,6 +98,45 @@ def test_prefill_small_all_rows(Hq, Hkv, T, chunk, k):
     _check(inp, c, out, qp, mask, rows, c["d"], k)
 
 
+def _plateau_inputs(c, mu=6.0, l0=33.0, l1=16.0):
+    """Inputs whose scores climb in two jumps: every query gets a common component mu*u (u a
+    seeded unit vector), keys 0..63 are -l0*u and keys 64..511 are -l1*u (identical keys, so
+    equal scores), the rest are the generator's.  A row's running max starts near -22 (log2
+    units) from tile 0, jumps to near -11 at position 64 and to the generator's scale (~2) at
+    position 512: two moves past the kernel's 8-unit slack, one of them inside the causally
+    masked steps of the workgroups that hold position 512."""
+    inp = make_prefill_inputs(c)
+    u = np.random.default_rng(2024).standard_normal(c["d"])
+    u = torch.from_numpy(u / np.linalg.norm(u))
+    dt = inp["q"].dtype
+    inp["q"] = (inp["q"].double() + mu * u).to(dt)
+    k = inp["k"].double()
+    k[:, :, :64] = -l0 * u
+    k[:, :, 64:512] = -l1 * u
+    inp["k"] = k.to(dt)
+    return inp
+
+
+@pytest.mark.parametrize("chunk", [512, 300, [448, 128, 448]])
+def test_prefill_running_max_moves(chunk):
+    """The online softmax's running max moving past its slack, in unmasked steps (the next
+    tile's scores checked before use) and in masked ones (the tile's own scores, with the
+    already computed next tile shifted too).  512-token chunks take the paired form, 300 the
+    consecutive one; [448, 128, 448] puts position 512 at a chunk's masked diagonal."""
+    c = config(4, B=1, Hq=8, Hkv=2, T=1024, k=96)
+    inp = _plateau_inputs(c)
+    # the jumps are there: scores of row 900 (oracle arithmetic) at keys 5, 100 and 700
+    P64 = storage_to_f64(inp["P"])
+    Kp = O.project_keys_stored(storage_to_f64(inp["k"][0, 0]), P64, "bf16", c["d"])
+    qp = O.project(storage_to_f64(inp["q"][0, 0, 900]), P64)
+    sel = O.select(qp[None], c["d"], 96)[0]
+    s = (np.where(sel, qp, 0) @ Kp.T) / math.sqrt(c["d"]) / math.log(2)
+    assert s[100] - s[5] > 8 and s[:901].max() - s[100] > 8
+    out, qp_g, mask = _run_chunks(inp, c, chunk)
+    rows = [(0, h, p) for h in range(8) for p in range(c["T"])]
+    _check(inp, c, out, qp_g, mask, rows, c["d"], 96)
+
+
 def test_prefill_memory_cut():
     """AQUA-Memory: K' keeps dims 0..95, top-64 of those 96."""
     c = config(4, B=1, Hq=8, Hkv=2, T=400, k=64)
