@@ -219,6 +219,18 @@ def bench_prefill(dev, reps: int):
                       "each call in one more pass"}
 
 
+def run_us(fn, n: int) -> float:
+    """Microseconds per call of fn over n calls back to back on the current stream, between two
+    HIP events (no marker packet between the launches)."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / n
+
+
 def bench_long_decode(dev, steps: int, warmup: int):
     """Decode over a long context (B=1, 32 query heads, 8 KV heads, T=131072 bf16) at each k of
     {128, 96, 64, 32}, and the same step over shorter prefixes of that context (T from 256 up),
@@ -277,11 +289,16 @@ def bench_long_decode(dev, steps: int, warmup: int):
         bare_us = (time.perf_counter() - t0) * 1e6 / steps
         step_us = events(step)
         cache.len = Tn
-        k_us = events(lambda: aq.aqua_decode(cache, Hq, qp, mask.view(B * Hq, d // 32), scale,
-                                             out, ws))
+
+        def dec():
+            aq.aqua_decode(cache, Hq, qp, mask.view(B * Hq, d // 32), scale, out, ws)
+
+        k_ev_us = events(dec)
+        k_us = run_us(dec, steps)
         U = union_rows(mask.cpu().numpy(), B, Hkv, G, d, d)
         nbytes = decode_bytes(U, cd, Tn)
         return {"step_us": step_us, "step_us_bare": bare_us, "kernel_us": k_us,
+                "kernel_us_launch_events": k_ev_us,
                 "mean_union_rows": float(U.mean()), "bytes": nbytes,
                 "kernel_gbs": nbytes / (k_us * 1e-6) / 1e9}
 
@@ -305,8 +322,9 @@ def bench_long_decode(dev, steps: int, warmup: int):
             "t_sweep": {str(t): {str(k): x for k, x in r.items()} for t, r in sweep.items()},
             "timing": "step_us: median over K steps of HIP events around each aqua_decode_step "
                       "launch on its stream (step_us_bare: K bare calls between two "
-                      "synchronizations, host-bound at short contexts); kernel_us: the same "
-                      "for aqua_decode alone on the step's masks"}
+                      "synchronizations, host-bound at short contexts); kernel_us: "
+                      "aqua_decode alone on the step's masks, K launches back to back between "
+                      "two HIP events (kernel_us_launch_events: median of events around each)"}
 
 
 def bench_memory_cut(dev, steps: int, warmup: int):
@@ -349,12 +367,13 @@ def bench_memory_cut(dev, steps: int, warmup: int):
                 aq.aqua_decode(cache, Hq, qp, mask, scale, out, ws)
                 e1.record()
             torch.cuda.synchronize()
-            k_us = statistics.median(a.elapsed_time(b) for a, b in ev) * 1e3
+            k_ev_us = statistics.median(a.elapsed_time(b) for a, b in ev) * 1e3
+            k_us = run_us(lambda: aq.aqua_decode(cache, Hq, qp, mask, scale, out, ws), steps)
             cc = dict(c, d_store=d_store)
             U = union_rows(mask.cpu().numpy().reshape(B, Hq, d // 32), B, Hkv, G, d, d_store)
             nbytes = decode_bytes(U, cc, T)
             rows[f"{d_store},{k}"] = {
-                "d_store": d_store, "k": k, "kernel_us": k_us,
+                "d_store": d_store, "k": k, "kernel_us": k_us, "kernel_us_launch_events": k_ev_us,
                 "mean_union_rows": float(U.mean()), "bytes": nbytes,
                 "kernel_gbs": nbytes / (k_us * 1e-6) / 1e9,
                 "kv_bytes_per_token": B * Hkv * (d_store + d) * 2}
@@ -369,8 +388,9 @@ def bench_memory_cut(dev, steps: int, warmup: int):
         del k_all, v_all
         torch.cuda.empty_cache()
     return {"cuts": res, "steps": steps, "warmup": warmup,
-            "timing": "kernel_us: median over K launches of HIP events around aqua_decode on "
-                      "its stream"}
+            "timing": "kernel_us: K launches of aqua_decode back to back on its stream "
+                      "between two HIP events; kernel_us_launch_events: median over K launches "
+                      "of HIP events around each"}
 
 
 def bench_retention(dev):
@@ -646,7 +666,28 @@ def main():
         res[path] = (ms, k_ms, ms_ev)
     best = min(res, key=lambda p: res[p][0])
     ms_per_step, k_ms, _ = res[best]
-    k_avg_s = statistics.mean(k_ms) * 1e-3
+
+    # The dominant launch's duration: that launch alone, K times back to back on its stream
+    # between two events.  Events around each launch (k_ms above) add a marker packet's cost,
+    # ~6 us, to every interval; over a run of launches only the launch gaps remain.
+    def launch_only():
+        if best == "three":
+            cache.len = T
+            aq.aqua_decode(cache, Hq, qp, mask, scale, out, ws)
+        else:
+            cache.len = T - 1
+            aq.aqua_decode_step(cache, Hq, q, k_new, v_new, P, d, k, scale, out, ws,
+                                mask_out=mask.view(B, Hq, d // 32))
+
+    for _ in range(args.warmup):
+        launch_only()
+    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    r0.record()
+    for _ in range(args.steps):
+        launch_only()
+    r1.record()
+    torch.cuda.synchronize()
+    k_avg_s = r0.elapsed_time(r1) * 1e-3 / args.steps
 
     U = union_rows(mask.cpu().numpy().reshape(B, Hq, d // 32), B, Hkv, G, d, c["d_store"])
     nbytes = step_bytes(U, c, T) if best == "fused" else decode_bytes(U, c, T)
@@ -666,15 +707,18 @@ def main():
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_bytes(best)},
         "kernel": kname,
         "kernel_us": k_avg_s * 1e6,
-        "kernel_us_p10_p90": [float(np.percentile(k_ms, 10) * 1e3),
-                              float(np.percentile(k_ms, 90) * 1e3)],
+        "kernel_us_launch_events": statistics.mean(k_ms) * 1e3,
+        "kernel_us_launch_events_p10_p90": [float(np.percentile(k_ms, 10) * 1e3),
+                                            float(np.percentile(k_ms, 90) * 1e3)],
         "bytes_per_launch": nbytes,
         "mean_union_rows": float(U.mean()),
         "ms_per_step_by_path": {p: res[p][0] for p in res},
         "kernel_us_by_path": {p: statistics.mean(res[p][1]) * 1e3 for p in res},
         "ms_per_step_with_kernel_events": {p: res[p][2] for p in res},
-        "timing": "value, ms_per_step: K bare steps between two synchronizations; kernel_us: "
-                  "HIP events around each decode launch, on its stream, over K more steps",
+        "timing": "value, ms_per_step: K bare steps between two synchronizations; kernel_us "
+                  "(roofline.achieved): the decode launch alone, K times back to back on its "
+                  "stream between two HIP events; kernel_us_launch_events: HIP events around "
+                  "each decode launch over K more steps (each pair adds ~6 us of its own)",
     }
     del kp, v, cache, ws
     torch.cuda.empty_cache()
