@@ -56,6 +56,38 @@ def test_decode_bf16_shapes(Hq, Hkv, T, k, d):
     assert_close(r["out"].cpu().double().numpy(), ref, "bf16", f"decode {Hq},{Hkv},{T}")
 
 
+@pytest.mark.parametrize("T,far", [(3000, "early"), (3000, "late"), (9000, "early"),
+                                   (9000, "late"), (40000, "early")])
+def test_decode_far_apart_maxima(T, far):
+    """Partials whose maxima lie ~24 log2 units apart: every query gets a common component 6u
+    (u a seeded unit vector) and the keys of one half of the context are -33u, so that half's
+    scores sit near -22 (log2 units) against ~2 elsewhere.  The merge of the splits (or of the
+    short kernel's 256-token workgroups) must weigh the far half by ~2^-24, not drop or
+    overflow it."""
+    c = config(2, B=2, Hq=8, Hkv=2, T=T, k=96)
+    inp = make_decode_inputs(c)
+    u = np.random.default_rng(2025).standard_normal(c["d"])
+    u = torch.from_numpy(u / np.linalg.norm(u))
+    dt = inp["q"].dtype
+    inp["q"] = (inp["q"].double() + 6.0 * u).to(dt)
+    k = inp["k"].double()
+    half = slice(0, T // 2) if far == "early" else slice(T // 2, T)
+    k[:, :, half] = -33.0 * u
+    inp["k"] = k.to(dt)
+    r = run_decode(inp, c)
+    m = _check_masks(r, c)
+    # the two halves' maxima are far apart (oracle arithmetic, head 0)
+    P64 = storage_to_f64(inp["P"])
+    Kp = O.project_keys_stored(storage_to_f64(inp["k"][0, 0]), P64, c["dtype"], c["d"])
+    qp = O.project(storage_to_f64(inp["q"][0, 0]), P64)
+    sc = (np.where(m[0, 0], qp, 0) @ Kp.T) / math.sqrt(c["d"]) / math.log(2)
+    far_max = sc[half].max()
+    near_max = np.delete(sc, np.arange(T)[half]).max()
+    assert near_max - far_max > 16
+    ref = oracle_decode(inp, c, m)
+    assert_close(r["out"].cpu().double().numpy(), ref, "bf16", f"far maxima {T},{far}")
+
+
 @pytest.mark.parametrize("T,d_store,k", [
     (3000, 96, 64),    # short-context kernel
     (3000, 64, 48),
