@@ -74,6 +74,9 @@ __device__ __forceinline__ float coherent_load(const float *p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
+template <int G>
+constexpr int kDecodeWaves = G == 8 ? 2 : G == 4 ? 8 : 4;
+
 template <typename KT, int D, int G, int NW, bool FUSED>
 struct DecodeSmem {
   static constexpr int TPL = Vec<KT>::N;
@@ -397,8 +400,12 @@ __device__ __forceinline__ void progress_priority(int done, int total) {
   else __builtin_amdgcn_s_setprio(0);
 }
 
-// Two workgroups per CU must stay resident (the decode streams at full bandwidth only then):
-// at least two waves per SIMD, i.e. at most 256 VGPRs.
+// At least two waves per SIMD must stay resident (the decode streams at full bandwidth only
+// then): at most 256 VGPRs.  Wavefronts per workgroup by group size (kDecodeWaves): 8 for G = 4,
+// one 512-thread workgroup per CU whose wavefronts are all of one age (with two 4-wavefront
+// workgroups per CU, the second one resident ran ~4 us behind the first; 8 measured 1 us faster
+// on the decode step), 2 for G = 8 (its LDS numerators are twice as large per wavefront), 4
+// otherwise.
 template <typename KT, int D, int G, int NW, bool FUSED>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_kernel(DecodeArgs a) {
@@ -1055,7 +1062,7 @@ hipError_t launch_short(const DecodeArgs &a, const H2OArgs &h, hipStream_t s) {
 
 template <typename KT, int D, int G, bool FUSED>
 hipError_t launch_g(const DecodeArgs &a, hipStream_t s) {
-  constexpr int NW = (G == 8) ? 2 : 4;
+  constexpr int NW = kDecodeWaves<G>;
   const dim3 grid(a.B * a.Hkv * a.S), block(NW * 64);
   decode_kernel<KT, D, G, NW, FUSED><<<grid, block, 0, s>>>(a);
   return hipGetLastError();
@@ -1077,7 +1084,7 @@ inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255);
 
 DecodeLayout decode_layout(int dtype, int G) {
   DecodeLayout L;
-  L.waves = (G == 8) ? 2 : 4;
+  L.waves = G == 8 ? kDecodeWaves<8> : G == 4 ? kDecodeWaves<4> : kDecodeWaves<1>;
   L.tokens_wave = 64 * (dtype == 1 ? 8 : 4);
   L.split = L.waves * L.tokens_wave;
   return L;

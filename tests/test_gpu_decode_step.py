@@ -99,7 +99,7 @@ def test_step_equals_separate_calls(T):
 @pytest.mark.parametrize("T0", [2045, 4093])
 def test_step_sequence_appends(T0):
     """Several steps in a row on one cache and workspace: each appends and attends correctly
-    (across a 256-token chunk and 2048-token split boundary, and across the switch from the
+    (across a 256-token chunk boundary of the short kernel, and across the switch from the
     short kernel to the split-T kernel after 4096 tokens)."""
     c = config(2, B=2, Hq=8, Hkv=2, T=T0 + 8)
     inp = make_decode_inputs(c)
@@ -146,7 +146,7 @@ def test_step_mass_mode():
 
 @pytest.mark.parametrize("k", [96, 32])
 def test_step_long_context_sampled(k):
-    """B=1, T=131072 (64 splits per KV group; the new token lands in the last one), with a spare
+    """B=1, T=131072 (32 splits per KV group; the new token lands in the last one), with a spare
     capacity of 256 tokens; every mask checked, sampled heads against the oracle."""
     c = config(3, k=k)
     T, d = c["T"], c["d"]
