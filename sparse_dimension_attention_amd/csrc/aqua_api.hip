@@ -157,7 +157,7 @@ aqua_status aqua_decode(const aqua_cache *c, int32_t Hq, const float *q_proj,
   a.d_store = c->d_store;
   a.T_cap = c->T_cap;
   a.len = c->len;
-  a.S = aqua::decode_splits(c->dtype, Hq / c->Hkv, c->len);
+  a.S = aqua::decode_splits(c->dtype, Hq / c->Hkv, c->B * c->Hkv, c->len);
   a.qscale = scale * 1.4426950408889634f;  // log2(e): scores are kept in log2 units
   return hip_status(aqua::launch_decode(c->dtype, a, static_cast<hipStream_t>(stream)),
                     "aqua_decode launch");
@@ -202,7 +202,7 @@ aqua_status aqua_decode_step(aqua_cache *c, int32_t Hq, const void *q, const voi
   a.d_store = c->d_store;
   a.T_cap = c->T_cap;
   a.len = c->len + 1;
-  a.S = aqua::decode_splits(c->dtype, Hq / c->Hkv, a.len);
+  a.S = aqua::decode_splits(c->dtype, Hq / c->Hkv, c->B * c->Hkv, a.len);
   a.qscale = scale * 1.4426950408889634f;
   a.q_raw = q;
   a.k_new = k_new;
@@ -318,7 +318,7 @@ aqua_status aqua_h2o_step(aqua_cache *c, int32_t Hq, const void *q, const void *
   a.d_store = c->d_store;
   a.T_cap = c->T_cap;
   a.len = c->len;
-  a.S = aqua::decode_splits(c->dtype, Hq / c->Hkv, c->len);
+  a.S = aqua::decode_splits(c->dtype, Hq / c->Hkv, c->B * c->Hkv, c->len);
   a.qscale = scale * 1.4426950408889634f;
   a.q_raw = q;
   a.k_new = k_new;

@@ -218,13 +218,15 @@ struct DecodeLayout {
   int split;        // tokens per workgroup (= waves * tokens_wave)
 };
 
-// Launch geometry of the decode kernel for a storage dtype (0 f32, 1 bf16) and group size.
-DecodeLayout decode_layout(int dtype, int G);
+// Launch geometry of the split-T decode kernel for a storage dtype (0 f32, 1 bf16), group size
+// G, groups = B * Hkv (0: the finest layout, the most splits) and context length len.
+DecodeLayout decode_layout(int dtype, int G, int groups, int len);
 // aqua_decode takes the short-context kernel (workgroups of 256 tokens that split the union of
 // K' rows over their wavefronts) up to this many tokens, the split-T kernel above it.
 constexpr int kDecodeShortMax = 4096;
 bool decode_short(int len);
-int decode_splits(int dtype, int G, int len);  // partials per head that aqua_decode writes
+// partials per head that aqua_decode writes (groups = B * Hkv)
+int decode_splits(int dtype, int G, int groups, int len);
 size_t decode_workspace_bytes(int dtype, int B, int Hq, int Hkv, int d, int T_cap);
 void decode_workspace_carve(void *ws, int dtype, int B, int Hq, int Hkv, int d, int T_cap,
                             DecodeArgs &a);

@@ -74,9 +74,6 @@ __device__ __forceinline__ float coherent_load(const float *p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
-template <int G>
-constexpr int kDecodeWaves = G == 8 ? 2 : G == 4 ? 8 : 4;
-
 template <typename KT, int D, int G, int NW, bool FUSED>
 struct DecodeSmem {
   static constexpr int TPL = Vec<KT>::N;
@@ -401,11 +398,12 @@ __device__ __forceinline__ void progress_priority(int done, int total) {
 }
 
 // At least two waves per SIMD must stay resident (the decode streams at full bandwidth only
-// then): at most 256 VGPRs.  Wavefronts per workgroup by group size (kDecodeWaves): 8 for G = 4,
-// one 512-thread workgroup per CU whose wavefronts are all of one age (with two 4-wavefront
-// workgroups per CU, the second one resident ran ~4 us behind the first; 8 measured 1 us faster
-// on the decode step), 2 for G = 8 (its LDS numerators are twice as large per wavefront), 4
-// otherwise.
+// then): at most 256 VGPRs.  Wavefronts per workgroup (decode_layout): 2 for G = 8 (its LDS
+// numerators are twice as large per wavefront), 4 otherwise; for G = 4, 8 when that still gives
+// at least one workgroup per CU: one 512-thread workgroup per CU, whose wavefronts are all of one
+// age (with two 4-wavefront workgroups per CU the second one resident ran ~4 us behind the first;
+// 8 measured 1 us faster on the 16 x 8-group, 8192-token decode, but halves the grid, and a
+// 32-workgroup grid at 16384 tokens and batch 1 ran 48 against 35 us).
 template <typename KT, int D, int G, int NW, bool FUSED>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_kernel(DecodeArgs a) {
@@ -1062,9 +1060,17 @@ hipError_t launch_short(const DecodeArgs &a, const H2OArgs &h, hipStream_t s) {
 
 template <typename KT, int D, int G, bool FUSED>
 hipError_t launch_g(const DecodeArgs &a, hipStream_t s) {
-  constexpr int NW = kDecodeWaves<G>;
-  const dim3 grid(a.B * a.Hkv * a.S), block(NW * 64);
-  decode_kernel<KT, D, G, NW, FUSED><<<grid, block, 0, s>>>(a);
+  const DecodeLayout L = decode_layout(sizeof(KT) == 2 ? 1 : 0, G, a.B * a.Hkv, a.len);
+  if (a.S != (a.len + L.split - 1) / L.split) return hipErrorInvalidConfiguration;
+  const dim3 grid(a.B * a.Hkv * a.S);
+  if constexpr (G == 4) {
+    if (L.waves == 8) {
+      decode_kernel<KT, D, G, 8, FUSED><<<grid, dim3(512), 0, s>>>(a);
+      return hipGetLastError();
+    }
+  }
+  constexpr int NW = G == 8 ? 2 : 4;
+  decode_kernel<KT, D, G, NW, FUSED><<<grid, dim3(NW * 64), 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -1082,26 +1088,31 @@ inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255);
 
 }  // namespace
 
-DecodeLayout decode_layout(int dtype, int G) {
+DecodeLayout decode_layout(int dtype, int G, int groups, int len) {
+  constexpr long kCUs = 256;  // MI355X
   DecodeLayout L;
-  L.waves = G == 8 ? kDecodeWaves<8> : G == 4 ? kDecodeWaves<4> : kDecodeWaves<1>;
   L.tokens_wave = 64 * (dtype == 1 ? 8 : 4);
+  L.waves = G == 8 ? 2 : 4;
+  if (G == 4) {
+    const long wide_splits = (static_cast<long>(len) + 8 * L.tokens_wave - 1) / (8 * L.tokens_wave);
+    if (static_cast<long>(groups) * wide_splits >= kCUs) L.waves = 8;
+  }
   L.split = L.waves * L.tokens_wave;
   return L;
 }
 
 bool decode_short(int len) { return len <= kDecodeShortMax; }
 
-int decode_splits(int dtype, int G, int len) {
+int decode_splits(int dtype, int G, int groups, int len) {
   if (decode_short(len)) return (len + kShortChunk - 1) / kShortChunk;
-  const DecodeLayout L = decode_layout(dtype, G);
+  const DecodeLayout L = decode_layout(dtype, G, groups, len);
   return (len + L.split - 1) / L.split;
 }
 
 namespace {
 // partials per head: enough for any len <= T_cap in either layout
 size_t partial_slots(int dtype, int G, int T_cap) {
-  const DecodeLayout L = decode_layout(dtype, G);
+  const DecodeLayout L = decode_layout(dtype, G, 0, T_cap);  // the finest layout: most splits
   const size_t s_long = (static_cast<size_t>(T_cap) + L.split - 1) / L.split;
   const int short_len = T_cap < kDecodeShortMax ? T_cap : kDecodeShortMax;
   const size_t s_short = (static_cast<size_t>(short_len) + kShortChunk - 1) / kShortChunk;
@@ -1151,7 +1162,7 @@ hipError_t launch_decode(int dtype, const DecodeArgs &a, hipStream_t s) {
   return a.d == 128 ? launch_d<float, 128, false>(a, s) : launch_d<float, 64, false>(a, s);
 }
 
-// a.S must be decode_splits(dtype, G, a.len): the short kernel's chunk count at short lengths
+// a.S must be decode_splits(dtype, G, B * Hkv, a.len): the short kernel's chunk count at short lengths
 hipError_t launch_decode_step(int dtype, const DecodeArgs &a, hipStream_t s) {
   if (decode_short(a.len)) return launch_short_mode<kShortStep>(dtype, a, H2OArgs{}, s);
   if (dtype == 1)

@@ -44,8 +44,9 @@ def test_tiny_decode_f32():
     (16, 2, 4500, 32, 128),    # G=8
     (4, 1, 4300, 40, 64),      # d = 64
     # past 16 splits per group the merge takes two levels (runs of 8 splits; the last run ragged)
-    (8, 2, 40000, 96, 128),    # G=4: 10 splits of 4096, one level
-    (8, 2, 70000, 96, 128),    # G=4: 18 splits of 4096
+    # (B2 x 2 groups is a small grid: 4-wavefront workgroups, splits of 2048)
+    (8, 2, 40000, 96, 128),    # G=4: 20 splits of 2048
+    (8, 2, 70000, 96, 128),    # G=4: 35 splits of 2048
     (16, 2, 20000, 32, 128),   # G=8: 20 splits of 1024
 ])
 def test_decode_bf16_shapes(Hq, Hkv, T, k, d):
@@ -94,7 +95,7 @@ def test_decode_far_apart_maxima(T, far):
     (3000, 64, 48),
     (9000, 96, 64),    # split-T kernel
     (9000, 64, 48),
-    (70000, 64, 48),   # two-level merge (18 splits of 4096)
+    (70000, 64, 48),   # two-level merge (35 splits of 2048)
 ])
 def test_decode_memory_cut(T, d_store, k):
     """AQUA-Memory's static cut at the decode shape: only K' dims [0, d_store) are stored and each
@@ -216,7 +217,7 @@ def test_decode_long_context_sampled(k, long_inputs):
 @pytest.mark.parametrize("T", [3000, 40000, 70000])
 def test_decode_mass_accumulation(T):
     """Mass mode: mass[t] grows by the sum over the group's heads of the softmax weights (short
-    kernel at 3000 tokens; split-T kernel at 40000, with the two-level merge at 70000)."""
+    kernel at 3000 tokens; split-T kernel with the two-level merge at 40000 and 70000)."""
     c = config(2, B=2, Hq=8, Hkv=2, T=T, d_store=96, d_sel=96, k=64)
     inp = make_decode_inputs(c)
     T_cap = (T + 8 + 63) // 64 * 64
