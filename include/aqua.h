@@ -22,7 +22,10 @@
  *  - Calls are thread-safe; ordering between calls comes only from the stream.
  *  - Floating point: storage of K' and V is fp32 or bf16 (round to nearest even, once); all
  *    arithmetic is fp32 except the prefill contractions, which use bf16 operands (masked q' and
- *    softmax weights, rounded to nearest even) with fp32 accumulation.
+ *    softmax weights, rounded to nearest even) with fp32 accumulation.  Projections (q' and K')
+ *    of bf16 inputs run on bf16 MFMA against an exact three-part bf16 split of the fp32 P (every
+ *    product exact, fp32 accumulation) in one fixed order of operations, so a row's q' or K' is
+ *    the same bits in every call that computes it; fp32 inputs are projected with fp32 fmas.
  */
 #ifndef AQUA_H
 #define AQUA_H
@@ -95,9 +98,11 @@ aqua_status aqua_select_dims(const void *q, int32_t qdt, int32_t N, int32_t d, c
                              int16_t *idx, void *stream);
 
 /* Bytes of workspace aqua_decode needs for this cache shape and Hq query heads (any len up to
- * T_cap).  The workspace must be zero-filled before its first use; every completed call leaves
- * it zero-filled again, so it can be reused without clearing.  Calls sharing a workspace must
- * not run concurrently. */
+ * T_cap).  The workspace needs no initialisation and no clearing between calls, whatever it holds
+ * (its cross-workgroup counters are tagged with a per-call sequence number, so the words of an
+ * earlier call, of an interrupted one, of another shape, or garbage, are never taken for this
+ * call's).  Calls sharing a workspace must not run concurrently (ordering on one stream is
+ * enough). */
 aqua_status aqua_decode_workspace(const aqua_cache *c, int32_t Hq, size_t *bytes);
 
 /* GQA decode attention over the selected dimensions (digest, 技术框架: attention computed on
@@ -126,7 +131,7 @@ aqua_status aqua_decode(const aqua_cache *c, int32_t Hq, const float *q_proj,
  *   k_new, v_new: device [B][Hkv][d_head], c->dtype (the new token's raw key and value); its K'
  *           and V are written at column len, then c->len += 1 (AQUA_ERR_CAPACITY if full).
  *   P     : device [d_head][d_head] fp32.   1 <= k <= d_sel <= d_store.
- *   mass, out, ws, ws_bytes: as aqua_decode (same workspace size, same zero-fill contract).
+ *   mass, out, ws, ws_bytes: as aqua_decode (the same workspace size; no clearing needed).
  *   q_proj_out, mask_out: NULL, or out device [B][Hq][d_head] fp32 and [B][Hq][d_head/32]
  *           uint32 (the q' and masks used, as aqua_select_dims would write them). */
 aqua_status aqua_decode_step(aqua_cache *c, int32_t Hq, const void *q, const void *k_new,
@@ -145,15 +150,31 @@ aqua_status aqua_prefill_workspace(const aqua_cache *c, int32_t Hq, int32_t Lq, 
  *   q_proj_out, mask_out: NULL, or out device [B][Hq][Lq][d_head] fp32 and
  *           [B][Hq][Lq][d_head/32] uint32 (the q' and masks used).
  *   ws    : workspace of at least aqua_prefill_workspace() bytes.
- * q' is computed at fp32 accuracy (bf16 MFMA on an exact three-part bf16 split of P), so it can
- * differ from aqua_select_dims' q' in the last bits; the mask is always the exact top-k of the
- * q' written to q_proj_out.
+ * q' is the one aqua_select_dims computes for the same bf16 rows (bit for bit); the mask is
+ * always the exact top-k of the q' written to q_proj_out.
  * Requires d_head == 128, bf16 storage, d_store % 16 == 0, T_cap <= 4194304, d_sel <= d_store,
  * Lq >= 1, pos0 >= 0. */
 aqua_status aqua_prefill_chunk(const aqua_cache *c, int32_t Hq, const void *q, int32_t Lq,
                                int32_t pos0, const float *P, int32_t d_sel, int32_t k,
                                float scale, float *out, float *q_proj_out, uint32_t *mask_out,
                                void *ws, size_t ws_bytes, void *stream);
+
+/* The starting state of an H2O compact cache (H2O combined with AQUA: abstract; blog "Key
+ * Advantages"): for each (b, g), the `heavy` positions of largest mass among the positions older
+ * than the recent window, [0, full->len - recent), ranked by (mass descending, position
+ * ascending), in ascending position order in slots 0 .. heavy-1, then the recent positions
+ * [full->len - recent, full->len) in slots heavy .. heavy+recent-1.  Each slot's K' column, V row
+ * and mass are copied from the full cache.
+ *   full     : the full-context cache (read only), full->len tokens.
+ *   mass_full: device fp32 [B][Hkv][full->T_cap], each >= +0 (the cumulative attention so far).
+ *   compact  : B, Hkv, d_head, d_store and dtype as full; T_cap == len == heavy + recent.
+ *   mass     : out device fp32 [B][Hkv][heavy + recent].
+ *   slot_pos : out device int32 [B][Hkv][heavy + recent] (the position each slot holds).
+ * Requires heavy, recent >= 0, heavy + recent >= 1, heavy + recent <= full->len.  The buffers of
+ * the compact state must not overlap the full cache. */
+aqua_status aqua_h2o_init(const aqua_cache *full, const float *mass_full, int32_t heavy,
+                          int32_t recent, aqua_cache *compact, float *mass, int32_t *slot_pos,
+                          void *stream);
 
 /* H2O eviction for a compact cache of n_slots slots per (b, g) (H2O combined with AQUA:
  * abstract; blog "Key Advantages").  Among the slots holding a position <= t_new - recent
@@ -164,7 +185,8 @@ aqua_status aqua_prefill_chunk(const aqua_cache *c, int32_t Hq, const void *q, i
  * victim is -1 and nothing else changes.
  *   mass    : device fp32 [B][Hkv][n_slots] (read and written).
  *   slot_pos: device int32 [B][Hkv][n_slots] (read and written).
- *   victim  : out device int32 [B][Hkv]. */
+ *   victim  : out device int32 [B][Hkv].
+ * All three 16-byte aligned. */
 aqua_status aqua_h2o_victim(float *mass, int32_t *slot_pos, int32_t B, int32_t Hkv,
                             int32_t n_slots, int32_t t_new, int32_t recent, int32_t *victim,
                             void *stream);

@@ -26,7 +26,7 @@ _STATUS_NAMES = {0: "AQUA_OK", 1: "AQUA_ERR_NULL", 2: "AQUA_ERR_SHAPE", 3: "AQUA
 
 EXPORTS = ("aqua_version", "aqua_last_error", "aqua_project_keys", "aqua_select_dims",
            "aqua_decode_workspace", "aqua_decode", "aqua_decode_step", "aqua_prefill_workspace",
-           "aqua_prefill_chunk", "aqua_h2o_victim", "aqua_h2o_step")
+           "aqua_prefill_chunk", "aqua_h2o_init", "aqua_h2o_victim", "aqua_h2o_step")
 
 
 class AquaError(RuntimeError):
@@ -66,6 +66,7 @@ def load_library() -> ctypes.CDLL:
         "aqua_prefill_workspace": ([cp, I32, I32, ctypes.POINTER(SZ)], ctypes.c_int),
         "aqua_prefill_chunk": ([cp, I32, P, I32, I32, P, I32, I32, ctypes.c_float, P, P, P, P,
                                 SZ, P], ctypes.c_int),
+        "aqua_h2o_init": ([cp, P, I32, I32, cp, P, P, P], ctypes.c_int),
         "aqua_h2o_victim": ([P, P, I32, I32, I32, I32, I32, P, P], ctypes.c_int),
         "aqua_h2o_step": ([cp, I32, P, P, P, P, I32, I32, ctypes.c_float, P, P, I32, I32, P, P, P,
                            P, P, SZ, P], ctypes.c_int),
@@ -171,6 +172,13 @@ def aqua_prefill_chunk(cache: aqua_cache, Hq: int, q, Lq: int, pos0: int, P, d_s
                                              int(pos0), _ptr(P), int(d_sel), int(k), float(scale),
                                              _ptr(out), _ptr(q_proj_out), _ptr(mask_out),
                                              _ptr(ws), nbytes, _stream(stream)))
+
+
+def aqua_h2o_init(full: aqua_cache, mass_full, heavy: int, recent: int, compact: aqua_cache,
+                  mass, slot_pos, stream=None):
+    _check(load_library().aqua_h2o_init(ctypes.byref(full), _ptr(mass_full), int(heavy),
+                                        int(recent), ctypes.byref(compact), _ptr(mass),
+                                        _ptr(slot_pos), _stream(stream)))
 
 
 def aqua_h2o_victim(mass, slot_pos, t_new: int, recent: int, victim, stream=None):

@@ -69,11 +69,31 @@ aqua_status check_prefill_cache(const aqua_cache *c, int32_t Hq) {
   return AQUA_OK;
 }
 
+// The cache and workspace fields every decode-path launch takes; S and epoch for this call.
+void fill_decode_args(const aqua_cache *c, int32_t Hq, int32_t len, float scale, float *mass,
+                      float *out, void *ws, aqua::DecodeArgs &a) {
+  a.kp = c->kp;
+  a.v = c->v;
+  a.mass = mass;
+  a.out = out;
+  aqua::decode_workspace_carve(ws, c->dtype, c->B, Hq, c->Hkv, c->d_head, c->T_cap, a);
+  a.B = c->B;
+  a.Hq = Hq;
+  a.Hkv = c->Hkv;
+  a.d = c->d_head;
+  a.d_store = c->d_store;
+  a.T_cap = c->T_cap;
+  a.len = len;
+  a.S = aqua::decode_splits(c->dtype, Hq / c->Hkv, c->B * c->Hkv, len, aqua::device_cu_count());
+  a.qscale = scale * 1.4426950408889634f;  // log2(e): scores are kept in log2 units
+  a.epoch = aqua::next_epoch();
+}
+
 }  // namespace
 
 extern "C" {
 
-const char *aqua_version(void) { return "libaqua 0.1.0 (gfx950)"; }
+const char *aqua_version(void) { return "libaqua 0.2.0 (gfx950)"; }
 
 const char *aqua_last_error(void) { return g_err; }
 
@@ -143,22 +163,9 @@ aqua_status aqua_decode(const aqua_cache *c, int32_t Hq, const float *q_proj,
     return fail(AQUA_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, need);
 
   aqua::DecodeArgs a{};
-  a.kp = c->kp;
-  a.v = c->v;
+  fill_decode_args(c, Hq, c->len, scale, mass, out, ws, a);
   a.q_proj = q_proj;
   a.mask = mask;
-  a.mass = mass;
-  a.out = out;
-  aqua::decode_workspace_carve(ws, c->dtype, c->B, Hq, c->Hkv, c->d_head, c->T_cap, a);
-  a.B = c->B;
-  a.Hq = Hq;
-  a.Hkv = c->Hkv;
-  a.d = c->d_head;
-  a.d_store = c->d_store;
-  a.T_cap = c->T_cap;
-  a.len = c->len;
-  a.S = aqua::decode_splits(c->dtype, Hq / c->Hkv, c->B * c->Hkv, c->len);
-  a.qscale = scale * 1.4426950408889634f;  // log2(e): scores are kept in log2 units
   return hip_status(aqua::launch_decode(c->dtype, a, static_cast<hipStream_t>(stream)),
                     "aqua_decode launch");
 }
@@ -188,22 +195,9 @@ aqua_status aqua_decode_step(aqua_cache *c, int32_t Hq, const void *q, const voi
     return fail(AQUA_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, need);
 
   aqua::DecodeArgs a{};
-  a.kp = c->kp;
-  a.v = c->v;
+  fill_decode_args(c, Hq, c->len + 1, scale, mass, out, ws, a);
   a.kp_w = c->kp;
   a.v_w = c->v;
-  a.mass = mass;
-  a.out = out;
-  aqua::decode_workspace_carve(ws, c->dtype, c->B, Hq, c->Hkv, c->d_head, c->T_cap, a);
-  a.B = c->B;
-  a.Hq = Hq;
-  a.Hkv = c->Hkv;
-  a.d = c->d_head;
-  a.d_store = c->d_store;
-  a.T_cap = c->T_cap;
-  a.len = c->len + 1;
-  a.S = aqua::decode_splits(c->dtype, Hq / c->Hkv, c->B * c->Hkv, a.len);
-  a.qscale = scale * 1.4426950408889634f;
   a.q_raw = q;
   a.k_new = k_new;
   a.v_new = v_new;
@@ -265,12 +259,12 @@ aqua_status aqua_h2o_victim(float *mass, int32_t *slot_pos, int32_t B, int32_t H
     return fail(AQUA_ERR_SHAPE, "B=%d, Hkv=%d, n_slots=%d must be >= 1", B, Hkv, n_slots);
   if (recent < 0 || t_new < 0)
     return fail(AQUA_ERR_SHAPE, "t_new=%d and recent=%d must be >= 0", t_new, recent);
+  if (!aligned16(mass) || !aligned16(slot_pos) || !aligned16(victim))
+    return fail(AQUA_ERR_ALIGN, "mass, slot_pos and victim must be 16-byte aligned");
   return hip_status(aqua::launch_h2o_victim(mass, slot_pos, B, Hkv, n_slots, t_new, recent,
                                             victim, static_cast<hipStream_t>(stream)),
                     "aqua_h2o_victim launch");
 }
-
-}  // extern "C"
 
 aqua_status aqua_h2o_step(aqua_cache *c, int32_t Hq, const void *q, const void *k_new,
                           const void *v_new, const float *P, int32_t d_sel, int32_t k,
@@ -304,22 +298,9 @@ aqua_status aqua_h2o_step(aqua_cache *c, int32_t Hq, const void *q, const void *
     return fail(AQUA_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, need);
 
   aqua::DecodeArgs a{};
-  a.kp = c->kp;
-  a.v = c->v;
+  fill_decode_args(c, Hq, c->len, scale, mass, out, ws, a);
   a.kp_w = c->kp;
   a.v_w = c->v;
-  a.mass = mass;
-  a.out = out;
-  aqua::decode_workspace_carve(ws, c->dtype, c->B, Hq, c->Hkv, c->d_head, c->T_cap, a);
-  a.B = c->B;
-  a.Hq = Hq;
-  a.Hkv = c->Hkv;
-  a.d = c->d_head;
-  a.d_store = c->d_store;
-  a.T_cap = c->T_cap;
-  a.len = c->len;
-  a.S = aqua::decode_splits(c->dtype, Hq / c->Hkv, c->B * c->Hkv, c->len);
-  a.qscale = scale * 1.4426950408889634f;
   a.q_raw = q;
   a.k_new = k_new;
   a.v_new = v_new;
@@ -336,3 +317,35 @@ aqua_status aqua_h2o_step(aqua_cache *c, int32_t Hq, const void *q, const void *
   return hip_status(aqua::launch_h2o_step(c->dtype, a, h, static_cast<hipStream_t>(stream)),
                     "aqua_h2o_step launch");
 }
+
+aqua_status aqua_h2o_init(const aqua_cache *full, const float *mass_full, int32_t heavy,
+                          int32_t recent, aqua_cache *compact, float *mass, int32_t *slot_pos,
+                          void *stream) {
+  g_err[0] = 0;
+  if (aqua_status st = check_cache(full)) return st;
+  if (aqua_status st = check_cache(compact)) return st;
+  if (!mass_full || !mass || !slot_pos)
+    return fail(AQUA_ERR_NULL, "mass_full, mass and slot_pos are required");
+  if (compact->B != full->B || compact->Hkv != full->Hkv || compact->d_head != full->d_head ||
+      compact->d_store != full->d_store || compact->dtype != full->dtype)
+    return fail(AQUA_ERR_SHAPE, "the compact cache must have the full cache's B, Hkv, d_head, "
+                "d_store and dtype");
+  if (heavy < 0 || recent < 0 || static_cast<int64_t>(heavy) + recent < 1)
+    return fail(AQUA_ERR_SHAPE, "heavy=%d and recent=%d must be >= 0 with a positive sum", heavy,
+                recent);
+  if (compact->T_cap != heavy + recent || compact->len != compact->T_cap)
+    return fail(AQUA_ERR_SHAPE, "the compact cache needs T_cap == len == heavy + recent = %d "
+                "(T_cap=%d, len=%d)", heavy + recent, compact->T_cap, compact->len);
+  if (static_cast<int64_t>(heavy) + recent > full->len)
+    return fail(AQUA_ERR_CAPACITY, "heavy + recent = %d exceeds the cached len %d",
+                heavy + recent, full->len);
+  if (!aligned16(mass_full) || !aligned16(mass) || !aligned16(slot_pos))
+    return fail(AQUA_ERR_ALIGN, "mass_full, mass and slot_pos must be 16-byte aligned");
+  return hip_status(aqua::launch_h2o_init(full->dtype, full->kp, full->v, mass_full, full->B,
+                                          full->Hkv, full->d_head, full->d_store, full->T_cap,
+                                          full->len, heavy, recent, compact->kp, compact->v,
+                                          mass, slot_pos, static_cast<hipStream_t>(stream)),
+                    "aqua_h2o_init launch");
+}
+
+}  // extern "C"

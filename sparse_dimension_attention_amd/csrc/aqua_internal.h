@@ -118,6 +118,86 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// ------------------------------------------------------------------ projection on MFMA
+// x' = x P for bf16 rows x at fp32 accuracy: every fp32 entry of P is the exact sum of three bf16
+// parts (RNE of P, of the remainder, of the remainder's remainder: 8 + 8 + 8 significand bits),
+// so every product of a bf16 x with a part is exact and only the fp32 accumulation rounds.
+// v_mfma_f32_16x16x32_bf16 lane layout: A lane l holds row l % 16, k = 8 (l / 16) + e (e = 0..7)
+// of a 32-wide k-step; B lane l holds column l % 16, the same k; D register r holds row
+// 4 (l / 16) + r, column l % 16.  Every bf16 projection in the library (queries before their
+// selection, keys before the cache, in every kernel) is this one sequence of operations, so a
+// row's x' does not depend on the kernel that computed it.
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void split3(float p, uint32_t &h, uint32_t &m, uint32_t &l) {
+  h = pack_bf16x2(p, 0.0f) & 0xffffu;
+  const float r1 = p - bf16_to_f32(static_cast<uint16_t>(h));
+  m = pack_bf16x2(r1, 0.0f) & 0xffffu;
+  const float r2 = r1 - bf16_to_f32(static_cast<uint16_t>(m));
+  l = pack_bf16x2(r2, 0.0f) & 0xffffu;
+}
+
+// The three parts of 16 columns of P [D][D] (D = 32 KS) as this lane's B operands.
+template <int KS> struct PParts {
+  u32x4_t h[KS], m[KS], l[KS];
+};
+
+// Columns col0 .. col0 + 15 of P; lane l takes column col0 + l % 16, rows 32 st + 8 (l / 16) + e.
+template <int KS>
+__device__ __forceinline__ void load_p_parts(const float *__restrict__ P, int col0,
+                                             PParts<KS> &pp) {
+  constexpr int D = 32 * KS;
+  const int lane = threadIdx.x & 63;
+  const float *pc = P + (8 * (lane >> 4)) * D + col0 + (lane & 15);
+  float v[KS][8];
+#pragma unroll
+  for (int st = 0; st < KS; ++st)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[st][e] = pc[(32 * st + e) * D];
+#pragma unroll
+  for (int st = 0; st < KS; ++st) {
+    uint32_t h[8], mi[8], lo[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) split3(v[st][e], h[e], mi[e], lo[e]);
+    pp.h[st] = u32x4_t{h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16, h[6] | h[7] << 16};
+    pp.m[st] = u32x4_t{mi[0] | mi[1] << 16, mi[2] | mi[3] << 16, mi[4] | mi[5] << 16,
+                       mi[6] | mi[7] << 16};
+    pp.l[st] = u32x4_t{lo[0] | lo[1] << 16, lo[2] | lo[3] << 16, lo[4] | lo[5] << 16,
+                       lo[6] | lo[7] << 16};
+  }
+}
+
+// This lane's A operand of one bf16 row x [32 KS]: x[32 st + 8 (lane / 16) .. + 7], st = 0..KS-1.
+template <int KS>
+__device__ __forceinline__ void load_a_row(const uint16_t *row, u32x4_t (&a)[KS]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int st = 0; st < KS; ++st)
+    a[st] = *reinterpret_cast<const u32x4_t *>(row + 32 * st + 8 * (lane >> 4));
+}
+
+// A 16 x 16 tile of x' = x P: 16 rows (A) by the 16 columns whose parts are pp.
+template <int KS>
+__device__ __forceinline__ f32x4_t proj_mfma(const u32x4_t (&a)[KS], const PParts<KS> &pp) {
+  f32x4_t acc_h = {0.0f, 0.0f, 0.0f, 0.0f}, acc_l = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int st = 0; st < KS; ++st) {
+    const bf16x8_t av = __builtin_bit_cast(bf16x8_t, a[st]);
+    acc_l = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, pp.l[st]),
+                                                    acc_l, 0, 0, 0);
+    acc_l = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, pp.m[st]),
+                                                    acc_l, 0, 0, 0);
+    acc_h = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, pp.h[st]),
+                                                    acc_h, 0, 0, 0);
+  }
+  f32x4_t r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = acc_h[i] + acc_l[i];
+  return r;
+}
+
 // ------------------------------------------------------------------ H2O eviction rule
 // Among the slots of one (b, g) holding a position <= limit (t_new - recent), the one ranked lowest
 // by (mass descending, position ascending): the minimum of the 64-bit key (mass bits,
@@ -185,9 +265,13 @@ struct DecodeArgs {
   const uint32_t *mask;  // [B][Hq][d/32]
   float *mass;           // [B][Hkv][T_cap] or nullptr
   float *out;            // [B][Hq][d]
-  uint32_t *counters;    // [B*Hkv], zero between calls
-  uint32_t *run_counters;  // [B*Hkv][run_stride]: per run of splits (two-level merge), zero
+  // Arrival counters of the cross-workgroup merge, each tagged with the call's epoch in its high
+  // 32 bits (arrive_last): a word left by another call, or garbage, is never taken for this
+  // call's count, so the workspace needs no clearing.
+  uint64_t *counters;      // [B*Hkv]
+  uint64_t *run_counters;  // [B*Hkv][run_stride]: per run of splits (two-level merge)
   int run_stride;
+  uint32_t epoch;        // nonzero, distinct for calls that may find each other's counters
   float *partials;       // [B][Hq][S][d+2]  (m, l, o[d]) in log2 units
   float *scores;         // [B][Hq][T_cap]   log2-domain scores (mass mode only)
   int B, Hq, Hkv, d, d_store, T_cap, len;
@@ -218,15 +302,25 @@ struct DecodeLayout {
   int split;        // tokens per workgroup (= waves * tokens_wave)
 };
 
+// Compute units of the current device (read once per device, then cached).
+int device_cu_count();
+// A fresh nonzero epoch for a call's arrival counters (process-wide sequence).
+uint32_t next_epoch();
+
 // Launch geometry of the split-T decode kernel for a storage dtype (0 f32, 1 bf16), group size
-// G, groups = B * Hkv (0: the finest layout, the most splits) and context length len.
-DecodeLayout decode_layout(int dtype, int G, int groups, int len);
+// G, groups = B * Hkv (0: the finest layout, the most splits), context length len and the
+// device's compute units.
+DecodeLayout decode_layout(int dtype, int G, int groups, int len, int cus);
 // aqua_decode takes the short-context kernel (workgroups of 256 tokens that split the union of
 // K' rows over their wavefronts) up to this many tokens, the split-T kernel above it.
 constexpr int kDecodeShortMax = 4096;
+constexpr int kShortChunk = 256;  // tokens per workgroup of the short-context kernel
+constexpr int kMergeFan = 8;      // splits per run of the two-level merge
+// forms of the short-context kernel: aqua_decode, aqua_decode_step, aqua_h2o_step
+enum ShortMode { kShortPlain = 0, kShortStep = 1, kShortH2O = 2 };
 bool decode_short(int len);
 // partials per head that aqua_decode writes (groups = B * Hkv)
-int decode_splits(int dtype, int G, int groups, int len);
+int decode_splits(int dtype, int G, int groups, int len, int cus);
 size_t decode_workspace_bytes(int dtype, int B, int Hq, int Hkv, int d, int T_cap);
 void decode_workspace_carve(void *ws, int dtype, int B, int Hq, int Hkv, int d, int T_cap,
                             DecodeArgs &a);
@@ -237,6 +331,14 @@ hipError_t launch_project_keys(int dtype, const void *k_raw, const void *v_raw, 
                                int B, int Hkv, int n, int d, int d_store, int T_cap, int len0,
                                const int32_t *slots, void *kp, void *v, hipStream_t s);
 hipError_t launch_decode(int dtype, const DecodeArgs &a, hipStream_t s);
+// the split-T kernel (per storage dtype, plain or fused) and the short-context kernel (mode:
+// 0 plain, 1 fused decode step, 2 fused H2O step), each in its own translation unit
+hipError_t launch_split_bf16(const DecodeArgs &a, const DecodeLayout &L, hipStream_t s);
+hipError_t launch_split_step_bf16(const DecodeArgs &a, const DecodeLayout &L, hipStream_t s);
+hipError_t launch_split_f32(const DecodeArgs &a, const DecodeLayout &L, bool fused,
+                            hipStream_t s);
+hipError_t launch_short_bf16(const DecodeArgs &a, const H2OArgs &h, int mode, hipStream_t s);
+hipError_t launch_short_f32(const DecodeArgs &a, const H2OArgs &h, int mode, hipStream_t s);
 hipError_t launch_decode_step(int dtype, const DecodeArgs &a, hipStream_t s);
 hipError_t launch_h2o_step(int dtype, const DecodeArgs &a, const H2OArgs &h, hipStream_t s);
 size_t prefill_workspace_bytes(int B, int Hq, int Lq);
@@ -246,5 +348,9 @@ hipError_t launch_prefill(const void *kp, const void *v, int B, int Hq, int Hkv,
                           void *ws, hipStream_t s);
 hipError_t launch_h2o_victim(float *mass, int32_t *slot_pos, int B, int Hkv, int n_slots,
                              int t_new, int recent, int32_t *victim, hipStream_t s);
+hipError_t launch_h2o_init(int dtype, const void *kp_full, const void *v_full,
+                           const float *mass_full, int B, int Hkv, int d, int d_store,
+                           int T_cap_full, int len, int heavy, int recent, void *kp, void *v,
+                           float *mass, int32_t *slot_pos, hipStream_t s);
 
 }  // namespace aqua

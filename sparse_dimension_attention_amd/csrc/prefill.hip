@@ -29,36 +29,20 @@
 namespace aqua {
 namespace {
 
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
 // ------------------------------------------------------------------ 1. selection
-// q' = q P on bf16 MFMA at fp32 accuracy: q is bf16, and every fp32 entry of P is the exact sum
-// of three bf16 parts (RNE of P, of the remainder, of the remainder's remainder: 8 + 8 + 8
-// significand bits), so q' = q P_hi + q P_mid + q P_lo with every product exact and fp32
-// accumulation.  A workgroup of 8 wavefronts walks blocks of 32 rows; wavefront w computes output
-// columns [16w, 16w + 16) on v_mfma_f32_16x16x32_bf16 (A lane l: row l % 16, k = 8 (l / 16) + e;
-// B lane l: column l % 16, same k; D register r: row 4 (l / 16) + r, column l % 16), its parts of
-// P held in registers, and writes its part of the q' tile to LDS; after one barrier each
-// wavefront selects 4 of the 32 rows (one row at a time, lane l holding dims l and l + 64).  The
+// q' = q P with the library's one bf16 projection (proj_mfma: v_mfma_f32_16x16x32_bf16 on P's
+// exact three-part bf16 split, fp32 accumulation; the q' of aqua_select_dims bit for bit).  A
+// workgroup of 8 wavefronts walks blocks of 32 rows; wavefront w computes output columns
+// [16w, 16w + 16), its parts of P held in registers, and writes its part of the q' tile to LDS;
+// after one barrier each wavefront selects 4 of the 32 rows (one row at a time, lane l holding
+// dims l and l + 64).  The
 // selection is a latency-bound chain of ballots and scalar steps per row, so the layout keeps
 // the registers low (16 columns' parts of P per wavefront) for four wavefronts per SIMD.
 constexpr int SQS = 128 + 8;  // LDS row stride (floats) of the q' tile
 constexpr int SEL_WAVES = 8;  // wavefronts per selection workgroup
 constexpr int SEL_ROWS_PER_WAVE = 32 / SEL_WAVES;
-
-typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
-
-__device__ __forceinline__ void split3(float p, uint32_t &h, uint32_t &m, uint32_t &l) {
-  const uint32_t hm = pack_bf16x2(p, 0.0f);
-  h = hm & 0xffffu;
-  const float r1 = p - bf16_to_f32(static_cast<uint16_t>(h));
-  m = pack_bf16x2(r1, 0.0f) & 0xffffu;
-  const float r2 = r1 - bf16_to_f32(static_cast<uint16_t>(m));
-  l = pack_bf16x2(r2, 0.0f) & 0xffffu;
-}
 
 __global__ __launch_bounds__(SEL_WAVES * 64) void prefill_select_kernel(
     const bf16_t *__restrict__ q, int N, const float *__restrict__ P, int d_sel, int k,
@@ -69,20 +53,8 @@ __global__ __launch_bounds__(SEL_WAVES * 64) void prefill_select_kernel(
   __shared__ __align__(16) bf16_t sM[SEL_WAVES * R * 128];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int col = 16 * w + (lane & 15);
-  // B operands: P[32 s + 8 (lane / 16) + e][col], e = 0..7, in three bf16 parts
-  u32x4_t bh[4], bm[4], bl[4];
-#pragma unroll
-  for (int st = 0; st < 4; ++st) {
-    uint32_t h[8], mi[8], lo[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      split3(P[(32 * st + 8 * (lane >> 4) + e) * 128 + col], h[e], mi[e], lo[e]);
-    bh[st] = u32x4_t{h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16, h[6] | h[7] << 16};
-    bm[st] = u32x4_t{mi[0] | mi[1] << 16, mi[2] | mi[3] << 16, mi[4] | mi[5] << 16,
-                     mi[6] | mi[7] << 16};
-    bl[st] = u32x4_t{lo[0] | lo[1] << 16, lo[2] | lo[3] << 16, lo[4] | lo[5] << 16,
-                     lo[6] | lo[7] << 16};
-  }
+  PParts<4> pp;  // B operands: P's three parts for output columns [16 w, 16 w + 16)
+  load_p_parts<4>(P, 16 * w, pp);
   const int nblk = (N + 31) / 32;
   bf16_t *qrows = sM + R * 128 * w;  // this wavefront's rows of qm, staged for 16-byte stores
   // A operands of a block (two halves of 16 rows); each block then loads the next one's before
@@ -90,12 +62,9 @@ __global__ __launch_bounds__(SEL_WAVES * 64) void prefill_select_kernel(
   u32x4_t av[2][4];
   auto load_rows = [&](int blk) {
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      const int arow = min(blk * 32 + 16 * hf + (lane & 15), N - 1);
-      const bf16_t *qa = q + static_cast<size_t>(arow) * 128 + 8 * (lane >> 4);
-#pragma unroll
-      for (int st = 0; st < 4; ++st) av[hf][st] = *reinterpret_cast<const u32x4_t *>(qa + 32 * st);
-    }
+    for (int hf = 0; hf < 2; ++hf)
+      load_a_row<4>(q + static_cast<size_t>(min(blk * 32 + 16 * hf + (lane & 15), N - 1)) * 128,
+                    av[hf]);
   };
   if (blockIdx.x < nblk) load_rows(blockIdx.x);
   int buf = 0;
@@ -105,20 +74,9 @@ __global__ __launch_bounds__(SEL_WAVES * 64) void prefill_select_kernel(
     float *tile = sQ[buf];
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
-      f32x4_t acc_h = {0.0f, 0.0f, 0.0f, 0.0f}, acc_l = {0.0f, 0.0f, 0.0f, 0.0f};
+      const f32x4_t x = proj_mfma<4>(av[hf], pp);
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, av[hf][st]);
-        acc_l = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, bl[st]),
-                                                        acc_l, 0, 0, 0);
-        acc_l = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, bm[st]),
-                                                        acc_l, 0, 0, 0);
-        acc_h = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, bh[st]),
-                                                        acc_h, 0, 0, 0);
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        tile[(16 * hf + 4 * (lane >> 4) + r) * SQS + col] = acc_h[r] + acc_l[r];
+      for (int r = 0; r < 4; ++r) tile[(16 * hf + 4 * (lane >> 4) + r) * SQS + col] = x[r];
     }
     if (blk + static_cast<int>(gridDim.x) < nblk) load_rows(blk + gridDim.x);
     lds_barrier();  // the next block's rows stay in flight through the selection

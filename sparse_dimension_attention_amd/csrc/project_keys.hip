@@ -3,11 +3,20 @@
 // AQUA Works", step 2).  Only dims 0..d_store-1 are kept (AQUA-Memory's static cut, blog section
 // "AQUA-Memory").  V is copied unchanged.
 //
-// One workgroup per tile of TT tokens of one (b, g).  The raw keys are staged in LDS as fp32;
-// thread (i, group) computes K'[t][i] = sum_j K[t][j] P[j][i] for its tokens (j ascending, fma),
-// reading P's row j coalesced across i and K[t][j..j+3] as an LDS broadcast.  The results are
-// rounded once to the storage type and transposed through LDS, so that each wavefront then
-// writes 64 consecutive token columns of one K' row.
+// bf16 keys take the library's one bf16 projection (proj_mfma: v_mfma_f32_16x16x32_bf16 on P's
+// exact three-part bf16 split, fp32 accumulation), so a key's K' is the same bits whichever
+// kernel projects it (this one, the fused decode step's, the fused H2O step's).  A workgroup of
+// 8 wavefronts walks tiles of 128 tokens of one (b, g): wavefront w keeps the parts of its 16
+// output dims in registers across the tiles, projects the tile's 16-token blocks, rounds to bf16
+// and transposes through LDS, so that each K' row then gets 128 consecutive tokens (256 bytes)
+// per tile, written 16 bytes per lane.  HBM-bound: 2 d bytes of K read, 2 d_store bytes of K'
+// and 4 d bytes of V moved per token.
+//
+// fp32 keys (the VALU path): tiles of 32 tokens staged in LDS as fp32; thread (i, group) computes
+// K'[t][i] = sum_j K[t][j] P[j][i] for its tokens (j ascending, fma), then the same transposed
+// write.
+#include <algorithm>
+
 #include "aqua_internal.h"
 
 namespace aqua {
@@ -145,22 +154,150 @@ __global__ __launch_bounds__(256) void project_keys_small_kernel(
   }
 }
 
+// ------------------------------------------------------------------ bf16: MFMA
+constexpr int kMT = 128;  // tokens per tile
+
+template <int D>
+__global__ __launch_bounds__(512) void project_keys_mfma_kernel(
+    const bf16_t *__restrict__ k_raw, const bf16_t *__restrict__ v_raw,
+    const float *__restrict__ P, int n, int d_store, int T_cap, int len0,
+    const int32_t *__restrict__ slots, bf16_t *__restrict__ kp, bf16_t *__restrict__ vc) {
+  constexpr int KS = D / 32, NB = D / 16;
+  constexpr int WPB = 8 / NB;  // wavefronts per column block (they split the token blocks)
+  constexpr int KROW = kMT + 8;  // LDS row stride (bf16) of the transposed tile
+  __shared__ __align__(16) bf16_t kt[D][KROW];
+  __shared__ int cols[kMT];
+  const int bg = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int blk = w % NB, tb0 = w / NB;
+  PParts<KS> pp;
+  load_p_parts<KS>(P, 16 * blk, pp);
+  const bf16_t *kb = k_raw + static_cast<size_t>(bg) * n * D;
+  const int ntiles = (n + kMT - 1) / kMT;
+  for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    const int t0 = tile * kMT, nt = min(kMT, n - t0);
+    if (tid < kMT) {
+      int col = -1;
+      if (tid < nt) col = slots ? slots[static_cast<size_t>(bg) * n + t0 + tid] : len0 + t0 + tid;
+      cols[tid] = (col >= 0 && col < T_cap) ? col : -1;
+    }
+    // K' of the tile: wavefront (blk, tb0) takes 16-token blocks tb0, tb0 + WPB, ...
+    for (int tb = tb0; tb < kMT / 16; tb += WPB) {
+      const int t = min(t0 + 16 * tb + (lane & 15), n - 1);  // rows past n repeat the last
+      u32x4_t av[KS];
+      load_a_row<KS>(kb + static_cast<size_t>(t) * D, av);
+      const f32x4_t x = proj_mfma<KS>(av, pp);
+      const uint32_t lo = pack_bf16x2(x[0], x[1]), hi = pack_bf16x2(x[2], x[3]);
+      *reinterpret_cast<uint2 *>(&kt[16 * blk + (lane & 15)][16 * tb + 4 * (lane >> 4)]) =
+          make_uint2(lo, hi);
+    }
+    __syncthreads();
+    // K' rows: 16 chunks of 8 tokens per row; a chunk whose 8 columns are consecutive and
+    // 16-byte aligned is one store, any other is written token by token
+    for (int e = tid; e < d_store * (kMT / 8); e += 512) {
+      const int row = e / (kMT / 8), c = e % (kMT / 8);
+      const int ta = 8 * c;
+      if (ta >= nt) continue;
+      bf16_t *dst = kp + (static_cast<size_t>(bg) * d_store + row) * T_cap;
+      const int c0 = cols[ta];
+      bool vec = ta + 8 <= nt && c0 >= 0 && (c0 & 7) == 0;
+#pragma unroll
+      for (int j = 1; j < 8; ++j) vec = vec && cols[ta + j] == c0 + j;
+      if (vec) {
+        *reinterpret_cast<uint4 *>(dst + c0) = *reinterpret_cast<const uint4 *>(&kt[row][ta]);
+      } else {
+        for (int j = 0; j < 8 && ta + j < nt; ++j)
+          if (cols[ta + j] >= 0) dst[cols[ta + j]] = kt[row][ta + j];
+      }
+    }
+    // V rows, 16 bytes per lane
+    if (v_raw) {
+      constexpr int PER_ROW = D / 8;
+      for (int e = tid; e < nt * PER_ROW; e += 512) {
+        const int t = e / PER_ROW, c = e % PER_ROW;
+        const int col = cols[t];
+        if (col < 0) continue;
+        *reinterpret_cast<uint4 *>(vc + (static_cast<size_t>(bg) * T_cap + col) * D + 8 * c) =
+            *reinterpret_cast<const uint4 *>(v_raw + (static_cast<size_t>(bg) * n + t0 + t) * D +
+                                             8 * c);
+      }
+    }
+    __syncthreads();  // kt and cols are rewritten by the next tile
+  }
+}
+
+// Few tokens per (b, g) (a decode step's new key, an H2O slot): one workgroup of D/16 wavefronts
+// per (b, g), wavefront w projecting output dims [16 w, 16 w + 16) of the n <= 16 rows.
+template <int D>
+__global__ __launch_bounds__(D / 16 * 64) void project_keys_small_mfma_kernel(
+    const bf16_t *__restrict__ k_raw, const bf16_t *__restrict__ v_raw,
+    const float *__restrict__ P, int n, int d_store, int T_cap, int len0,
+    const int32_t *__restrict__ slots, bf16_t *__restrict__ kp, bf16_t *__restrict__ vc) {
+  constexpr int KS = D / 32;
+  __shared__ int cols[16];
+  const int bg = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  if (tid < n) {
+    const int col = slots ? slots[static_cast<size_t>(bg) * n + tid] : len0 + tid;
+    cols[tid] = (col >= 0 && col < T_cap) ? col : -1;
+  }
+  u32x4_t av[KS];
+  load_a_row<KS>(k_raw + (static_cast<size_t>(bg) * n + min(lane & 15, n - 1)) * D, av);
+  PParts<KS> pp;
+  load_p_parts<KS>(P, 16 * w, pp);
+  const f32x4_t x = proj_mfma<KS>(av, pp);
+  __syncthreads();
+  const int dim = 16 * w + (lane & 15);
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    const int t = 4 * (lane >> 4) + rr;
+    if (t < n && dim < d_store && cols[t] >= 0)
+      kp[(static_cast<size_t>(bg) * d_store + dim) * T_cap + cols[t]] = f32_to_bf16_rne(x[rr]);
+  }
+  if (v_raw) {
+    for (int e = tid; e < n * D; e += D / 16 * 64) {
+      const int t = e / D;
+      if (cols[t] >= 0)
+        vc[(static_cast<size_t>(bg) * T_cap + cols[t]) * D + e % D] =
+            v_raw[static_cast<size_t>(bg) * n * D + e];
+    }
+  }
+}
+
 template <typename KT, int D>
 hipError_t launch_pk(const void *k_raw, const void *v_raw, const float *P, int B, int Hkv, int n,
                      int d_store, int T_cap, int len0, const int32_t *slots, void *kp, void *v,
                      hipStream_t s) {
-  using C = ProjCfg<KT, D>;
-  if (n <= kSmallN) {
-    project_keys_small_kernel<KT, D><<<dim3(B * Hkv), dim3(256), 0, s>>>(
+  if constexpr (sizeof(KT) == 2) {
+    const bf16_t *kr = static_cast<const bf16_t *>(k_raw);
+    const bf16_t *vr = static_cast<const bf16_t *>(v_raw);
+    if (n <= 16) {
+      project_keys_small_mfma_kernel<D><<<dim3(B * Hkv), dim3(D / 16 * 64), 0, s>>>(
+          kr, vr, P, n, d_store, T_cap, len0, slots, static_cast<bf16_t *>(kp),
+          static_cast<bf16_t *>(v));
+      return hipGetLastError();
+    }
+    // tiles per (b, g) spread over about 1024 workgroups in all, each walking several tiles
+    // with its parts of P kept in registers
+    const int groups = B * Hkv, ntiles = (n + kMT - 1) / kMT;
+    const int per = std::max(1, 1024 / groups);
+    const dim3 grid(std::min(ntiles, per), groups);
+    project_keys_mfma_kernel<D><<<grid, dim3(512), 0, s>>>(
+        kr, vr, P, n, d_store, T_cap, len0, slots, static_cast<bf16_t *>(kp),
+        static_cast<bf16_t *>(v));
+    return hipGetLastError();
+  } else {
+    using C = ProjCfg<KT, D>;
+    if (n <= kSmallN) {
+      project_keys_small_kernel<KT, D><<<dim3(B * Hkv), dim3(256), 0, s>>>(
+          static_cast<const KT *>(k_raw), static_cast<const KT *>(v_raw), P, n, d_store, T_cap,
+          len0, slots, static_cast<KT *>(kp), static_cast<KT *>(v));
+      return hipGetLastError();
+    }
+    const dim3 grid((n + C::TT - 1) / C::TT, B * Hkv), block(256);
+    project_keys_kernel<KT, D><<<grid, block, 0, s>>>(
         static_cast<const KT *>(k_raw), static_cast<const KT *>(v_raw), P, n, d_store, T_cap,
         len0, slots, static_cast<KT *>(kp), static_cast<KT *>(v));
     return hipGetLastError();
   }
-  const dim3 grid((n + C::TT - 1) / C::TT, B * Hkv), block(256);
-  project_keys_kernel<KT, D><<<grid, block, 0, s>>>(
-      static_cast<const KT *>(k_raw), static_cast<const KT *>(v_raw), P, n, d_store, T_cap, len0,
-      slots, static_cast<KT *>(kp), static_cast<KT *>(v));
-  return hipGetLastError();
 }
 
 }  // namespace

@@ -2,25 +2,59 @@
 // projected-query magnitude: digest of arXiv 2509.11155, section 方法详解 / 核心思路 and 技术框架;
 // edgentiq blog, "How AQUA Works", step 2).
 //
-// One wavefront per query row.  Lane l owns projected dims l and l + 64 (d = 128) or dim l
-// (d = 64), so that the 64-bit ballot of "dim selected" over the lanes is directly the mask
-// word pair of dims 0..63 (and 64..127).
+// Projection: q'_i = sum_j q_j P[j][i] at fp32 accuracy.  bf16 queries take the library's one
+// bf16 projection (proj_mfma: v_mfma_f32_16x16x32_bf16 on P's exact three-part bf16 split), the
+// arithmetic the fused decode and H2O steps and the prefill use too; fp32 queries take an fma
+// chain over j ascending on the VALU, with P staged in LDS.
 //
-// Projection: q'_i = sum_j q_j P[j][i] in fp32, j ascending (fma chain); q_j is broadcast from
-// its owner lane with v_readlane.  The workgroup first stages all of P in LDS with 16-byte
-// loads (one round trip to L2 instead of one per row j), then each wavefront reads P's rows
-// from LDS (consecutive lanes, consecutive banks).
-//
-// Selection: wave_topk_threshold (exact comparison of sign-cleared fp32 bit patterns, ties to
-// the lower index; the k-th largest key built MSB first from wave ballots, stopping as soon as
-// exactly k keys clear the running threshold).
+// Selection, one wavefront per row: lane l owns projected dims l and l + 64 (d = 128) or dim l
+// (d = 64), so that the 64-bit ballot of "dim selected" over the lanes is directly the mask word
+// pair of dims 0..63 (and 64..127); wave_topk_threshold compares sign-cleared fp32 bit patterns
+// exactly, ties to the lower index, building the k-th largest key MSB first from wave ballots and
+// stopping as soon as exactly k keys clear the running threshold.
 #include "aqua_internal.h"
 
 namespace aqua {
 namespace {
 
-template <typename QT, int D>
-__global__ __launch_bounds__(256) void select_kernel(const QT *__restrict__ q, int N,
+// The outputs of one selected row: q' (if asked for), the mask words (lane l < D/32 writes word
+// l: bits of dims 32 l .. 32 l + 31) and the ascending index list (if asked for).
+template <int D>
+__device__ __forceinline__ void write_selection(int row, const float (&x)[D / 64],
+                                                const bool (&sel)[D / 64], int k,
+                                                float *__restrict__ q_proj,
+                                                uint32_t *__restrict__ mask,
+                                                int16_t *__restrict__ idx) {
+  constexpr int E = D / 64;
+  const int lane = threadIdx.x & 63;
+  uint64_t sb[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) sb[e] = __ballot(sel[e]);
+  if (q_proj) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) q_proj[static_cast<size_t>(row) * D + lane + 64 * e] = x[e];
+  }
+  if (lane < D / 32) {
+    const uint64_t b = (lane >> 1) ? sb[E - 1] : sb[0];
+    mask[static_cast<size_t>(row) * (D / 32) + lane] =
+        (lane & 1) ? static_cast<uint32_t>(b >> 32) : static_cast<uint32_t>(b);
+  }
+  if (idx) {
+    int before = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int pos = before + __builtin_amdgcn_mbcnt_hi(
+                                   static_cast<uint32_t>(sb[e] >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(sb[e]), 0u));
+      if (sel[e]) idx[static_cast<size_t>(row) * k + pos] = static_cast<int16_t>(lane + 64 * e);
+      before += __popcll(sb[e]);
+    }
+  }
+}
+
+// fp32 queries (VALU): P staged in LDS, one wavefront per row.
+template <int D>
+__global__ __launch_bounds__(256) void select_kernel(const float *__restrict__ q, int N,
                                                      const float *__restrict__ P, int d_sel,
                                                      int k, float *__restrict__ q_proj,
                                                      uint32_t *__restrict__ mask,
@@ -42,10 +76,10 @@ __global__ __launch_bounds__(256) void select_kernel(const QT *__restrict__ q, i
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= N) return;  // whole wave leaves; no workgroup barrier follows
 
-  const QT *qr = q + static_cast<size_t>(row) * D;
+  const float *qr = q + static_cast<size_t>(row) * D;
   float qv[E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) qv[e] = load_elem<QT>(qr + lane + 64 * e);
+  for (int e = 0; e < E; ++e) qv[e] = qr[lane + 64 * e];
 
   float acc[E];
 #pragma unroll
@@ -60,30 +94,37 @@ __global__ __launch_bounds__(256) void select_kernel(const QT *__restrict__ q, i
 
   bool sel[E];
   wave_topk_threshold<E>(acc, d_sel, k, sel);
+  write_selection<D>(row, acc, sel, k, q_proj, mask, idx);
+}
 
-  // ---- outputs
-  uint64_t sb[E];
+// bf16 queries (MFMA): a workgroup of D/16 wavefronts takes 16 rows; wavefront w projects output
+// columns [16 w, 16 w + 16) with proj_mfma (the library's one bf16 projection), the q' tile goes
+// through LDS, and each wavefront then selects 16 / (D/16) of the rows.
+template <int D>
+__global__ __launch_bounds__(D / 16 * 64) void select_mfma_kernel(
+    const bf16_t *__restrict__ q, int N, const float *__restrict__ P, int d_sel, int k,
+    float *__restrict__ q_proj, uint32_t *__restrict__ mask, int16_t *__restrict__ idx) {
+  constexpr int KS = D / 32, NB = D / 16, RPW = 16 / NB, E = D / 64;
+  __shared__ float tile[16][D + 4];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int r0 = blockIdx.x * 16;
+  u32x4_t av[KS];
+  load_a_row<KS>(q + static_cast<size_t>(min(r0 + (lane & 15), N - 1)) * D, av);
+  PParts<KS> pp;
+  load_p_parts<KS>(P, 16 * w, pp);
+  const f32x4_t x = proj_mfma<KS>(av, pp);
 #pragma unroll
-  for (int e = 0; e < E; ++e) sb[e] = __ballot(sel[e]);
-  if (q_proj) {
+  for (int rr = 0; rr < 4; ++rr) tile[4 * (lane >> 4) + rr][16 * w + (lane & 15)] = x[rr];
+  __syncthreads();
+  for (int i = 0; i < RPW; ++i) {
+    const int rl = w * RPW + i, row = r0 + rl;
+    if (row >= N) break;  // uniform over the wavefront; no barrier follows
+    float xs[E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) q_proj[static_cast<size_t>(row) * D + lane + 64 * e] = acc[e];
-  }
-  if (lane < D / 32) {
-    const uint64_t b = (lane >> 1) ? sb[E - 1] : sb[0];
-    mask[static_cast<size_t>(row) * (D / 32) + lane] =
-        (lane & 1) ? static_cast<uint32_t>(b >> 32) : static_cast<uint32_t>(b);
-  }
-  if (idx) {
-    int before = 0;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const int pos = before + __builtin_amdgcn_mbcnt_hi(
-                                   static_cast<uint32_t>(sb[e] >> 32),
-                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(sb[e]), 0u));
-      if (sel[e]) idx[static_cast<size_t>(row) * k + pos] = static_cast<int16_t>(lane + 64 * e);
-      before += __popcll(sb[e]);
-    }
+    for (int e = 0; e < E; ++e) xs[e] = tile[rl][lane + 64 * e];
+    bool sel[E];
+    wave_topk_threshold<E>(xs, d_sel, k, sel);
+    write_selection<D>(row, xs, sel, k, q_proj, mask, idx);
   }
 }
 
@@ -91,19 +132,23 @@ __global__ __launch_bounds__(256) void select_kernel(const QT *__restrict__ q, i
 
 hipError_t launch_select(const void *q, int qdt, int N, int d, const float *P, int d_sel, int k,
                          float *q_proj, uint32_t *mask, int16_t *idx, hipStream_t s) {
-  const dim3 grid((N + 3) / 4), block(256);
-  if (qdt == 0 && d == 128)
-    select_kernel<float, 128><<<grid, block, 0, s>>>(static_cast<const float *>(q), N, P, d_sel,
-                                                     k, q_proj, mask, idx);
-  else if (qdt == 0 && d == 64)
-    select_kernel<float, 64><<<grid, block, 0, s>>>(static_cast<const float *>(q), N, P, d_sel,
-                                                    k, q_proj, mask, idx);
-  else if (qdt == 1 && d == 128)
-    select_kernel<bf16_t, 128><<<grid, block, 0, s>>>(static_cast<const bf16_t *>(q), N, P,
-                                                      d_sel, k, q_proj, mask, idx);
-  else
-    select_kernel<bf16_t, 64><<<grid, block, 0, s>>>(static_cast<const bf16_t *>(q), N, P,
-                                                     d_sel, k, q_proj, mask, idx);
+  if (qdt == 0) {
+    const dim3 grid((N + 3) / 4), block(256);
+    if (d == 128)
+      select_kernel<128><<<grid, block, 0, s>>>(static_cast<const float *>(q), N, P, d_sel, k,
+                                                q_proj, mask, idx);
+    else
+      select_kernel<64><<<grid, block, 0, s>>>(static_cast<const float *>(q), N, P, d_sel, k,
+                                               q_proj, mask, idx);
+  } else {
+    const dim3 grid((N + 15) / 16);
+    if (d == 128)
+      select_mfma_kernel<128><<<grid, dim3(512), 0, s>>>(static_cast<const bf16_t *>(q), N, P,
+                                                         d_sel, k, q_proj, mask, idx);
+    else
+      select_mfma_kernel<64><<<grid, dim3(256), 0, s>>>(static_cast<const bf16_t *>(q), N, P,
+                                                        d_sel, k, q_proj, mask, idx);
+  }
   return hipGetLastError();
 }
 

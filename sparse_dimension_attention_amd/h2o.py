@@ -17,9 +17,9 @@ ones only gain (non-negative fp32 additions), so the full-recompute heavy set of
 previous set minus one member, plus the token that has just left the recent window.
 
 :meth:`H2OCache.from_full` builds the starting state from a full-context cache and its mass
-(the cumulative attention of earlier steps): the ``heavy`` positions of highest mass among
-those older than the recent window, plus the ``recent`` latest positions.  It is set-up work,
-done once with torch tensor ops; every step after it runs in libaqua's kernels.
+(the cumulative attention of earlier steps) with ``aqua_h2o_init``: the ``heavy`` positions of
+highest mass among those older than the recent window, plus the ``recent`` latest positions.
+Torch only allocates the compact state's tensors; every number in it comes from libaqua.
 """
 from __future__ import annotations
 
@@ -45,29 +45,23 @@ class H2OCache:
         """Starting state after ``length`` tokens (positions 0..length-1) of a full cache
         ``kp_full [B][Hkv][d_store][T_cap]``, ``v_full [B][Hkv][T_cap][d]`` whose mass is
         ``mass_full [B][Hkv][T_cap]``.  Requires ``length - recent >= heavy``."""
-        n_old = length - recent
-        if n_old < heavy:
+        if length - recent < heavy:
             raise ValueError("fewer older tokens than heavy-hitter slots")
-        dev = kp_full.device
-        m_old = mass_full[:, :, :n_old]
-        # stable descending sort: equal masses keep ascending position order
-        order = torch.sort(m_old, dim=-1, descending=True, stable=True).indices[..., :heavy]
-        heavy_pos = torch.sort(order, dim=-1).values
-        B, Hkv = kp_full.shape[:2]
-        rec = torch.arange(n_old, length, device=dev).expand(B, Hkv, recent)
-        pos = torch.cat([heavy_pos, rec], dim=-1).contiguous()          # [B][Hkv][n_slots]
-        d_store = kp_full.shape[2]
-        kp = torch.gather(kp_full, 3, pos[:, :, None, :].expand(B, Hkv, d_store, pos.shape[-1]))
-        v = torch.gather(v_full, 2, pos[..., None].expand(B, Hkv, pos.shape[-1],
-                                                         v_full.shape[-1]))
-        mass = torch.gather(mass_full, 2, pos)
-        return cls(kp.contiguous(), v.contiguous(), pos.to(torch.int32), mass.contiguous(), heavy,
-                   recent)
+        B, Hkv, d_store, _ = kp_full.shape
+        n_slots = heavy + recent
+        kp = torch.empty(B, Hkv, d_store, n_slots, dtype=kp_full.dtype, device=kp_full.device)
+        v = torch.empty(B, Hkv, n_slots, v_full.shape[-1], dtype=v_full.dtype,
+                        device=v_full.device)
+        mass = torch.empty(B, Hkv, n_slots, dtype=torch.float32, device=kp_full.device)
+        pos = torch.empty(B, Hkv, n_slots, dtype=torch.int32, device=kp_full.device)
+        A.aqua_h2o_init(A.make_cache(kp_full, v_full, length), mass_full, heavy, recent,
+                        A.make_cache(kp, v, n_slots), mass, pos)
+        return cls(kp, v, pos, mass, heavy, recent)
 
     def workspace(self, Hq: int):
         if self.ws is None:
             n = A.aqua_decode_workspace(self.cache, Hq)
-            self.ws = torch.zeros(n, dtype=torch.uint8, device=self.kp.device)
+            self.ws = torch.empty(n, dtype=torch.uint8, device=self.kp.device)  # no clearing needed
         return self.ws
 
     def step(self, q, k_new, v_new, P, t_new: int, d_sel: int, k: int, scale: float, out,

@@ -14,6 +14,33 @@ DEV = torch.device("cuda:0") if torch.cuda.is_available() else None
 
 F32_TOL = 1e-5                  # max-abs, fp32 storage
 BF16_MAXABS, BF16_RELL2 = 1e-2, 5e-3
+U = 2.0 ** -24                  # fp32 unit roundoff
+
+
+def gamma(n):
+    return n * U / (1 - n * U)
+
+
+def mass_tol(qp, m, Kp, scale, k):
+    """Relative bound on the GPU's softmax weights against fp64 weights computed from the GPU's
+    own q' and K' (no figure is given for it, so it is derived from the fp32 arithmetic).
+    qp, m [G][d] (GPU q', masks); Kp [n][d_store] (GPU K', token-major).  A score error
+    |ds| <= gamma_(k+2) * scale * sum_i |q'_i K'_i| moves a weight by a factor
+    exp(ds_t - sum_u p_u ds_u), i.e. relative error <= 2 max|ds|; the log2-domain subtraction
+    s - max s (|s - m| <= 2 S log2 e) rounds once more, and exp2, the division and the fp32
+    additions a few u."""
+    S = scale * float((np.abs(qp[:, :Kp.shape[1]] * m[:, :Kp.shape[1]]) @ np.abs(Kp).T).max())
+    return 2 * gamma(k + 2) * S + 6 * U * S + 8 * U
+
+
+def check_mass_update(before, after, add, tol, what=""):
+    """after = before + add per element, in fp32: |after - (before + add)| must stay within the
+    weights' relative bound tol * add plus the rounding of the fp32 sum, 2u (before + add)."""
+    before, after, add = (np.asarray(x, np.float64) for x in (before, after, add))
+    want = before + add
+    dm = np.abs(after - want)
+    lim = tol * add + 2 * U * np.abs(want)
+    assert np.all(dm <= lim), f"{what}: mass error / bound {float(np.max(dm / lim))}"
 
 
 def unpack_mask(mask_i32: torch.Tensor, d: int) -> np.ndarray:
@@ -46,6 +73,11 @@ def new_cache(B, Hkv, d, d_store, T_cap, dtype):
     kp = torch.full((B, Hkv, d_store, T_cap), float("nan"), dtype=tdtype(dtype), device=DEV)
     v = torch.full((B, Hkv, T_cap, d), float("nan"), dtype=tdtype(dtype), device=DEV)
     return kp, v
+
+
+def kp_token_major(kp, b, g, length):
+    """The GPU's K' of group (b, g), tokens [0, length), as fp64 [length][d_store]."""
+    return kp[b, g, :, :length].T.cpu().double().numpy()
 
 
 def select(q_dev, P_dev, d_sel, k, want_idx=False):

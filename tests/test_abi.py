@@ -30,7 +30,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 11
+    assert len(names) == 12
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(aq.EXPORTS)
@@ -123,6 +123,35 @@ def test_h2o_victim_rejects(lib):
     assert lib.aqua_h2o_victim(None, FAKE, 1, 1, 4, 10, 2, FAKE, None) == A.AQUA_ERR_NULL
     assert lib.aqua_h2o_victim(FAKE, FAKE, 1, 1, 0, 10, 2, FAKE, None) == A.AQUA_ERR_SHAPE
     assert lib.aqua_h2o_victim(FAKE, FAKE, 1, 1, 4, 10, -1, FAKE, None) == A.AQUA_ERR_SHAPE
+    assert lib.aqua_h2o_victim(FAKE + 4, FAKE, 1, 1, 4, 10, 2, FAKE, None) == A.AQUA_ERR_ALIGN
+    assert lib.aqua_h2o_victim(FAKE, FAKE + 8, 1, 1, 4, 10, 2, FAKE, None) == A.AQUA_ERR_ALIGN
+    assert lib.aqua_h2o_victim(FAKE, FAKE, 1, 1, 4, 10, 2, FAKE + 4, None) == A.AQUA_ERR_ALIGN
+
+
+def _h2o_init(lib, full, compact, heavy=1024, recent=256, mass_full=FAKE, mass=FAKE,
+              slot_pos=FAKE):
+    return lib.aqua_h2o_init(ctypes.byref(full), mass_full, heavy, recent, ctypes.byref(compact),
+                             mass, slot_pos, None)
+
+
+@pytest.mark.parametrize("fkw,ckw,args,status", [
+    (dict(), dict(), dict(mass=None), A.AQUA_ERR_NULL),
+    (dict(), dict(), dict(mass_full=FAKE + 4), A.AQUA_ERR_ALIGN),
+    (dict(), dict(), dict(slot_pos=FAKE + 8), A.AQUA_ERR_ALIGN),
+    (dict(), dict(d_store=128), dict(), A.AQUA_ERR_SHAPE),         # d_store differs
+    (dict(), dict(dtype=A.AQUA_F32), dict(), A.AQUA_ERR_SHAPE),    # dtype differs
+    (dict(), dict(B=2), dict(), A.AQUA_ERR_SHAPE),                 # batch differs
+    (dict(), dict(len=1200), dict(), A.AQUA_ERR_SHAPE),            # compact cache not full
+    (dict(), dict(), dict(heavy=1000), A.AQUA_ERR_SHAPE),          # T_cap != heavy + recent
+    (dict(), dict(), dict(heavy=-64, recent=1344), A.AQUA_ERR_SHAPE),
+    (dict(len=1000), dict(), dict(), A.AQUA_ERR_CAPACITY),         # fewer tokens than slots
+    (dict(d_head=96), dict(), dict(), A.AQUA_ERR_SHAPE),
+])
+def test_h2o_init_rejects(lib, fkw, ckw, args, status):
+    full = _cache(**dict(dict(B=1, Hkv=8, d_store=96, T_cap=32768, len=32768), **fkw))
+    compact = _cache(**dict(dict(B=1, Hkv=8, d_store=96, T_cap=1280, len=1280), **ckw))
+    assert _h2o_init(lib, full, compact, **args) == status
+    assert lib.aqua_last_error().decode() != ""
 
 
 def test_binding_raises_with_message(lib):

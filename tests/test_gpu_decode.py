@@ -6,7 +6,8 @@ import pytest
 import torch
 
 import sparse_dimension_attention_amd as aq
-from gpu_util import (DEV, assert_close, oracle_decode, rel_l2, run_decode, unpack_mask)
+from gpu_util import (DEV, assert_close, check_mass_update, kp_token_major, mass_tol,
+                      oracle_decode, rel_l2, run_decode, unpack_mask)
 from oracle import aqua_oracle as O
 from synth import config, make_decode_inputs, storage_to_f64
 
@@ -155,10 +156,6 @@ def test_decode_deterministic_and_reusable_workspace():
     torch.cuda.synchronize()
     for o in outs:
         assert torch.equal(o, r["out"])
-    # the workspace is left cleared
-    ws = r["ws"]
-    n = c["B"] * c["Hkv"] * 4
-    assert int(ws[:n].count_nonzero()) == 0
 
 
 def test_decode_workspace_reuse_across_inputs():
@@ -180,21 +177,6 @@ def test_decode_workspace_reuse_across_inputs():
         assert torch.equal(out, r["out"]), f"call {it}"
 
 
-def test_decode_llama8b_full_size_sampled():
-    """B=16, Hq=32, Hkv=8, T=8192, k=96 (the benchmark workload): every mask checked, outputs
-    of a sample of heads checked against the oracle one by one."""
-    c = config(2)
-    inp = make_decode_inputs(c)
-    r = run_decode(inp, c)
-    m = _check_masks(r, c)
-    heads = [(0, 0), (0, 31), (5, 13), (9, 2), (15, 30), (15, 31), (7, 16), (3, 9)]
-    ref = oracle_decode(inp, c, m, heads=heads)
-    got = r["out"].cpu().double().numpy()
-    for b, h in heads:
-        assert_close(got[b, h], ref[b, h], "bf16", f"head {(b, h)}")
-    assert np.isfinite(got).all()
-
-
 @pytest.fixture(scope="module")
 def long_inputs():
     return make_decode_inputs(config(3))
@@ -214,6 +196,29 @@ def test_decode_long_context_sampled(k, long_inputs):
         assert_close(got[b, h], ref[b, h], "bf16", f"k={k} head {h}")
 
 
+def check_mass_mode(r, inp, c, mass0, mass):
+    """Mass mode: every token's mass grew by the group's summed softmax weight, per element within
+    the weights' derived relative bound (gpu_util.mass_tol), the fp64 weights computed from the
+    GPU's own q' and K'; the sum of the additions is G; tokens past len are untouched."""
+    B, Hq, Hkv, d, T, k = c["B"], c["Hq"], c["Hkv"], c["d"], c["T"], c["k"]
+    G = Hq // Hkv
+    scale = 1 / math.sqrt(d)
+    m = unpack_mask(r["mask"], d)
+    qp = r["qp"].cpu().double().numpy()
+    before = mass0.cpu().double().numpy()
+    after = mass.cpu().double().numpy()
+    for b in range(B):
+        for g in range(Hkv):
+            Kp = kp_token_major(r["kp"], b, g, T)
+            V = storage_to_f64(inp["v"][b, g, :T])
+            hs = slice(g * G, (g + 1) * G)
+            add = O.h2o_seed_mass(qp[b, hs], m[b, hs], Kp, V, scale)
+            tol = mass_tol(qp[b, hs], m[b, hs], Kp, scale, k)
+            check_mass_update(before[b, g, :T], after[b, g, :T], add, tol, f"group {(b, g)}")
+            assert abs((after[b, g, :T] - before[b, g, :T]).sum() - G) < 1e-3
+            assert np.array_equal(after[b, g, T:], before[b, g, T:])
+
+
 @pytest.mark.parametrize("T", [3000, 40000, 70000])
 def test_decode_mass_accumulation(T):
     """Mass mode: mass[t] grows by the sum over the group's heads of the softmax weights (short
@@ -224,19 +229,35 @@ def test_decode_mass_accumulation(T):
     mass0 = torch.rand(c["B"], c["Hkv"], T_cap, device=DEV)
     mass = mass0.clone()
     r = run_decode(inp, c, T_cap=T_cap, mass=mass)
+    _check_masks(r, c)
+    check_mass_mode(r, inp, c, mass0, mass)
+
+
+def test_decode_mass_eight_wave_d64():
+    """Mass mode and d = 64 on the 8-wavefront layout (16 groups x 16 full 4096-token splits:
+    one 512-thread workgroup per CU of a 256-CU device), against the oracle on every head."""
+    c = config(2, B=2, Hq=32, Hkv=8, T=65536, d=64, d_store=64, d_sel=64, k=40)
+    inp = make_decode_inputs(c, workers=16)
+    T_cap = c["T"] + 256
+    mass0 = torch.rand(c["B"], c["Hkv"], T_cap, device=DEV)
+    mass = mass0.clone()
+    r = run_decode(inp, c, T_cap=T_cap, mass=mass)
     m = _check_masks(r, c)
-    P64 = storage_to_f64(inp["P"])
-    qp64 = O.project(storage_to_f64(inp["q"]), P64)
-    G = c["Hq"] // c["Hkv"]
-    got = mass.cpu().double().numpy() - mass0.cpu().double().numpy()
-    for b in range(c["B"]):
-        for g in range(c["Hkv"]):
-            Kp = O.project_keys_stored(storage_to_f64(inp["k"][b, g]), P64, "bf16", 96)
-            V = storage_to_f64(inp["v"][b, g])
-            add = np.zeros(c["T"])
-            for h in range(g * G, (g + 1) * G):
-                _, p = O.attend(qp64[b, h], m[b, h], Kp, V, 1 / math.sqrt(c["d"]))
-                add += p
-            assert np.max(np.abs(got[b, g, :c["T"]] - add)) <= 1e-3 * add.max()
-            assert abs(got[b, g, :c["T"]].sum() - G) < 1e-3
-            assert np.all(got[b, g, c["T"]:] == 0)
+    ref = oracle_decode(inp, c, m)
+    assert_close(r["out"].cpu().double().numpy(), ref, "bf16", "d=64, 8-wave")
+    check_mass_mode(r, inp, c, mass0, mass)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,T", [
+    (4, 32, 8, 16384),   # 32 groups x 8 full 2048-token splits: the 8-wavefront layout
+    (2, 8, 2, 9000),     # 4 groups: the 4-wavefront layout (1024-token splits)
+])
+def test_decode_f32_group4_layouts(B, Hq, Hkv, T):
+    """fp32 storage at G = 4 on the split-T kernel in both layouts, every head against the oracle
+    within the fp32 tolerance."""
+    c = config(1, B=B, Hq=Hq, Hkv=Hkv, d=128, T=T, k=96, d_store=128, d_sel=128)
+    inp = make_decode_inputs(c, workers=16)
+    r = run_decode(inp, c)
+    m = _check_masks(r, c)
+    ref = oracle_decode(inp, c, m)
+    assert_close(r["out"].cpu().double().numpy(), ref, "f32", f"f32 G=4 {B},{T}")

@@ -6,7 +6,8 @@ import pytest
 import torch
 
 import sparse_dimension_attention_amd as aq
-from gpu_util import DEV, assert_close, new_cache, oracle_decode, unpack_mask
+from gpu_util import (DEV, assert_close, check_mass_update, kp_token_major, mass_tol, new_cache,
+                      oracle_decode, unpack_mask)
 from oracle import aqua_oracle as O
 from synth import config, make_decode_inputs, storage_to_f64
 
@@ -124,24 +125,30 @@ def test_step_sequence_appends(T0):
         assert_close(out.cpu().double().numpy(), ref, "bf16", f"step at {t}")
 
 
-def test_step_mass_mode():
-    c = config(2, B=1, Hq=8, Hkv=2, T=1280, d_store=96, d_sel=96, k=64)
+@pytest.mark.parametrize("T,T_cap", [(1280, 1280), (9000, 9024)])
+def test_step_mass_mode(T, T_cap):
+    """Mass mode of the fused step (short kernel at 1280 tokens, split-T past 4096): every token's
+    mass, the new one's included, grows by the group's summed weight, per element within the
+    derived relative bound (fp64 weights from the GPU's own q' and K')."""
+    c = config(2, B=1, Hq=8, Hkv=2, T=T, d_store=96, d_sel=96, k=64)
     inp = make_decode_inputs(c)
-    mass = torch.zeros(c["B"], c["Hkv"], 1280, device=DEV)
-    r = _step(inp, c, c["T"], T_cap=1280, mass=mass)
+    mass0 = torch.rand(c["B"], c["Hkv"], T_cap, device=DEV)
+    mass = mass0.clone()
+    r = _step(inp, c, c["T"], T_cap=T_cap, mass=mass)
     m = unpack_mask(r["mask"], c["d"])
-    P64 = storage_to_f64(inp["P"])
-    qp64 = O.project(storage_to_f64(inp["q"]), P64)
+    assert np.array_equal(m, O.select(r["qp"].cpu().double().numpy(), 96, 64))
+    qp = r["qp"].cpu().double().numpy()
     G = c["Hq"] // c["Hkv"]
+    scale = 1 / math.sqrt(c["d"])
     for g in range(c["Hkv"]):
-        Kp = O.project_keys_stored(storage_to_f64(inp["k"][0, g]), P64, "bf16", 96)
+        Kp = kp_token_major(r["kp"], 0, g, T)
         V = storage_to_f64(inp["v"][0, g])
-        add = np.zeros(c["T"])
-        for h in range(g * G, (g + 1) * G):
-            _, p = O.attend(qp64[0, h], m[0, h], Kp, V, 1 / math.sqrt(c["d"]))
-            add += p
-        got = mass[0, g].cpu().double().numpy()
-        assert np.max(np.abs(got - add)) <= 1e-3 * add.max()
+        hs = slice(g * G, (g + 1) * G)
+        add = O.h2o_seed_mass(qp[0, hs], m[0, hs], Kp, V, scale)
+        tol = mass_tol(qp[0, hs], m[0, hs], Kp, scale, 64)
+        check_mass_update(mass0[0, g, :T].cpu().numpy(), mass[0, g, :T].cpu().numpy(), add, tol,
+                          f"group {g}")
+        assert torch.equal(mass[0, g, T:], mass0[0, g, T:])
 
 
 @pytest.mark.parametrize("k", [96, 32])

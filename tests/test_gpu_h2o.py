@@ -5,15 +5,15 @@ heavy + recent set computed from the GPU's own (fp32) mass; the masks must equal
 selection of the GPU's q'; the output must match the fp64 attention over that set; and the GPU's
 mass after the step must equal its mass before plus the fp64 softmax weights.
 
-Mass tolerance (no figure is given for it, so it is derived from the arithmetic).  The oracle's
-weights are computed from the GPU's own q' and K' (their roundings are checked by the selection
-and key-projection tests: one bf16 ulp of K' alone moves a weight by ~1e-4), so the GPU's
-weights differ only by the fp32 score sum and the exp2/divide roundings: a score error
-|ds| <= gamma_{n+2} * scale * sum_i |q'_i K'_i| (n = k terms; gamma_n = n u / (1 - n u),
-u = 2^-24) moves p_t by a factor exp(ds_t - sum_u p_u ds_u), i.e. relative error <= 2 max|ds|;
-the log2-domain subtraction s - max s, exp2, the division and the fp32 mass additions add a few
-u more.  The bound is computed from the
-data at every check."""
+Mass tolerance (no figure is given for it, so it is derived from the arithmetic: gpu_util's
+mass_tol).  The oracle's weights are computed from the GPU's own q' and K' (their roundings are
+checked by the selection and key-projection tests: one bf16 ulp of K' alone moves a weight by
+~1e-4), so the GPU's weights differ only by the fp32 score sum and the exp2/divide roundings.  The
+bound is computed from the data at every check.
+
+Both step forms are checked this way: the four calls (victim, slot append, selection, mass-mode
+decode) and the one launch aqua_h2o_step.  The starting state comes from aqua_h2o_init, whose
+slot set is checked against the oracle's heavy set of the GPU's seeding mass, bit for bit."""
 import math
 
 import numpy as np
@@ -22,24 +22,14 @@ import torch
 
 import sparse_dimension_attention_amd as aq
 from sparse_dimension_attention_amd.h2o import H2OCache
-from gpu_util import DEV, BF16_MAXABS, BF16_RELL2, F32_TOL, new_cache, rel_l2, unpack_mask
+from gpu_util import (DEV, BF16_MAXABS, BF16_RELL2, F32_TOL, mass_tol, new_cache, rel_l2,
+                      unpack_mask)
 from oracle import aqua_oracle as O
 from synth import config, make_h2o_inputs, storage_to_f64
 
 pytestmark = pytest.mark.gpu
 
-U = 2.0 ** -24
-
-
-def _gamma(n):
-    return n * U / (1 - n * U)
-
-
-def _mass_tol(qp, m, Kp, scale, k):
-    """Relative bound on the GPU's softmax weights: qp, m [G][d] (GPU q', masks), Kp [n][d_store]."""
-    S = scale * float((np.abs(qp[:, :Kp.shape[1]] * m[:, :Kp.shape[1]]) @ np.abs(Kp).T).max())
-    # 2 max|ds|; the log2-domain subtraction s - m (|s - m| <= 2 S log2 e) rounds once more
-    return 2 * _gamma(k + 2) * S + 6 * U * S + 8 * U
+_mass_tol = mass_tol
 
 
 def _seed(inp, c):
@@ -63,7 +53,7 @@ def _seed(inp, c):
     return st, qp, mask, mass[:, :, :T], P, kp
 
 
-def _run(c):
+def _run(c, fused=False):
     inp = make_h2o_inputs(c)
     B, Hq, Hkv, d, T, S = c["B"], c["Hq"], c["Hkv"], c["d"], c["T"], c["steps"]
     G = Hq // Hkv
@@ -111,7 +101,7 @@ def _run(c):
     for s in range(S):
         t_new = T + s
         st.step(inp["q_steps"][s].to(DEV), inp["k_steps"][s].to(DEV), inp["v_steps"][s].to(DEV),
-                P, t_new, c["d_sel"], c["k"], scale, out, qp, mask)
+                P, t_new, c["d_sel"], c["k"], scale, out, qp, mask, fused=fused)
         torch.cuda.synchronize()
         pos = st.slot_pos.cpu().numpy()
         victim = st.victim.cpu().numpy()
@@ -160,10 +150,63 @@ def test_h2o_small_bf16_g8():
     _run(c)
 
 
-def test_h2o_llama8b_t32768_64_steps():
+@pytest.mark.parametrize("fused", [False, True])
+def test_h2o_llama8b_t32768_64_steps(fused):
     """The heavy-hitter workload: 32768-token context, 1024 heavy + 256 recent slots, AQUA-Memory
-    (96 stored dims, top-64 of them), 64 steps."""
-    _run(config(5))
+    (96 stored dims, top-64 of them), 64 steps; as four calls per step and as the one launch
+    aqua_h2o_step (the benchmarked form), each checked against the oracle at every step."""
+    _run(config(5), fused=fused)
+
+
+def test_h2o_small_fused_every_step_evicts():
+    """The one-launch step against the oracle where every step evicts (fp32 storage, G = 4) and
+    with G = 8 in bf16."""
+    _run(config(5, T=320, heavy=40, recent=24, steps=48, dtype="f32"), fused=True)
+    _run(config(5, Hq=16, Hkv=2, T=700, heavy=96, recent=32, steps=40), fused=True)
+
+
+@pytest.mark.parametrize("T,heavy,recent,ties", [
+    (32768, 1024, 256, False),   # the heavy-hitter workload's shape
+    (5000, 668, 100, True),      # masses from a 5-value set: ties ranked by position
+    (2048, 1984, 64, True),      # every older position is a heavy hitter
+    (640, 0, 64, False),         # recent window only
+    (2000, 64, 0, True),         # no recent window
+])
+def test_h2o_init_matches_oracle(T, heavy, recent, ties):
+    """aqua_h2o_init: each (b, g)'s slot positions are the oracle's heavy set of the same (fp32)
+    mass, in ascending order, followed by the recent window, bit for bit; every slot's K' column,
+    V row and mass are the full cache's at that position, bit for bit."""
+    B, Hkv, d, d_store = 2, 4, 128, 96
+    T_cap = (T + 63) // 64 * 64
+    g = torch.Generator(device="cpu").manual_seed(T + heavy)
+    kp = torch.randn(B, Hkv, d_store, T_cap, generator=g).to(torch.bfloat16).to(DEV)
+    v = torch.randn(B, Hkv, T_cap, d, generator=g).to(torch.bfloat16).to(DEV)
+    if ties:
+        vals = torch.tensor([0.0, 1e-3, 2e-3, 0.5, 3e-7])
+        mass = vals[torch.randint(0, 5, (B, Hkv, T_cap), generator=g)]
+    else:
+        mass = torch.rand(B, Hkv, T_cap, generator=g) ** 4
+    mass = mass.float().to(DEV)
+    n = heavy + recent
+    kc = torch.full((B, Hkv, d_store, n), float("nan"), dtype=torch.bfloat16, device=DEV)
+    vc = torch.full((B, Hkv, n, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+    mc = torch.full((B, Hkv, n), float("nan"), device=DEV)
+    pos = torch.full((B, Hkv, n), -7, dtype=torch.int32, device=DEV)
+    aq.aqua_h2o_init(aq.make_cache(kp, v, T), mass, heavy, recent, aq.make_cache(kc, vc, n), mc,
+                     pos)
+    torch.cuda.synchronize()
+    pos_np = pos.cpu().numpy().astype(np.int64)
+    m64 = mass.cpu().double().numpy()
+    for b in range(B):
+        for gg in range(Hkv):
+            H = O.h2o_heavy_set(m64[b, gg, :T], T - 1, heavy, recent) if heavy else \
+                np.zeros(0, np.int64)
+            want = np.concatenate([H, np.arange(T - recent, T)])
+            assert np.array_equal(pos_np[b, gg], want), f"group {(b, gg)}"
+            idx = torch.from_numpy(want).to(DEV)
+            assert torch.equal(kc[b, gg], kp[b, gg][:, idx])
+            assert torch.equal(vc[b, gg], v[b, gg][idx])
+            assert torch.equal(mc[b, gg], mass[b, gg][idx])
 
 
 @pytest.mark.parametrize("over", [

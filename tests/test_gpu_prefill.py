@@ -166,24 +166,44 @@ def test_prefill_q_proj_fp32_accuracy():
     _check(inp, c, out, qp, mask, rows, 128, 96)
 
 
-def test_prefill_llama8b_t16384_sampled():
-    """The chunked-prefill workload: T=16384 in 8 chunks of 2048, k=96; sampled rows from
-    every chunk, head and the first/last positions of chunks."""
+def test_prefill_llama8b_t16384():
+    """The chunked-prefill workload (T=16384 in 8 chunks of 2048, k=96): all 524288 masks
+    bit-exact against the oracle's selection of the GPU's q'; 384 rows per chunk against the
+    oracle, covering every head of every chunk (the first and last position of each chunk, and
+    random ones); every output finite."""
     c = config(4)
-    inp = make_prefill_inputs(c)
+    inp = make_prefill_inputs(c, workers=16)
     out, qp, mask = _run_chunks(inp, c, c["chunk"])
-    rng = np.random.default_rng(0)
-    rows = [(0, int(h), int(p)) for h, p in zip(rng.integers(0, 32, 24),
-                                                 rng.integers(0, 16384, 24))]
-    rows += [(0, 0, 0), (0, 31, 16383), (0, 5, 2047), (0, 6, 2048), (0, 17, 14335)]
+    T, Hq, chunk = c["T"], c["Hq"], c["chunk"]
     m = unpack_mask(mask, 128)
-    for b, h, p in rows:
-        assert np.array_equal(m[b, h, p], O.select(qp[b, h, p].cpu().double().numpy()[None],
-                                                   128, 96)[0])
+    assert np.array_equal(m.reshape(-1, 128),
+                          O.select(qp.cpu().double().numpy().reshape(-1, 128), 128, 96))
+    rng = np.random.default_rng(0)
+    rows = []
+    for c0 in range(0, T, chunk):
+        for h in range(Hq):
+            rows += [(0, h, c0), (0, h, c0 + chunk - 1)]
+            rows += [(0, h, int(p)) for p in c0 + rng.integers(0, chunk, 10)]
     ref = _oracle_rows(inp, c, m, rows)
-    got = np.stack([out[b, h, p].cpu().double().numpy() for b, h, p in rows])
+    out_np = out.cpu().numpy()
+    got = np.stack([out_np[b, h, p].astype(np.float64) for b, h, p in rows])
     assert_close(got, ref, "bf16", "prefill T16384")
     assert torch.isfinite(out).all()
+
+
+def test_prefill_q_proj_equals_select():
+    """The prefill's q' and masks are aqua_select_dims' for the same bf16 rows, bit for bit (both
+    run the library's one bf16 projection and the same selection)."""
+    c = config(4, B=1, Hq=8, Hkv=2, T=640, k=96)
+    inp = make_prefill_inputs(c)
+    out, qp, mask = _run_chunks(inp, c, 320)
+    q = inp["q"].reshape(-1, 128).to(DEV)
+    qp2 = torch.empty(q.shape[0], 128, device=DEV)
+    mask2 = torch.empty(q.shape[0], 4, dtype=torch.int32, device=DEV)
+    aq.aqua_select_dims(q, inp["P"].to(DEV), 128, 96, qp2, mask2)
+    torch.cuda.synchronize()
+    assert torch.equal(qp.reshape(-1, 128), qp2)
+    assert torch.equal(mask.reshape(-1, 4), mask2)
 
 
 @pytest.mark.parametrize("d_sel,k", [(128, 96), (128, 5), (96, 40), (128, 127), (128, 128)])

@@ -41,10 +41,13 @@ def test_select_matches_oracle(d, d_sel, k, dtype, N):
     # bit-exact against the oracle fed the GPU's q'
     assert np.array_equal(m_g, O.select(qp_g, d_sel, k))
     assert (m_g.sum(1) == k).all() and not m_g[:, d_sel:].any()
-    # q' itself: fp32 accumulation of the stored inputs
-    qp64 = O.project(storage_to_f64(q), storage_to_f64(P32))
-    scale = np.abs(storage_to_f64(q)).sum(1, keepdims=True) * np.abs(P64).max()
-    assert np.all(np.abs(qp_g - qp64) <= 1e-6 * scale + 1e-30)
+    # q' itself: fp32 accumulation of the stored inputs' exact products (bf16: 3 d products of q
+    # with P's three bf16 parts; fp32: d fmas), |dq'_i| <= gamma_(3d+1) sum_j |q_j P_ji|
+    q64, P64s = storage_to_f64(q), storage_to_f64(P32)
+    qp64 = O.project(q64, P64s)
+    n = 3 * d + 1
+    bound = n * 2.0 ** -24 / (1 - n * 2.0 ** -24) * (np.abs(q64) @ np.abs(P64s))
+    assert np.all(np.abs(qp_g - qp64) <= bound)
     # idx: the kept dims in ascending order
     ix = idx.cpu().numpy().astype(np.int64)
     for r in range(N):
@@ -88,8 +91,13 @@ def _ulp_bf16(x):
     ("f32", 64, 64, 256, 0, 256),
     ("f32", 128, 128, 33, 100, 192),
     ("bf16", 64, 64, 1, 63, 64),
-    ("bf16", 128, 128, 8, 5, 64),      # largest few-token launch
-    ("bf16", 128, 96, 9, 0, 64),       # smallest tiled launch
+    ("bf16", 128, 128, 8, 5, 64),      # a few tokens at an unaligned column
+    ("bf16", 128, 128, 16, 48, 64),    # largest few-token launch (one 16-row MFMA tile)
+    ("bf16", 128, 96, 17, 0, 64),      # smallest tiled launch (bf16)
+    ("bf16", 128, 128, 256, 0, 256),   # two whole 128-token tiles, aligned 16-byte writes
+    ("bf16", 128, 128, 200, 8, 256),   # aligned start, ragged last tile
+    ("bf16", 64, 64, 200, 3, 256),     # d = 64 tiles (two wavefronts per column block)
+    ("f32", 128, 96, 9, 0, 64),        # smallest tiled launch (fp32)
     ("f32", 128, 128, 1, 191, 192),    # a decode step filling the last column
 ])
 def test_project_keys_append(dtype, d, d_store, n, len0, T_cap):
@@ -108,8 +116,10 @@ def test_project_keys_append(dtype, d, d_store, n, len0, T_cap):
     ref = O.project_keys_stored(storage_to_f64(K), storage_to_f64(P32), dtype, d_store)
     got = np.swapaxes(kp_h[:, :, :, len0:len0 + n], 2, 3)
     exact = O.project(storage_to_f64(K), storage_to_f64(P32))[..., :d_store]
-    # |bf16(fp32 sum) - bf16(exact)| <= one ulp + the fp32 summation error bound d u sum|K||P|
-    acc_err = d * 2.0 ** -24 * (np.abs(storage_to_f64(K)) @ np.abs(storage_to_f64(P32)))
+    # |bf16(fp32 sum) - bf16(exact)| <= one ulp + the fp32 summation error bound
+    # (3 d + 1) u sum|K||P| (bf16 keys: 3 d exact products with P's parts)
+    acc_err = (3 * d + 1) * 2.0 ** -24 * (np.abs(storage_to_f64(K)) @
+                                          np.abs(storage_to_f64(P32)))
     big = np.maximum(np.abs(exact), np.abs(got))
     ulp = _ulp_bf16(big) if dtype == "bf16" else big * 2.0 ** -23
     assert np.all(np.abs(got - ref) <= ulp + acc_err[..., :d_store]), \
@@ -121,14 +131,18 @@ def test_project_keys_append(dtype, d, d_store, n, len0, T_cap):
     assert np.isnan(kp_h[:, :, :, :len0]).all() and np.isnan(kp_h[:, :, :, len0 + n:]).all()
 
 
-def test_project_keys_slots():
-    B, Hkv, d, n, T_cap = 1, 2, 128, 5, 64
+@pytest.mark.parametrize("n", [5, 40])
+def test_project_keys_slots(n):
+    """Explicit destination columns (the H2O slot append): a few-token launch and a tiled one
+    (the tiled kernel writes token by token where the columns are not consecutive)."""
+    B, Hkv, d, T_cap = 1, 2, 128, 64
     P64 = gen.make_projection(6, d)
     P32 = torch.from_numpy(P64.astype(np.float32))
     rng = np.random.default_rng(6)
     K = to_storage(rng.standard_normal((B, Hkv, n, d)), "bf16")
     V = to_storage(rng.standard_normal((B, Hkv, n, d)), "bf16")
-    slots = torch.tensor([[[9, 3, 60, 0, 33], [1, 2, 63, 40, 20]]], dtype=torch.int32)
+    perm = [np.random.default_rng(60 + g).permutation(T_cap)[:n] for g in range(Hkv)]
+    slots = torch.from_numpy(np.stack(perm)[None].astype(np.int32))
     kp, v = new_cache(B, Hkv, d, d, T_cap, "bf16")
     cache = aq.make_cache(kp, v, 7)
     aq.aqua_project_keys(cache, K.to(DEV), V.to(DEV), P32.to(DEV), n, slots=slots.to(DEV))
@@ -139,10 +153,27 @@ def test_project_keys_slots():
     for g in range(Hkv):
         for t in range(n):
             col = int(slots[0, g, t])
-            bound = _ulp_bf16(ref[0, g, t]) + d * 2.0 ** -24 * (
+            bound = _ulp_bf16(ref[0, g, t]) + (3 * d + 1) * 2.0 ** -24 * (
                 np.abs(storage_to_f64(K)[0, g, t]) @ np.abs(storage_to_f64(P32)))
             assert np.all(np.abs(kp_h[0, g, :, col] - ref[0, g, t]) <= bound)
             assert np.array_equal(v_h[0, g, col], storage_to_f64(V)[0, g, t])
     written = np.zeros(T_cap, bool)
     written[slots[0, 0].numpy()] = True
     assert np.isnan(kp_h[0, 0, :, ~written]).all()
+
+
+def test_project_keys_bulk_equals_few_token():
+    """bf16 keys projected in one tiled launch and one at a time (the decode step's path) give the
+    same K' bits: both run the library's one bf16 projection."""
+    B, Hkv, d, n = 2, 2, 128, 40
+    P32 = torch.from_numpy(gen.make_projection(8, d).astype(np.float32)).to(DEV)
+    rng = np.random.default_rng(8)
+    K = to_storage(rng.standard_normal((B, Hkv, n, d)), "bf16").to(DEV)
+    kp1, v1 = new_cache(B, Hkv, d, d, 64, "bf16")
+    kp2, v2 = new_cache(B, Hkv, d, d, 64, "bf16")
+    c1, c2 = aq.make_cache(kp1, v1, 0), aq.make_cache(kp2, v2, 0)
+    aq.aqua_project_keys(c1, K, None, P32, n)
+    for t in range(n):
+        aq.aqua_project_keys(c2, K[:, :, t:t + 1].contiguous(), None, P32, 1)
+    torch.cuda.synchronize()
+    assert torch.equal(kp1[..., :n], kp2[..., :n])
