@@ -139,6 +139,19 @@ aqua_status aqua_decode_step(aqua_cache *c, int32_t Hq, const void *q, const voi
                              float scale, float *mass, float *out, float *q_proj_out,
                              uint32_t *mask_out, void *ws, size_t ws_bytes, void *stream);
 
+/* aqua_decode_step without a workspace argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * workspace is a fixed 32 MiB device array inside the library, one per device, held until the
+ * process ends.  Same arguments, results and errors as aqua_decode_step, less ws and ws_bytes;
+ * AQUA_ERR_WORKSPACE if the shape needs more than 32 MiB (aqua_decode_workspace() bytes, less
+ * B * Hq * T_cap * 4 when mass is NULL; e.g. B16 x Hq32 at T_cap 8448 needs 4.3 MB, 21.6 MB
+ * with mass).  It allocates nothing.  Every call on a device shares that device's array, so
+ * calls that may overlap on one device (different streams, threads) race: order them. */
+aqua_status aqua_decode_step_noalloc(aqua_cache *c, int32_t Hq, const void *q, const void *k_new,
+                                     const void *v_new, const float *P, int32_t d_sel, int32_t k,
+                                     float scale, float *mass, float *out, float *q_proj_out,
+                                     uint32_t *mask_out, void *stream);
+
 /* Bytes of workspace aqua_prefill_chunk needs for a chunk of Lq queries (no clearing needed). */
 aqua_status aqua_prefill_workspace(const aqua_cache *c, int32_t Hq, int32_t Lq, size_t *bytes);
 

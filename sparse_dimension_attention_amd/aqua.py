@@ -25,7 +25,8 @@ _STATUS_NAMES = {0: "AQUA_OK", 1: "AQUA_ERR_NULL", 2: "AQUA_ERR_SHAPE", 3: "AQUA
                  7: "AQUA_ERR_HIP"}
 
 EXPORTS = ("aqua_version", "aqua_last_error", "aqua_project_keys", "aqua_select_dims",
-           "aqua_decode_workspace", "aqua_decode", "aqua_decode_step", "aqua_prefill_workspace",
+           "aqua_decode_workspace", "aqua_decode", "aqua_decode_step", "aqua_decode_step_noalloc",
+           "aqua_prefill_workspace",
            "aqua_prefill_chunk", "aqua_h2o_init", "aqua_h2o_victim", "aqua_h2o_step")
 
 
@@ -63,6 +64,8 @@ def load_library() -> ctypes.CDLL:
         "aqua_decode": ([cp, I32, P, P, ctypes.c_float, P, P, P, SZ, P], ctypes.c_int),
         "aqua_decode_step": ([cp, I32, P, P, P, P, I32, I32, ctypes.c_float, P, P, P, P, P, SZ,
                               P], ctypes.c_int),
+        "aqua_decode_step_noalloc": ([cp, I32, P, P, P, P, I32, I32, ctypes.c_float, P, P, P, P,
+                                      P], ctypes.c_int),
         "aqua_prefill_workspace": ([cp, I32, I32, ctypes.POINTER(SZ)], ctypes.c_int),
         "aqua_prefill_chunk": ([cp, I32, P, I32, I32, P, I32, I32, ctypes.c_float, P, P, P, P,
                                 SZ, P], ctypes.c_int),
@@ -156,6 +159,15 @@ def aqua_decode_step(cache: aqua_cache, Hq: int, q, k_new, v_new, P, d_sel: int,
                                            float(scale), _ptr(mass), _ptr(out),
                                            _ptr(q_proj_out), _ptr(mask_out), _ptr(ws), nbytes,
                                            _stream(stream)))
+
+
+def aqua_decode_step_noalloc(cache: aqua_cache, Hq: int, q, k_new, v_new, P, d_sel: int, k: int,
+                             scale: float, out, mass=None, q_proj_out=None, mask_out=None,
+                             stream=None):
+    _check(load_library().aqua_decode_step_noalloc(
+        ctypes.byref(cache), int(Hq), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(P), int(d_sel),
+        int(k), float(scale), _ptr(mass), _ptr(out), _ptr(q_proj_out), _ptr(mask_out),
+        _stream(stream)))
 
 
 def aqua_prefill_workspace(cache: aqua_cache, Hq: int, Lq: int) -> int:

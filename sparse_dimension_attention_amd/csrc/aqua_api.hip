@@ -1,5 +1,6 @@
 // libaqua C ABI: argument validation (before any HIP call), workspace sizing and dispatch to the
 // gfx950 kernels.  The library never allocates device memory and never synchronises.
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -69,6 +70,39 @@ aqua_status check_prefill_cache(const aqua_cache *c, int32_t Hq) {
   return AQUA_OK;
 }
 
+// ---- the workspace of aqua_decode_step_noalloc: a file-scope device array of fixed size, one
+// copy per device that runs the library, held until the process ends.  Host code never passes
+// the array's name to a kernel (in host code it is a stand-in, not a device address): each
+// device's address comes from hipGetSymbolAddress, called once per device with that device
+// current, and is kept in scratch_ptr.  Every call on a device shares its array; nothing in it
+// needs clearing (the arrival counters carry each call's epoch), and calls that overlap on one
+// device race.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+constexpr int kScratchDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::atomic<void *> scratch_ptr[kScratchDevices];
+
+// This device's scratch address (nullptr with the error set if it cannot be had).
+void *device_scratch(aqua_status *st) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kScratchDevices) {
+    *st = e != hipSuccess ? fail(AQUA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e))
+                          : fail(AQUA_ERR_HIP, "device %d: static scratch is kept for devices "
+                                 "0..%d only", dev, kScratchDevices - 1);
+    return nullptr;
+  }
+  void *p = scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !p) {
+    *st = fail(AQUA_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    return nullptr;
+  }
+  scratch_ptr[dev].store(p, std::memory_order_release);
+  return p;
+}
+
 // The cache and workspace fields every decode-path launch takes; S and epoch for this call.
 void fill_decode_args(const aqua_cache *c, int32_t Hq, int32_t len, float scale, float *mass,
                       float *out, void *ws, aqua::DecodeArgs &a) {
@@ -87,6 +121,30 @@ void fill_decode_args(const aqua_cache *c, int32_t Hq, int32_t len, float scale,
   a.S = aqua::decode_splits(c->dtype, Hq / c->Hkv, c->B * c->Hkv, len, aqua::device_cu_count());
   a.qscale = scale * 1.4426950408889634f;  // log2(e): scores are kept in log2 units
   a.epoch = aqua::next_epoch();
+}
+
+// aqua_decode_step once its arguments and workspace are validated
+aqua_status launch_decode_step(aqua_cache *c, int32_t Hq, const void *q, const void *k_new,
+                               const void *v_new, const float *P, int32_t d_sel, int32_t k,
+                               float scale, float *mass, float *out, float *q_proj_out,
+                               uint32_t *mask_out, void *ws, hipStream_t stream) {
+  aqua::DecodeArgs a{};
+  fill_decode_args(c, Hq, c->len + 1, scale, mass, out, ws, a);
+  a.kp_w = c->kp;
+  a.v_w = c->v;
+  a.q_raw = q;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.P = P;
+  a.q_proj_out = q_proj_out;
+  a.mask_out = mask_out;
+  a.d_sel = d_sel;
+  a.k = k;
+  if (aqua_status st =
+          hip_status(aqua::launch_decode_step(c->dtype, a, stream), "aqua_decode_step launch"))
+    return st;
+  c->len += 1;
+  return AQUA_OK;
 }
 
 }  // namespace
@@ -193,25 +251,42 @@ aqua_status aqua_decode_step(aqua_cache *c, int32_t Hq, const void *q, const voi
       aqua::decode_workspace_bytes(c->dtype, c->B, Hq, c->Hkv, c->d_head, c->T_cap);
   if (ws_bytes < need)
     return fail(AQUA_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, need);
+  return launch_decode_step(c, Hq, q, k_new, v_new, P, d_sel, k, scale, mass, out, q_proj_out,
+                            mask_out, ws, static_cast<hipStream_t>(stream));
+}
 
-  aqua::DecodeArgs a{};
-  fill_decode_args(c, Hq, c->len + 1, scale, mass, out, ws, a);
-  a.kp_w = c->kp;
-  a.v_w = c->v;
-  a.q_raw = q;
-  a.k_new = k_new;
-  a.v_new = v_new;
-  a.P = P;
-  a.q_proj_out = q_proj_out;
-  a.mask_out = mask_out;
-  a.d_sel = d_sel;
-  a.k = k;
-  if (aqua_status st = hip_status(
-          aqua::launch_decode_step(c->dtype, a, static_cast<hipStream_t>(stream)),
-          "aqua_decode_step launch"))
-    return st;
-  c->len += 1;
-  return AQUA_OK;
+
+aqua_status aqua_decode_step_noalloc(aqua_cache *c, int32_t Hq, const void *q,
+                                     const void *k_new, const void *v_new, const float *P,
+                                     int32_t d_sel, int32_t k, float scale, float *mass,
+                                     float *out, float *q_proj_out, uint32_t *mask_out,
+                                     void *stream) {
+  g_err[0] = 0;
+  if (aqua_status st = check_cache(c)) return st;
+  if (aqua_status st = check_heads(c, Hq)) return st;
+  if (!q || !k_new || !v_new || !P || !out)
+    return fail(AQUA_ERR_NULL, "q, k_new, v_new, P and out are required");
+  if (!(1 <= k && k <= d_sel && d_sel <= c->d_store))
+    return fail(AQUA_ERR_SHAPE, "need 1 <= k (%d) <= d_sel (%d) <= d_store (%d)", k, d_sel,
+                c->d_store);
+  if (static_cast<int64_t>(c->len) + 1 > c->T_cap)
+    return fail(AQUA_ERR_CAPACITY, "append at len=%d exceeds T_cap=%d", c->len, c->T_cap);
+  if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(P) ||
+      !aligned16(out) || (mass && !aligned16(mass)) || (q_proj_out && !aligned16(q_proj_out)) ||
+      (mask_out && !aligned16(mask_out)))
+    return fail(AQUA_ERR_ALIGN, "all buffers must be 16-byte aligned");
+  // the workspace layout of aqua_decode_step; its last region (scores) only in mass mode
+  size_t need = aqua::decode_workspace_bytes(c->dtype, c->B, Hq, c->Hkv, c->d_head, c->T_cap);
+  if (!mass) need -= static_cast<size_t>(c->B) * Hq * c->T_cap * 4;
+  if (need > kScratchBytes)
+    return fail(AQUA_ERR_WORKSPACE, "this shape needs %zu bytes of workspace; the static scratch "
+                "of aqua_decode_step_noalloc holds %zu (use aqua_decode_step with a workspace)",
+                need, kScratchBytes);
+  aqua_status st = AQUA_OK;
+  void *ws = device_scratch(&st);
+  if (!ws) return st;
+  return launch_decode_step(c, Hq, q, k_new, v_new, P, d_sel, k, scale, mass, out, q_proj_out,
+                            mask_out, ws, static_cast<hipStream_t>(stream));
 }
 
 aqua_status aqua_prefill_workspace(const aqua_cache *c, int32_t Hq, int32_t Lq, size_t *bytes) {

@@ -30,7 +30,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 12
+    assert len(names) == 13
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(aq.EXPORTS)
@@ -230,3 +230,23 @@ def _h2o_step(lib, cache, Hq=8, k=64, t_new=300, recent=16, mass=FAKE, slot_pos=
 def test_h2o_step_rejects(lib, kw, args, status):
     c = _cache(**dict(dict(d_store=96, T_cap=256, len=256), **kw))
     assert _h2o_step(lib, c, **args) == status
+
+
+@pytest.mark.parametrize("kw,args,status", [
+    (dict(), dict(Hq=6), A.AQUA_ERR_SHAPE),
+    (dict(len=256), dict(), A.AQUA_ERR_CAPACITY),
+    (dict(), dict(q=None), A.AQUA_ERR_NULL),
+    (dict(), dict(k=0), A.AQUA_ERR_SHAPE),
+    (dict(), dict(out=FAKE + 4), A.AQUA_ERR_ALIGN),
+    # more workspace than the 32 MiB static scratch: 64 x 128 heads x 8192 tokens of scores
+    (dict(B=64, Hkv=32, T_cap=8192, len=100), dict(Hq=128, mass=FAKE), A.AQUA_ERR_WORKSPACE),
+])
+def test_decode_step_noalloc_rejects(lib, kw, args, status):
+    c = _cache(**kw)
+    a = dict(Hq=8, q=FAKE, k=96, out=FAKE, mass=None)
+    a.update(args)
+    assert lib.aqua_decode_step_noalloc(ctypes.byref(c), a["Hq"], a["q"], FAKE, FAKE, FAKE, 128,
+                                        a["k"], 0.1, a["mass"], a["out"], None, None,
+                                        None) == status
+    assert lib.aqua_last_error().decode() != ""
+    assert c.len == kw.get("len", 10)
