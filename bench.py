@@ -9,22 +9,28 @@ calls (aqua_project_keys + aqua_select_dims + aqua_decode) is timed too and repo
 Inputs are seeded synthetic tensors resident in HBM before timing starts.
 
 Prints one JSON line.  value = query-head x token pairs attended per second over the whole step;
-roofline = algorithmic HBM bytes of the step's launch (the K' rows of each KV group's mask union
-and all of V over the context, raw q, the new token in and out, P, output) / its average
-duration from HIP events on the launch stream.
-cpu_baseline = the fp64 oracle timed on the host cores on a bounded sample of the same step.
+roofline = algorithmic HBM bytes of the whole step (the K' rows of each KV group's mask union and
+all of V over the context, raw q, the new token in and out, P, output) / the whole step's GPU time
+(the faster form's launches, K steps back to back between two HIP events on their stream);
+measured_peak_gbs = the box's streaming-read bandwidth from aqua_stream_read_probe, beside the
+vendor's 8 TB/s.  cpu_baseline = the fp64 oracle timed on the host cores on a bounded sample of the
+same step; cpu_oracle = the oracle on bounded samples of the other workloads and on one thread.
 
-Two further workloads are measured beside the headline and reported in the same line:
+Further workloads are measured beside the headline and reported in the same line:
  * prefill: causal chunked prefill of 16384 tokens in 8 chunks of 2048 (32 heads, k=96), each
-   chunk = aqua_prefill_chunk (selection + MFMA attention); executed-useful flops
-   Hq * 4 d * T (T + 1) / 2 against the bf16 MFMA peak;
+   chunk = aqua_project_keys of its 2048 keys + aqua_prefill_chunk (selection + MFMA
+   attention); executed-useful flops Hq * 4 d * T (T + 1) / 2 against the bf16 MFMA peak;
  * h2o: 64 heavy-hitter decode steps over a compact AQUA-Memory cache of 1024 heavy + 256
    recent slots (32768-token context, 96 stored dims, top-64), each step = eviction, slot
    append, selection and mass-mode decode; timed from a Python loop and as a replayed HIP graph
-   of the 64 steps (launch-bound: about 4.6 MB per step, cache-resident);
+   of the 64 steps (launch-bound: about 4.6 MB per step, cache-resident); the starting state
+   (aqua_h2o_init) timed once;
  * long_decode: decode over a 131072-token context (B=1) at k = 128, 96, 64, 32 (GB/s and the
    speedup over k=128), and the same step over shorter prefixes of that context (T = 256 ..
    131072), where the gain of fewer kept dims over k=128 sets in;
+ * ragged: the headline step at context lengths that leave a partial last split (4097 .. 8193);
+ * shard: the headline step on one GPU's share under 8-way KV-head sharding (B=16, 4 query heads,
+   1 KV head);
  * memory_cut: AQUA-Memory's static cut (K' stored on 96 or 64 of 128 dims, top-64 or top-48 of
    them kept) at both decode shapes: decode kernel time, GB/s, KV bytes, speedup over the full
    cache;
@@ -87,12 +93,12 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_llama8b_b16_t8192_hbm_traf
 
 
 def kernel_source_hash() -> str:
-    """sha256[:16] over the decode kernel's sources (decode.hip, then aqua_internal.h)."""
+    """sha256[:16] over the decode kernel's sources (decode_kernels.h, then aqua_internal.h)."""
     import hashlib
 
     csrc = os.path.join(ROOT, "sparse_dimension_attention_amd", "csrc")
     h = hashlib.sha256()
-    for f in ("decode.hip", "aqua_internal.h"):
+    for f in ("decode_kernels.h", "aqua_internal.h"):
         h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -151,6 +157,120 @@ def cpu_baseline(c: dict, n_groups: int, reps: int):
                       f"host has {os.cpu_count()} CPUs, affinity {len(os.sched_getaffinity(0))}"}
 
 
+def cpu_oracle_timings():
+    """The oracle on bounded samples of the other workloads (all host threads its BLAS takes),
+    and the tiny decode and a small decode-step sample on one thread.  Each figure is the work of
+    the sample over its wall time; the sample is stated with it."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    from oracle import aqua_oracle as O
+    from synth import storage_to_f64
+
+    threads = int(max([x.get("num_threads", 1) for x in threadpool_info()] or [1]))
+    res = {"threads": threads, "host_cpus": os.cpu_count(),
+           "affinity": len(os.sched_getaffinity(0))}
+
+    def decode_groups(c, groups, T):
+        inp = make_decode_inputs(c, groups=groups)
+        P = storage_to_f64(inp["P"])
+        q, K, V = (storage_to_f64(inp[x]) for x in ("q", "k", "v"))
+        t0 = time.perf_counter()
+        for i in range(len(groups)):
+            Kp = O.project_keys_stored(K[i, :T], P, c["dtype"], c["d_store"])
+            qp = O.project(q[i], P)
+            m = O.select(qp, c["d_sel"], c["k"])
+            for h in range(qp.shape[0]):
+                O.attend(qp[h], m[h], Kp, V[i, :T], 1 / math.sqrt(c["d"]))
+        return time.perf_counter() - t0
+
+    # long decode (131072 tokens, k = 96): one of the 8 KV groups, keys projected in the timing
+    c3 = config(3)
+    t = decode_groups(c3, [(0, 0)], c3["T"])
+    G = c3["Hq"] // c3["Hkv"]
+    res["long_decode"] = {"value": G * c3["T"] / t, "unit": "q-head·tokens/s", "seconds": t,
+                          "sample": "1 of 8 KV groups of one 131072-token decode step at k=96 "
+                                    "(131072 keys projected, 4 queries projected, selected and "
+                                    "attended)"}
+    # chunked prefill: one KV group's 16384 keys projected, and 64 query rows of one head at
+    # positions spread over the context (each selects and attends causally)
+    c4 = config(4)
+    inp = make_prefill_inputs(c4, heads=[(0, 0)])
+    P = storage_to_f64(inp["P"])
+    K, V = (storage_to_f64(inp[x][0, 0]) for x in ("k", "v"))
+    q = storage_to_f64(inp["q"][0])  # [T][d] of head (0, 0)
+    t0 = time.perf_counter()
+    Kp = O.project_keys_stored(K, P, "bf16", 128)
+    t_proj = time.perf_counter() - t0
+    rows = np.linspace(0, c4["T"] - 1, 64).astype(int)
+    t0 = time.perf_counter()
+    for p in rows:
+        qp = O.project(q[p], P)
+        m = O.select(qp[None], 128, c4["k"])[0]
+        O.attend(qp, m, Kp[:p + 1], V[:p + 1], 1 / math.sqrt(128))
+    t_rows = time.perf_counter() - t0
+    full_s = c4["Hkv"] * t_proj + c4["Hq"] * c4["T"] / len(rows) * t_rows
+    flops = c4["Hq"] * 4 * 128 * c4["T"] * (c4["T"] + 1) / 2
+    res["prefill"] = {"value": flops / full_s / 1e12, "unit": "TFLOP/s (executed-useful)",
+                      "extrapolated_seconds": full_s, "sample_seconds": t_proj + t_rows,
+                      "sample": "1 of 8 KV groups' 16384 keys projected, and 64 query rows of "
+                                "one head at positions 0..16383 (each projected, selected and "
+                                "attended causally); extrapolated to the 8 chunks of 32 heads"}
+    # H2O: one KV group's full run (seeding decode over 32768 tokens, then the 64 steps)
+    c5 = config(5)
+    inp = make_h2o_inputs(c5, workers=16)
+    G5 = c5["Hq"] // c5["Hkv"]
+    f = {x: storage_to_f64(inp[x]) for x in ("P", "q_seed", "q_steps", "k", "v", "k_steps",
+                                             "v_steps")}
+    t0 = time.perf_counter()
+    O.h2o_run(f["P"], f["q_seed"][0, :G5], f["q_steps"][:, 0, :G5], f["k"][0, 0], f["v"][0, 0],
+              f["k_steps"][:, 0, 0], f["v_steps"][:, 0, 0], c5["d_sel"], c5["k"],
+              c5["d_store"], c5["heavy"], c5["recent"], 1 / math.sqrt(128), kv_dtype="bf16")
+    t = time.perf_counter() - t0
+    res["h2o"] = {"value": t / c5["steps"] * 1e6, "unit": "us per step per KV group",
+                  "seconds": t, "sample": "1 of 8 KV groups: the seeding decode over 32768 "
+                                          "tokens and the 64 steps (full-recompute heavy set)"}
+    # one thread: the tiny fp32 decode, and 4 groups of the benchmark step
+    with threadpool_limits(1):
+        c1 = config(1)
+        t = decode_groups(c1, [(0, 0)], c1["T"])
+        res["tiny_decode_1thread"] = {"value": c1["T"] / t, "unit": "q-head·tokens/s",
+                                      "seconds": t, "cores": 1,
+                                      "sample": "the whole tiny fp32 decode (T=256, k=48)"}
+        c2 = config(2)
+        t = decode_groups(c2, [(0, 0), (5, 3), (9, 6), (15, 7)], c2["T"])
+        res["decode_1thread"] = {"value": 4 * 4 * c2["T"] / t, "unit": "q-head·tokens/s",
+                                 "seconds": t, "cores": 1,
+                                 "sample": "4 of 128 KV groups of the benchmark step (keys "
+                                           "projected, 16 queries selected and attended)"}
+    return res
+
+
+def bench_stream_probe(dev, reps: int = 20):
+    """The box's streaming-read bandwidth: aqua_stream_read_probe over a 2 GiB buffer (8x the
+    last-level cache), median of reps per grid size, the best grid size reported."""
+    nbytes = 2 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    res = {}
+    for blocks in (512, 1024, 2048, 4096, 8192):
+        sink = torch.empty(blocks, dtype=torch.int32, device=dev)
+        for _ in range(3):
+            aq.aqua_stream_read_probe(buf, blocks, sink)
+        us = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            aq.aqua_stream_read_probe(buf, blocks, sink)
+            e1.record()
+            torch.cuda.synchronize()
+            us.append(e0.elapsed_time(e1) * 1e3)
+        res[str(blocks)] = nbytes / (statistics.median(us) * 1e-6) / 1e9
+    del buf
+    best = max(res.values())
+    return {"gbs": best, "by_workgroups": res, "bytes": nbytes, "reps": reps,
+            "timing": "HIP events around one aqua_stream_read_probe launch, median of reps"}
+
+
 def copy_probe(nbytes: int, reps: int):
     """A plain device copy of known size (for scaling HBM byte counters)."""
     src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
@@ -162,7 +282,10 @@ def copy_probe(nbytes: int, reps: int):
 
 
 def bench_prefill(dev, reps: int):
-    """The 16384-token causal prefill in 8 chunks of 2048 (inputs resident in HBM)."""
+    """The 16384-token causal prefill in 8 chunks of 2048, each chunk = aqua_project_keys of its
+    2048 new keys (appended to the cache) then aqua_prefill_chunk of its 2048 queries (inputs
+    resident in HBM).  Also timed: the attention calls alone over a filled cache, and each part per
+    chunk."""
     c = config(4)
     B, Hq, Hkv, d, T, k, chunk = c["B"], c["Hq"], c["Hkv"], c["d"], c["T"], c["k"], c["chunk"]
     inp = make_prefill_inputs(c, workers=16)
@@ -170,53 +293,68 @@ def bench_prefill(dev, reps: int):
     kp = torch.empty(B, Hkv, d, T, dtype=torch.bfloat16, device=dev)
     v = torch.empty(B, Hkv, T, d, dtype=torch.bfloat16, device=dev)
     cache = aq.make_cache(kp, v, 0)
-    aq.aqua_project_keys(cache, inp["k"].to(dev), inp["v"].to(dev), P, T)
-    qs = [inp["q"][:, :, c0:c0 + chunk].contiguous().to(dev) for c0 in range(0, T, chunk)]
+    chunks = range(0, T, chunk)
+    qs = [inp["q"][:, :, c0:c0 + chunk].contiguous().to(dev) for c0 in chunks]
+    ks = [inp["k"][:, :, c0:c0 + chunk].contiguous().to(dev) for c0 in chunks]
+    vs = [inp["v"][:, :, c0:c0 + chunk].contiguous().to(dev) for c0 in chunks]
     del inp
     out = torch.empty(B, Hq, chunk, d, device=dev)
-    ws = torch.empty(aq.aqua_prefill_workspace(cache, Hq, chunk), dtype=torch.uint8, device=dev)
+    ws = torch.empty(aq.aqua_prefill_workspace(aq.make_cache(kp, v, T), Hq, chunk),
+                     dtype=torch.uint8, device=dev)
     scale = 1.0 / math.sqrt(d)
 
-    def run(events):
-        for i, c0 in enumerate(range(0, T, chunk)):
-            if events is not None:
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record()
+    def run(events, project=True):
+        cache.len = 0 if project else T
+        for i, c0 in enumerate(chunks):
+            if project:
+                if events is not None:
+                    events.append([torch.cuda.Event(enable_timing=True) for _ in range(3)])
+                    events[-1][0].record()
+                aq.aqua_project_keys(cache, ks[i], vs[i], P, chunk)
+                if events is not None:
+                    events[-1][1].record()
             aq.aqua_prefill_chunk(cache, Hq, qs[i], chunk, c0, P, d, k, scale, out, ws=ws)
             if events is not None:
-                e1.record()
-                events.append((e0, e1))
+                events[-1][2].record()
+
+    def timed(project):
+        totals = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            run(None, project)
+            e1.record()
+            torch.cuda.synchronize()
+            totals.append(e0.elapsed_time(e1))
+        return float(np.median(totals)), totals
 
     # warm-up passes: the GPU's clocks ramp over the first tens of milliseconds of this load
     # (measured: consecutive passes 2.75, 2.54, 2.43, 2.38, 2.35, 2.34, 2.32 ms from cold)
     for _ in range(WARMUP_PREFILL_PASSES):
         run(None)
     torch.cuda.synchronize()
-    # the whole prefill (8 chunk calls back to back) between two events, per rep; then one rep
-    # with events around every call for the per-chunk breakdown
-    totals = []
-    for _ in range(reps):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        run(None)
-        e1.record()
-        torch.cuda.synchronize()
-        totals.append(e0.elapsed_time(e1))
+    ms, totals = timed(True)
+    ms_attn, totals_attn = timed(False)
     ev = []
     run(ev)
     torch.cuda.synchronize()
-    per_chunk = [a.elapsed_time(b) for a, b in ev]
-    ms = float(np.median(totals))
+    proj_ms = [a.elapsed_time(b) for a, b, _ in ev]
+    attn_ms = [b.elapsed_time(c_) for _, b, c_ in ev]
     flops = Hq * 4 * d * T * (T + 1) / 2 * B
     tflops = flops / (ms * 1e-3) / 1e12
+    tflops_attn = flops / (ms_attn * 1e-3) / 1e12
     return {"workload": c["name"], "chunks": T // chunk, "chunk": chunk, "ms": ms,
-            "ms_reps": totals, "per_chunk_ms": per_chunk, "reps": reps,
+            "ms_reps": totals, "ms_attention_only": ms_attn, "ms_attention_only_reps": totals_attn,
+            "per_chunk_project_keys_ms": proj_ms, "per_chunk_prefill_ms": attn_ms, "reps": reps,
             "flops_executed_useful": flops, "tflops": tflops,
             "frac_bf16_mfma_peak": tflops / BF16_MFMA_PEAK_TFLOPS,
+            "tflops_attention_only": tflops_attn,
+            "frac_bf16_mfma_peak_attention_only": tflops_attn / BF16_MFMA_PEAK_TFLOPS,
             "warmup_passes": WARMUP_PREFILL_PASSES,
-            "timing": "HIP events around the 8 aqua_prefill_chunk calls on the launch stream, "
-                      "median of reps after the warm-up passes; per_chunk_ms from events around "
-                      "each call in one more pass"}
+            "timing": "ms: HIP events around the whole prefill, 8 x (aqua_project_keys of the "
+                      "chunk's 2048 keys + aqua_prefill_chunk), median of reps after the warm-up "
+                      "passes; ms_attention_only: the 8 aqua_prefill_chunk calls over the filled "
+                      "cache; per-chunk figures from events around each call in one more pass"}
 
 
 def run_us(fn, n: int) -> float:
@@ -229,6 +367,68 @@ def run_us(fn, n: int) -> float:
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) * 1e3 / n
+
+
+def bench_shard(dev, steps: int, warmup: int):
+    """One GPU's share of the benchmark step under 8-way KV-head sharding (the usual 8-GPU layout
+    of this model): B=16, 4 query heads, 1 KV head, T=8192 (capacity T + 256), k=96.  The whole
+    step (aqua_decode_step) K times back to back between two HIP events; GB/s on its algorithmic
+    bytes."""
+    c = config(2, Hq=4, Hkv=1)
+    B, Hq, Hkv, d, T, k = c["B"], c["Hq"], c["Hkv"], c["d"], c["T"], c["k"]
+    inp = make_decode_inputs(c, workers=16)
+    P = inp["P"].to(dev)
+    T_cap = T + CAP_SLACK
+    kp = torch.empty(B, Hkv, d, T_cap, dtype=torch.bfloat16, device=dev)
+    v = torch.empty(B, Hkv, T_cap, d, dtype=torch.bfloat16, device=dev)
+    cache = aq.make_cache(kp, v, 0)
+    aq.aqua_project_keys(cache, inp["k"][:, :, :T - 1].contiguous().to(dev),
+                         inp["v"][:, :, :T - 1].contiguous().to(dev), P, T - 1)
+    q = inp["q"].to(dev)
+    k_new = inp["k"][:, :, T - 1].contiguous().to(dev)
+    v_new = inp["v"][:, :, T - 1].contiguous().to(dev)
+    out = torch.empty(B, Hq, d, device=dev)
+    mask = torch.empty(B, Hq, d // 32, dtype=torch.int32, device=dev)
+    ws = torch.empty(aq.aqua_decode_workspace(cache, Hq), dtype=torch.uint8, device=dev)
+
+    def step():
+        cache.len = T - 1
+        aq.aqua_decode_step(cache, Hq, q, k_new, v_new, P, d, k, 1.0 / math.sqrt(d), out, ws,
+                            mask_out=mask)
+
+    for _ in range(warmup):
+        step()
+    us = run_us(step, steps)
+    U = union_rows(mask.cpu().numpy(), B, Hkv, Hq // Hkv, d, d)
+    nbytes = step_bytes(U, c, T)
+    return {"workload": "llama8b_decode_bf16_b16_t8192_one_kv_head_shard", "B": B, "Hq": Hq,
+            "Hkv": Hkv, "T": T, "T_cap": T_cap, "k": k, "step_us": us, "bytes": nbytes,
+            "gbs": nbytes / (us * 1e-6) / 1e9,
+            "frac_hbm_peak": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "q_head_tokens_per_s": B * Hq * T / (us * 1e-6),
+            "timing": "aqua_decode_step, K launches back to back between two HIP events"}
+
+
+def bench_ragged(cache, q, k_new, v_new, P, c, ws, out, mask, steps: int, warmup: int):
+    """The headline step at context lengths that leave a ragged last split, on the headline's
+    cache (which holds 8192 tokens and room for 256 more): per length, the whole step
+    (aqua_decode_step) K times back to back between two HIP events, and its GB/s."""
+    B, Hq, Hkv, d, k = c["B"], c["Hq"], c["Hkv"], c["d"], c["k"]
+    res = {}
+    for Tn in (4097, 5000, 6000, 7000, 8193):
+        def step():
+            cache.len = Tn - 1
+            aq.aqua_decode_step(cache, Hq, q, k_new, v_new, P, d, k, 1.0 / math.sqrt(d), out, ws,
+                                mask_out=mask.view(B, Hq, d // 32))
+
+        for _ in range(warmup):
+            step()
+        us = run_us(step, steps)
+        U = union_rows(mask.cpu().numpy().reshape(B, Hq, d // 32), B, Hkv, Hq // Hkv, d, d)
+        nbytes = step_bytes(U, c, Tn)
+        res[str(Tn)] = {"step_us": us, "bytes": nbytes, "gbs": nbytes / (us * 1e-6) / 1e9}
+    return {"workload": "llama8b_decode_bf16_b16_ragged", "by_T": res,
+            "timing": "aqua_decode_step, K launches back to back between two HIP events"}
 
 
 def bench_long_decode(dev, steps: int, warmup: int):
@@ -476,6 +676,13 @@ def bench_h2o(dev, reps: int):
     ws = torch.zeros(aq.aqua_decode_workspace(full, Hq), dtype=torch.uint8, device=dev)
     aq.aqua_decode(full, Hq, qp, mask, scale, out, ws, mass=mass)  # the seeding step
     st = H2OCache.from_full(kp, v, mass, T, c["heavy"], c["recent"])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    H2OCache.from_full(kp, v, mass, T, c["heavy"], c["recent"])
+    e1.record()
+    torch.cuda.synchronize()
+    init_us = e0.elapsed_time(e1) * 1e3
     # the same starting state for the fused step (one launch per step, aqua_h2o_step)
     st_f = H2OCache(st.kp.clone(), st.v.clone(), st.slot_pos.clone(), st.mass.clone(),
                     st.heavy, st.recent)
@@ -524,7 +731,8 @@ def bench_h2o(dev, reps: int):
             rec["graph_error"] = str(exc)[:200]
         return statistics.median(loop_us), graph
 
-    rec = {"workload": c["name"], "steps": S, "slots": c["heavy"] + c["recent"]}
+    rec = {"workload": c["name"], "steps": S, "slots": c["heavy"] + c["recent"],
+           "init_us": init_us}
     rec["us_per_step_python_loop"], rec["us_per_step_graph"] = timed(st, False)
     rec["fused_us_per_step_python_loop"], rec["fused_us_per_step_graph"] = timed(st_f, True)
     U = union_rows(mask.cpu().numpy().reshape(B, Hq, d // 32), B, Hkv, Hq // Hkv, d,
@@ -539,7 +747,9 @@ def bench_h2o(dev, reps: int):
     rec["bytes_per_step"] = nbytes
     rec["gbs"] = nbytes / (best * 1e-6) / 1e9
     rec["note"] = ("latency-bound (working set cache-resident): four launches per step, or one "
-                   "(fused_*, aqua_h2o_step); GB/s is algorithmic bytes per step / best step time")
+                   "(fused_*, aqua_h2o_step); GB/s is algorithmic bytes per step / best step time; "
+                   "init_us: aqua_h2o_init (heavy-hitter selection over 32512 positions and the "
+                   "gather of 1280 slots per KV group), HIP events around one call")
     return rec
 
 
@@ -550,15 +760,15 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--cpu-groups", type=int, default=48)
     ap.add_argument("--cpu-reps", type=int, default=3)
-    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timings")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES")
     ap.add_argument("--only", choices=("fused", "three"), default=None,
                     help="run one step implementation only, untimed (for counter runs)")
     ap.add_argument("--no-secondary", action="store_true",
-                    help="skip the prefill and H2O workloads")
+                    help="skip the workloads beside the headline")
     ap.add_argument("--secondary-only",
-                    choices=("prefill", "h2o", "long", "memory", "retention"), default=None,
-                    help="run only that workload and print its record (for profiler runs)")
+                    choices=("prefill", "h2o", "long", "memory", "retention", "shard", "probe"),
+                    default=None, help="run only that workload and print its record")
     ap.add_argument("--secondary-reps", type=int, default=5)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -576,15 +786,14 @@ def main():
 
     dev = torch.device("cuda:0")
     if args.secondary_only:
-        if args.secondary_only == "long":
-            r = bench_long_decode(dev, min(args.steps, 50), min(args.warmup, 10))
-        elif args.secondary_only == "memory":
-            r = bench_memory_cut(dev, min(args.steps, 50), min(args.warmup, 10))
-        elif args.secondary_only == "retention":
-            r = bench_retention(dev)
-        else:
-            fn = bench_prefill if args.secondary_only == "prefill" else bench_h2o
-            r = fn(dev, args.secondary_reps)
+        s_steps, s_warm = min(args.steps, 50), min(args.warmup, 10)
+        r = {"prefill": lambda: bench_prefill(dev, args.secondary_reps),
+             "h2o": lambda: bench_h2o(dev, args.secondary_reps),
+             "long": lambda: bench_long_decode(dev, s_steps, s_warm),
+             "memory": lambda: bench_memory_cut(dev, s_steps, s_warm),
+             "retention": lambda: bench_retention(dev),
+             "shard": lambda: bench_shard(dev, s_steps, s_warm),
+             "probe": lambda: bench_stream_probe(dev)}[args.secondary_only]()
         print(json.dumps({args.secondary_only: r}))
         return
     c = config(2)
@@ -609,92 +818,60 @@ def main():
     qp = torch.empty(B * Hq, d, device=dev)
     mask = torch.empty(B * Hq, d // 32, dtype=torch.int32, device=dev)
     out = torch.empty(B, Hq, d, device=dev)
-    ws = torch.zeros(aq.aqua_decode_workspace(cache, Hq), dtype=torch.uint8, device=dev)
+    ws = torch.empty(aq.aqua_decode_workspace(cache, Hq), dtype=torch.uint8, device=dev)
     scale = 1.0 / math.sqrt(d)
     torch.cuda.synchronize()
+
+    def step(path: str):
+        cache.len = T - 1
+        if path == "three":
+            aq.aqua_project_keys(cache, k_new[:, :, None], v_new[:, :, None], P, 1)
+            aq.aqua_select_dims(q.reshape(B * Hq, d), P, d, k, qp, mask)
+            aq.aqua_decode(cache, Hq, qp, mask, scale, out, ws)
+        else:
+            aq.aqua_decode_step(cache, Hq, q, k_new, v_new, P, d, k, scale, out, ws,
+                                mask_out=mask.view(B, Hq, d // 32))
+
     if args.only:
         # a short run of one path only (for counter collection under rocprofv3)
         for _ in range(args.steps):
-            cache.len = T - 1
-            if args.only == "three":
-                aq.aqua_project_keys(cache, k_new[:, :, None], v_new[:, :, None], P, 1)
-                aq.aqua_select_dims(q.reshape(B * Hq, d), P, d, k, qp, mask)
-                aq.aqua_decode(cache, Hq, qp, mask, scale, out, ws)
-            else:
-                aq.aqua_decode_step(cache, Hq, q, k_new, v_new, P, d, k, scale, out, ws)
+            step(args.only)
         torch.cuda.synchronize()
         print(json.dumps({"only": args.only, "steps": args.steps}))
         return
 
     # Two implementations of the same step; both are timed, the faster one is the headline.
     #  fused: aqua_decode_step (one launch);  three: aqua_project_keys + aqua_select_dims +
-    #  aqua_decode.  The timed region runs K bare steps: an event record is a marker packet on
-    #  the stream, and the two around a launch cost ~6 us of GPU time per step themselves.  The
-    #  dominant launch (the decode kernel) is then timed live over K more steps, with HIP events
-    #  recorded just before and after it on its stream.
-    def run(path: str, n: int, events: list | None):
-        for i in range(n):
-            cache.len = T - 1
-            if path == "three":
-                aq.aqua_project_keys(cache, k_new[:, :, None], v_new[:, :, None], P, 1)
-                aq.aqua_select_dims(q.reshape(B * Hq, d), P, d, k, qp, mask)
-            if events is not None:
-                events[i][0].record()
-            if path == "three":
-                aq.aqua_decode(cache, Hq, qp, mask, scale, out, ws)
-            else:
-                aq.aqua_decode_step(cache, Hq, q, k_new, v_new, P, d, k, scale, out, ws,
-                                    mask_out=mask.view(B, Hq, d // 32))
-            if events is not None:
-                events[i][1].record()
-
+    #  aqua_decode.  The timed region runs K bare steps between two synchronizations (value,
+    #  ms_per_step); the GPU time of a step (roofline.achieved) is K steps back to back between two
+    #  HIP events on their stream.  An event is a marker packet of its own: events around every
+    #  launch would add ~6 us of GPU time to each interval.
     res = {}
     for path in ("fused", "three"):
-        run(path, args.warmup, None)
+        for _ in range(args.warmup):
+            step(path)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        run(path, args.steps, None)
+        for _ in range(args.steps):
+            step(path)
         torch.cuda.synchronize()
         ms = (time.perf_counter() - t0) * 1e3 / args.steps
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
-        t1 = time.perf_counter()
-        run(path, args.steps, ev)
-        torch.cuda.synchronize()
-        ms_ev = (time.perf_counter() - t1) * 1e3 / args.steps
-        k_ms = [a.elapsed_time(b) for a, b in ev]
-        res[path] = (ms, k_ms, ms_ev)
+        gpu_us = run_us(lambda: step(path), args.steps)
+        res[path] = (ms, gpu_us)
     best = min(res, key=lambda p: res[p][0])
-    ms_per_step, k_ms, _ = res[best]
-
-    # The dominant launch's duration: that launch alone, K times back to back on its stream
-    # between two events.  Events around each launch (k_ms above) add a marker packet's cost,
-    # ~6 us, to every interval; over a run of launches only the launch gaps remain.
-    def launch_only():
-        if best == "three":
-            cache.len = T
-            aq.aqua_decode(cache, Hq, qp, mask, scale, out, ws)
-        else:
-            cache.len = T - 1
-            aq.aqua_decode_step(cache, Hq, q, k_new, v_new, P, d, k, scale, out, ws,
-                                mask_out=mask.view(B, Hq, d // 32))
-
-    for _ in range(args.warmup):
-        launch_only()
-    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    r0.record()
-    for _ in range(args.steps):
-        launch_only()
-    r1.record()
-    torch.cuda.synchronize()
-    k_avg_s = r0.elapsed_time(r1) * 1e-3 / args.steps
+    ms_per_step, step_gpu_us = res[best]
+    # the decode kernel of the three-launch form alone, on the step's masks (for reference)
+    cache.len = T
+    decode_us = run_us(lambda: aq.aqua_decode(cache, Hq, qp, mask, scale, out, ws), args.steps)
 
     U = union_rows(mask.cpu().numpy().reshape(B, Hq, d // 32), B, Hkv, G, d, c["d_store"])
-    nbytes = step_bytes(U, c, T) if best == "fused" else decode_bytes(U, c, T)
-    achieved = nbytes / k_avg_s / 1e9
+    nbytes = step_bytes(U, c, T)
+    dbytes = decode_bytes(U, c, T)
+    achieved = nbytes / (step_gpu_us * 1e-6) / 1e9
     value = B * Hq * T / (ms_per_step * 1e-3)
-    kname = ("decode_kernel<bf16, d=128, G=4, fused>" if best == "fused"
-             else "decode_kernel<bf16, d=128, G=4>")
+    probe = bench_stream_probe(dev)
+    kname = ("decode_kernel<bf16, d=128, G=4, NW=8, fused> (aqua_decode_step)" if best == "fused"
+             else "project_keys + select + decode_kernel<bf16, d=128, G=4, NW=8> (three launches)")
     rec = {
         "metric": METRIC, "value": value, "unit": "q-head·tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
@@ -704,36 +881,46 @@ def main():
                    "T_cap": T_cap, "k": k, "storage": c["dtype"], "step": best,
                    "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_bytes(best)},
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_bytes(best),
+                     "measured_peak_gbs": probe["gbs"],
+                     "frac_of_measured_peak": achieved / probe["gbs"]},
         "kernel": kname,
-        "kernel_us": k_avg_s * 1e6,
-        "kernel_us_launch_events": statistics.mean(k_ms) * 1e3,
-        "kernel_us_launch_events_p10_p90": [float(np.percentile(k_ms, 10) * 1e3),
-                                            float(np.percentile(k_ms, 90) * 1e3)],
-        "bytes_per_launch": nbytes,
+        "step_gpu_us": step_gpu_us,
+        "bytes_per_step": nbytes,
         "mean_union_rows": float(U.mean()),
         "ms_per_step_by_path": {p: res[p][0] for p in res},
-        "kernel_us_by_path": {p: statistics.mean(res[p][1]) * 1e3 for p in res},
-        "ms_per_step_with_kernel_events": {p: res[p][2] for p in res},
-        "timing": "value, ms_per_step: K bare steps between two synchronizations; kernel_us "
-                  "(roofline.achieved): the decode launch alone, K times back to back on its "
-                  "stream between two HIP events; kernel_us_launch_events: HIP events around "
-                  "each decode launch over K more steps (each pair adds ~6 us of its own)",
+        "step_gpu_us_by_path": {p: res[p][1] for p in res},
+        "decode_kernel_us": decode_us,
+        "decode_kernel_bytes": dbytes,
+        "decode_kernel_frac": dbytes / (decode_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+        "stream_probe": probe,
+        "timing": "value, ms_per_step: K bare steps between two synchronizations; step_gpu_us "
+                  "(roofline.achieved): the same step's launches, K steps back to back on their "
+                  "stream between two HIP events; decode_kernel_us: aqua_decode alone on the "
+                  "step's masks over the 8192 tokens, the same way (decode_kernel_frac: its own "
+                  "algorithmic bytes over that time, against 8 TB/s)",
     }
+    if not args.no_secondary:
+        rec["ragged"] = bench_ragged(cache, q, k_new, v_new, P, c, ws, out, mask,
+                                     min(args.steps, 50), min(args.warmup, 10))
     del kp, v, cache, ws
     torch.cuda.empty_cache()
     if not args.no_secondary:
+        s_steps, s_warm = min(args.steps, 50), min(args.warmup, 10)
+        rec["shard"] = bench_shard(dev, s_steps, s_warm)
+        torch.cuda.empty_cache()
         rec["prefill"] = bench_prefill(dev, args.secondary_reps)
         torch.cuda.empty_cache()
         rec["h2o"] = bench_h2o(dev, args.secondary_reps)
         torch.cuda.empty_cache()
-        rec["long_decode"] = bench_long_decode(dev, min(args.steps, 50), min(args.warmup, 10))
+        rec["long_decode"] = bench_long_decode(dev, s_steps, s_warm)
         torch.cuda.empty_cache()
-        rec["memory_cut"] = bench_memory_cut(dev, min(args.steps, 50), min(args.warmup, 10))
+        rec["memory_cut"] = bench_memory_cut(dev, s_steps, s_warm)
         torch.cuda.empty_cache()
         rec["retention"] = bench_retention(dev)
     if not args.no_cpu:
         rec["cpu_baseline"] = cpu_baseline(c, args.cpu_groups, args.cpu_reps)
+        rec["cpu_oracle"] = cpu_oracle_timings()
     print(json.dumps(rec))
 
 

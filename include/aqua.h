@@ -227,6 +227,14 @@ aqua_status aqua_h2o_step(aqua_cache *c, int32_t Hq, const void *q, const void *
                           int32_t recent, int32_t *victim, float *out, float *q_proj_out,
                           uint32_t *mask_out, void *ws, size_t ws_bytes, void *stream);
 
+/* Diagnostics.  Streaming-read probe: reads `bytes` of buf once (16-byte non-temporal loads,
+ * the decode kernel's access, sixteen in flight per lane; `blocks` workgroups of 256 threads,
+ * each over one contiguous slice of ceil(bytes / 16 / blocks) pieces) and writes one folded word
+ * per workgroup to sink [blocks] (so that the reads are not optimised away).  Timing a launch gives the device's measured streaming-read bandwidth, the denominator
+ * reported next to the vendor's HBM peak.  bytes a positive multiple of 16. */
+aqua_status aqua_stream_read_probe(const void *buf, size_t bytes, int32_t blocks, uint32_t *sink,
+                                   void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -27,7 +27,8 @@ _STATUS_NAMES = {0: "AQUA_OK", 1: "AQUA_ERR_NULL", 2: "AQUA_ERR_SHAPE", 3: "AQUA
 EXPORTS = ("aqua_version", "aqua_last_error", "aqua_project_keys", "aqua_select_dims",
            "aqua_decode_workspace", "aqua_decode", "aqua_decode_step", "aqua_decode_step_noalloc",
            "aqua_prefill_workspace",
-           "aqua_prefill_chunk", "aqua_h2o_init", "aqua_h2o_victim", "aqua_h2o_step")
+           "aqua_prefill_chunk", "aqua_h2o_init", "aqua_h2o_victim", "aqua_h2o_step",
+           "aqua_stream_read_probe")
 
 
 class AquaError(RuntimeError):
@@ -71,6 +72,7 @@ def load_library() -> ctypes.CDLL:
                                 SZ, P], ctypes.c_int),
         "aqua_h2o_init": ([cp, P, I32, I32, cp, P, P, P], ctypes.c_int),
         "aqua_h2o_victim": ([P, P, I32, I32, I32, I32, I32, P, P], ctypes.c_int),
+        "aqua_stream_read_probe": ([P, SZ, I32, P, P], ctypes.c_int),
         "aqua_h2o_step": ([cp, I32, P, P, P, P, I32, I32, ctypes.c_float, P, P, I32, I32, P, P, P,
                            P, P, SZ, P], ctypes.c_int),
     }
@@ -209,3 +211,9 @@ def aqua_h2o_step(cache: aqua_cache, Hq: int, q, k_new, v_new, P, d_sel: int, k:
                                         _ptr(mass), _ptr(slot_pos), int(t_new), int(recent),
                                         _ptr(victim), _ptr(out), _ptr(q_proj_out),
                                         _ptr(mask_out), _ptr(ws), nbytes, _stream(stream)))
+
+
+def aqua_stream_read_probe(buf, blocks: int, sink, stream=None):
+    """One streaming read of the whole tensor buf (a diagnostic for the measured bandwidth)."""
+    _check(load_library().aqua_stream_read_probe(_ptr(buf), buf.numel() * buf.element_size(),
+                                                 int(blocks), _ptr(sink), _stream(stream)))

@@ -423,4 +423,18 @@ aqua_status aqua_h2o_init(const aqua_cache *full, const float *mass_full, int32_
                     "aqua_h2o_init launch");
 }
 
+aqua_status aqua_stream_read_probe(const void *buf, size_t bytes, int32_t blocks,
+                                   uint32_t *sink, void *stream) {
+  g_err[0] = 0;
+  if (!buf || !sink) return fail(AQUA_ERR_NULL, "buf and sink are required");
+  if (bytes == 0 || bytes % 16 != 0)
+    return fail(AQUA_ERR_SHAPE, "bytes (%zu) must be a positive multiple of 16", bytes);
+  if (blocks < 1) return fail(AQUA_ERR_SHAPE, "blocks=%d must be >= 1", blocks);
+  if (!aligned16(buf) || !aligned16(sink))
+    return fail(AQUA_ERR_ALIGN, "buf and sink must be 16-byte aligned");
+  return hip_status(aqua::launch_stream_read(buf, bytes, blocks, sink,
+                                             static_cast<hipStream_t>(stream)),
+                    "aqua_stream_read_probe launch");
+}
+
 }  // extern "C"

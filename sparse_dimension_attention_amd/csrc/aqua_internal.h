@@ -145,17 +145,22 @@ template <int KS> struct PParts {
 };
 
 // Columns col0 .. col0 + 15 of P; lane l takes column col0 + l % 16, rows 32 st + 8 (l / 16) + e.
+// load_p_raw issues the loads, split_p_parts turns the values into the three parts (callers that
+// want other loads in flight behind P's issue them in between).
 template <int KS>
-__device__ __forceinline__ void load_p_parts(const float *__restrict__ P, int col0,
-                                             PParts<KS> &pp) {
+__device__ __forceinline__ void load_p_raw(const float *__restrict__ P, int col0,
+                                           float (&v)[KS][8]) {
   constexpr int D = 32 * KS;
   const int lane = threadIdx.x & 63;
   const float *pc = P + (8 * (lane >> 4)) * D + col0 + (lane & 15);
-  float v[KS][8];
 #pragma unroll
   for (int st = 0; st < KS; ++st)
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[st][e] = pc[(32 * st + e) * D];
+}
+
+template <int KS>
+__device__ __forceinline__ void split_p_parts(const float (&v)[KS][8], PParts<KS> &pp) {
 #pragma unroll
   for (int st = 0; st < KS; ++st) {
     uint32_t h[8], mi[8], lo[8];
@@ -167,6 +172,14 @@ __device__ __forceinline__ void load_p_parts(const float *__restrict__ P, int co
     pp.l[st] = u32x4_t{lo[0] | lo[1] << 16, lo[2] | lo[3] << 16, lo[4] | lo[5] << 16,
                        lo[6] | lo[7] << 16};
   }
+}
+
+template <int KS>
+__device__ __forceinline__ void load_p_parts(const float *__restrict__ P, int col0,
+                                             PParts<KS> &pp) {
+  float v[KS][8];
+  load_p_raw<KS>(P, col0, v);
+  split_p_parts<KS>(v, pp);
 }
 
 // This lane's A operand of one bf16 row x [32 KS]: x[32 st + 8 (lane / 16) .. + 7], st = 0..KS-1.
@@ -348,6 +361,8 @@ hipError_t launch_prefill(const void *kp, const void *v, int B, int Hq, int Hkv,
                           void *ws, hipStream_t s);
 hipError_t launch_h2o_victim(float *mass, int32_t *slot_pos, int B, int Hkv, int n_slots,
                              int t_new, int recent, int32_t *victim, hipStream_t s);
+hipError_t launch_stream_read(const void *buf, size_t bytes, int blocks, uint32_t *sink,
+                              hipStream_t s);
 hipError_t launch_h2o_init(int dtype, const void *kp_full, const void *v_full,
                            const float *mass_full, int B, int Hkv, int d, int d_store,
                            int T_cap_full, int len, int heavy, int recent, void *kp, void *v,

@@ -117,10 +117,12 @@ struct DecodeSmem {
   // main region: softmax numerators [wave][token][head], reused for the wave merge
   static constexpr int MAIN = NW * WT * G * 4;
   static constexpr int BIG = PRO > MAIN ? PRO : MAIN;
-  // persistent small arrays
-  static constexpr int OFF_DL = BIG;                                     // int   [D]
-  static constexpr int OFF_QW = OFF_DL + D * 4;                          // float [D][G]
-  static constexpr int OFF_QP = OFF_QW + D * G * 4;                      // float [G+1][D]
+  // persistent small arrays; the walk list has at most D + 24 entries (16 speculative rows, the
+  // rest of the union, padding to whole batches)
+  static constexpr int NL = D + 24;
+  static constexpr int OFF_DL = BIG;                                     // int   [NL]
+  static constexpr int OFF_QW = OFF_DL + NL * 4;                         // float [NL][G]
+  static constexpr int OFF_QP = OFF_QW + NL * G * 4;                     // float [G+1][D]
   static constexpr int OFF_MW = OFF_QP + (FUSED ? (G + 1) * D * 4 : 0);  // uint  [G][NWORD]
   static constexpr int OFF_KN = OFF_MW + G * NWORD * 4;                  // float [D] new K'
   static constexpr int OFF_VN = OFF_KN + (FUSED ? D * 4 : 0);            // float [D] new V
@@ -439,10 +441,11 @@ __device__ __forceinline__ void select_group_heads(const DecodeArgs &a, size_t h
 // (proj_mfma: the arithmetic of aqua_select_dims and aqua_project_keys for bf16, so q', the masks
 // and the stored K' are those of the separate calls bit for bit), then select_group_heads.  The
 // A operand is 16 rows: the G queries, the new key at row G, and the key again past it (those
-// rows are discarded).  Wavefront w computes column blocks w, w + NW, ...  ALL: every block's
-// parts of P are loaded before after_loads() (the caller issues its own loads there, and they
-// stay in flight through the projection and the selection); otherwise the blocks go one at a
-// time, each load followed by its use, for fewer live registers.  LDS: s_qp [G+1][D],
+// rows are discarded).  Wavefront w computes column blocks w, w + NW, ...  ALL: the loads of every
+// block's values of P are issued before after_loads() (the caller issues its own loads there, and
+// they stay in flight through the projection and the selection: the waits for P's values leave
+// them outstanding); otherwise the blocks go one at a time, each load followed by its use, for
+// fewer live registers.  LDS: s_qp [G+1][D],
 // s_mw [G][D/32], s_knew and s_vnew [D].  Ends with a workgroup barrier.
 template <int D, int G, int NT, bool ALL, typename F>
 __device__ __forceinline__ void fused_project_select_mfma(const DecodeArgs &a, size_t head0,
@@ -470,13 +473,18 @@ __device__ __forceinline__ void fused_project_select_mfma(const DecodeArgs &a, s
     }
   };
   if constexpr (ALL) {
-    PParts<KS> pp[BPW];
+    float pv[BPW][KS][8];
 #pragma unroll
-    for (int i = 0; i < BPW; ++i) load_p_parts<KS>(a.P, 16 * min(w + i * NW, NB - 1), pp[i]);
+    for (int i = 0; i < BPW; ++i) load_p_raw<KS>(a.P, 16 * min(w + i * NW, NB - 1), pv[i]);
+    __builtin_amdgcn_sched_barrier(0);  // P's loads are issued before the caller's
     after_loads();
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < BPW; ++i)
-      if (w + i * NW < NB) store_tile(w + i * NW, proj_mfma<KS>(av, pp[i]));  // uniform
+    for (int i = 0; i < BPW; ++i) {
+      PParts<KS> pp;
+      split_p_parts<KS>(pv[i], pp);
+      if (w + i * NW < NB) store_tile(w + i * NW, proj_mfma<KS>(av, pp));  // uniform
+    }
   } else {
     after_loads();
     for (int blk = w; blk < NB; blk += NW) {
@@ -538,33 +546,92 @@ void decode_kernel(DecodeArgs a) {
   float *s_L = s_M + G;
   __shared__ int s_last;
 
+  // Every kernel argument this workgroup uses is read here, in one batch: left to the compiler,
+  // the reads go out one dependent round trip at a time, ~1 us each before the first HBM load.
+  asm volatile("" ::"s"(a.kp), "s"(a.v), "s"(a.q_proj), "s"(a.mask), "s"(a.q_raw), "s"(a.k_new),
+               "s"(a.P), "s"(a.partials), "s"(a.Hq), "s"(a.Hkv), "s"(a.d_store), "s"(a.T_cap),
+               "s"(a.len), "s"(a.S), "s"(a.qscale), "s"(a.d_sel), "s"(a.k));
+  // Grid (split, KV head, batch): the linear workgroup index (the one the dispatcher deals to
+  // the XCDs in turn) is split + S (g + Hkv b).
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int bg = blockIdx.x / a.S, split = blockIdx.x - bg * a.S;
-  const int b = bg / a.Hkv, g = bg - b * a.Hkv;
+  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int bg = b * a.Hkv + g;
+  const int wg_lin = bg * a.S + split;
   const size_t head0 = static_cast<size_t>(b) * a.Hq + static_cast<size_t>(g) * G;
   // Fused: the cache holds len - 1 tokens, the new one is position len - 1.
   const int len_c = FUSED ? a.len - 1 : a.len;
   const bool owner = FUSED && split == (a.len - 1) / SPLIT;
 
+  // This wavefront's tokens.  Lanes past the cached length read the last valid 16-byte chunk
+  // instead (same cache line as a live lane); their scores are discarded below.
+  const int tw0 = split * SPLIT + w * WT;
+  const int tl = tw0 + lane * TPL;
+  const bool wave_live = tw0 < len_c;
+  const int tl_ld = len_c > 0 ? min(tl, ((len_c - 1) / TPL) * TPL) : 0;
+  const KT *kbase = static_cast<const KT *>(a.kp) +
+                    static_cast<size_t>(bg) * a.d_store * a.T_cap + tl_ld;
+  // Each workgroup starts its walk over the K' rows at its own offset, so that workgroups running
+  // at the same time read different rows (rows of one group are T_cap apart, and a lock-step walk
+  // would send every workgroup to the same few HBM channels).  The offset mixes in the higher
+  // bits of the workgroup index: with many splits per group (a long context at batch 1)
+  // workgroups 16 apart would otherwise start on the same batch (measured at 131072 tokens:
+  // 106 us with the plain multiple, 97 us mixed; unchanged at batch 16).
+  const int wg_mix = (wg_lin * 5) ^ (wg_lin >> 4);
+
+  // Fused, bf16 storage: the first two batches of K' rows are requested before the prologue,
+  // speculatively, so that HBM is busy while the queries are projected and selected.  They are a
+  // cyclic run of 16 of the lowest spec_w stored dims (spec_w: the largest power of two up to
+  // 32 and d_store, so that the run wraps with a mask), which the selection nearly always keeps
+  // (the offline projection orders its dims by decreasing importance); a speculative row no head
+  // kept is weighted 0.  The walk then goes on over the rest of the union.
+  constexpr bool SPEC = FUSED && sizeof(KT) == 2 && NW >= 4;
+  constexpr int NSPEC = SPEC ? 2 * kUnroll : 0;
+  const int spec_w = a.d_store >= 32 ? 32 : 1 << (31 - __clz(a.d_store));
+  const int spec_r0 = wg_mix & (spec_w - 1);
+  const int spec_n = min(NSPEC, spec_w);  // distinct speculative rows
+  uint4 kA[kUnroll], kB[kUnroll];
+
   // ---- fused prologue: project the group's queries (and the new key), select their dims
   if constexpr (FUSED) {
-    if constexpr (sizeof(KT) == 2)
+    if constexpr (SPEC) {
+      fused_project_select_mfma<D, G, NT, true>(
+          a, head0, bg, owner, split == 0, s_qp, s_mw, s_knew, s_vnew, [&] {
+            // unconditional (a wavefront past the cached tokens reads its clamped, valid
+            // addresses): loads issued under a branch would make every later wait count them as
+            // possibly absent, i.e. wait for all of them at once
+#pragma unroll
+            for (int i = 0; i < kUnroll; ++i)
+              kA[i] = load16(kbase + static_cast<size_t>((spec_r0 + i) & (spec_w - 1)) * a.T_cap);
+#pragma unroll
+            for (int i = 0; i < kUnroll; ++i)
+              kB[i] = load16(kbase + static_cast<size_t>((spec_r0 + kUnroll + i) & (spec_w - 1)) *
+                                         a.T_cap);
+          });
+    } else if constexpr (sizeof(KT) == 2) {
       fused_project_select_mfma<D, G, NT, false>(a, head0, bg, owner, split == 0, s_qp, s_mw,
                                                  s_knew, s_vnew, [] {});
-    else
+    } else {
       fused_project_select<KT, D, G, NT>(a, head0, bg, owner, split == 0,
                                          reinterpret_cast<float *>(smem),
                                          reinterpret_cast<float(*)[D]>(smem + D * D * 4), s_qp,
                                          s_mw, s_knew, s_vnew, [] {});
+    }
   }
 
-  // ---- union of the group's masks, restricted to stored dims (uniform per workgroup)
+  // ---- the walk list: the speculative rows (fused bf16), then the union U of the group's masks
+  // (restricted to stored dims) less those rows, padded to whole batches with a dim at zero
+  // weight (re-reads hit in cache).  Entry e: dim s_dl[e], head weights s_qw[e][h] =
+  // q'_h[dim] * scale * log2 e where head h selected dim, else 0.  Uniform per workgroup.
   auto mask_word = [&](int h, int wd) -> uint32_t {
     if constexpr (FUSED) return s_mw[h][wd];
     else return a.mask[(head0 + h) * NWORD + wd];
   };
-  uint32_t U[NWORD];
-  int nU = 0, last_dim = 0;
+  auto q_val = [&](int h, int dim) -> float {
+    if constexpr (FUSED) return s_qp[h][dim];
+    else return a.q_proj[(head0 + h) * D + dim];
+  };
+  uint32_t R[NWORD];
+  int nR = 0, last_dim = 0;
 #pragma unroll
   for (int wd = 0; wd < NWORD; ++wd) {
     uint32_t u = 0;
@@ -573,77 +640,78 @@ void decode_kernel(DecodeArgs a) {
     const int lo = wd * 32;
     if (a.d_store <= lo) u = 0;
     else if (a.d_store < lo + 32) u &= (1u << (a.d_store - lo)) - 1u;
-    U[wd] = u;
-    nU += __popc(u);
+    if (SPEC && wd == 0) {  // the speculative rows lie in dims 0..31: spec_n of them, cyclic
+      const uint64_t run = ((spec_n >= 32 ? 0xffffffffull : ((1ull << spec_n) - 1)) << spec_r0);
+      const uint32_t wmask = spec_w >= 32 ? 0xffffffffu : (1u << spec_w) - 1u;
+      const uint32_t sp = (static_cast<uint32_t>(run) | static_cast<uint32_t>(run >> spec_w)) & wmask;
+      u &= ~sp;
+    }
+    R[wd] = u;
+    nR += __popc(u);
     if (u) last_dim = lo + 31 - __clz(u);
   }
-  // padded to whole batches with the last dim at zero weight (re-reads hit in cache)
-  const int nUp = (nU + kUnroll - 1) / kUnroll * kUnroll;
+  const int nRp = (nR + kUnroll - 1) / kUnroll * kUnroll;
+  if (SPEC && tid < NSPEC) {
+    // speculative entry tid: dim (r0 + tid) mod spec_w; entries past the distinct ones weigh 0
+    const int dim = (spec_r0 + tid) & (spec_w - 1);
+    s_dl[tid] = dim;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const bool keep = tid < spec_n && ((mask_word(h, dim >> 5) >> (dim & 31)) & 1u);
+      s_qw[tid][h] = keep ? q_val(h, dim) * a.qscale : 0.0f;
+    }
+  }
   if (tid < D) {
     const int wd = tid >> 5, bit = tid & 31;
+    // this dim's mask bits and q' for every head, read before they are known to be needed (in
+    // the plain form they are global loads: one round trip with the union's)
     uint32_t mw[G];
     float qv[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       mw[h] = mask_word(h, wd);
-      if constexpr (FUSED) qv[h] = s_qp[h][tid];
-      else qv[h] = a.q_proj[(head0 + h) * D + tid];
+      qv[h] = q_val(h, tid);
     }
-    uint32_t uw = 0;
+    uint32_t rw = 0;
     int pos = 0;
 #pragma unroll
     for (int x = 0; x < NWORD; ++x) {
-      if (x < wd) pos += __popc(U[x]);
-      if (x == wd) uw = U[x];
+      if (x < wd) pos += __popc(R[x]);
+      if (x == wd) rw = R[x];
     }
-    pos += __popc(uw & ((1u << bit) - 1u));
-    // Each workgroup walks the list from its own batch-aligned offset, so that workgroups
-    // running at the same time read different K' rows (rows of one group are T_cap apart, and
-    // a lock-step walk would send every workgroup to the same few HBM channels).  The offset
-    // mixes in the higher bits of the workgroup index: with many splits per group (a long
-    // context at batch 1) workgroups 16 apart would otherwise start on the same batch (measured
-    // at 131072 tokens: 106 us with the plain multiple, 97 us mixed; unchanged at batch 16).
-    const int nb = nUp / kUnroll;
-    const int rot = nb ? (((blockIdx.x * 5) ^ (blockIdx.x >> 4)) % nb) * kUnroll : 0;
-    if ((uw >> bit) & 1u) {
-      const int at = (pos + nUp - rot) % nUp;
+    pos += __popc(rw & ((1u << bit) - 1u));
+    const int nb = nRp / kUnroll;
+    const int rot = nb ? (wg_mix % nb) * kUnroll : 0;
+    if ((rw >> bit) & 1u) {
+      const int at = NSPEC + (pos + nRp - rot) % nRp;
       s_dl[at] = tid;
 #pragma unroll
       for (int h = 0; h < G; ++h) s_qw[at][h] = ((mw[h] >> bit) & 1u) ? qv[h] * a.qscale : 0.0f;
     }
-    if (tid >= nU && tid < nUp) {
-      const int at = (tid + nUp - rot) % nUp;
+    if (tid >= nR && tid < nRp) {
+      const int at = NSPEC + (tid + nRp - rot) % nRp;
       s_dl[at] = last_dim;
 #pragma unroll
       for (int h = 0; h < G; ++h) s_qw[at][h] = 0.0f;
     }
   }
-  __syncthreads();
+  // LDS only: the speculative loads stay in flight
+  lds_barrier();
 
   // ---- phase 1: log2-domain scores of this wavefront's cached tokens
-  // Lanes past the cached length read the last valid 16-byte chunk instead (same cache line as
-  // a live lane); their scores are discarded below.  Loads are unconditional so that the
-  // prefetch of the next batch overlaps the arithmetic of the current one.
-  const int tw0 = split * SPLIT + w * WT;
-  const int tl = tw0 + lane * TPL;
-  const bool wave_live = tw0 < len_c;
-  const int tl_ld = len_c > 0 ? min(tl, ((len_c - 1) / TPL) * TPL) : 0;
-  const KT *kbase = static_cast<const KT *>(a.kp) +
-                    static_cast<size_t>(bg) * a.d_store * a.T_cap + tl_ld;
   float acc[G][TPL];
 #pragma unroll
   for (int h = 0; h < G; ++h)
 #pragma unroll
     for (int j = 0; j < TPL; ++j) acc[h][j] = 0.0f;
 
-  // Software pipeline over batches of kUnroll rows, two register sets A and B in turn: the
-  // loads of batch i + 1 are issued before the arithmetic of batch i.  Inside the loop every
-  // load is unconditional, so the wait before each batch's arithmetic is exactly "one batch
-  // still in flight"; the last one or two batches are peeled off so that nothing is fetched
-  // past the end (a re-read there would go back to memory: the loads are non-temporal).
+  // Software pipeline over batches of kUnroll rows, two register sets A and B in turn, with a
+  // batch in flight during the arithmetic of the one before; the last batches are peeled off so
+  // that nothing is fetched past the end (a re-read there would go back to memory: the loads are
+  // non-temporal).
 #define AQUA_K_LOAD(BUF, BATCH)                                                          \
   _Pragma("unroll") for (int i = 0; i < kUnroll; ++i) BUF[i] = load16(                   \
-      kbase + static_cast<size_t>(s_dl[min(BATCH, nbat - 1) * kUnroll + i]) * a.T_cap)
+      kbase + static_cast<size_t>(s_dl[(BATCH) * kUnroll + i]) * a.T_cap)
 #define AQUA_K_FMA(BUF, BATCH)                                                           \
   _Pragma("unroll") for (int i = 0; i < kUnroll; ++i) {                                  \
     float kv[TPL];                                                                        \
@@ -654,30 +722,55 @@ void decode_kernel(DecodeArgs a) {
         _Pragma("unroll") for (int j = 0; j < TPL; ++j) acc[h][j] =                       \
         fmaf(qw[h], kv[j], acc[h][j]);                                                    \
   }
-  const int nbat = nUp / kUnroll;
+  const int nbat = (NSPEC + nRp) / kUnroll;
+  const int ptot = nbat + WT / (TPI * kUnroll);
   if (wave_live && nbat > 0) {
-    uint4 kA[kUnroll], kB[kUnroll];
-    AQUA_K_LOAD(kA, 0);
     int bi = 0;
-    for (; bi + 2 < nbat; bi += 2) {
-      progress_priority(bi, nbat + WT / (TPI * kUnroll));
-      AQUA_K_LOAD(kB, bi + 1);
-      __builtin_amdgcn_sched_barrier(0);
+    if constexpr (SPEC) {
+      // batches 0 and 1 are in flight already: each batch's loads go out two batches ahead
+      for (; bi + 3 < nbat; bi += 2) {
+        progress_priority(bi, ptot);
+        AQUA_K_FMA(kA, bi);
+        AQUA_K_LOAD(kA, bi + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        AQUA_K_FMA(kB, bi + 1);
+        AQUA_K_LOAD(kB, bi + 3);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // the last one to three batches (bi .. nbat - 1): nothing fetched past the end
+      progress_priority(bi, ptot);
+      const int left = nbat - bi;
       AQUA_K_FMA(kA, bi);
-      AQUA_K_LOAD(kA, bi + 2);
+      if (left == 3) AQUA_K_LOAD(kA, bi + 2);
       __builtin_amdgcn_sched_barrier(0);
-      AQUA_K_FMA(kB, bi + 1);
-    }
-    // the last one or two batches: nothing more to prefetch
-    progress_priority(bi, nbat + WT / (TPI * kUnroll));
-    if (bi + 1 < nbat) {
-      AQUA_K_LOAD(kB, bi + 1);
+      if (left >= 2) AQUA_K_FMA(kB, bi + 1);
       __builtin_amdgcn_sched_barrier(0);
-      AQUA_K_FMA(kA, bi);
-      __builtin_amdgcn_sched_barrier(0);
-      AQUA_K_FMA(kB, bi + 1);
+      if (left == 3) AQUA_K_FMA(kA, bi + 2);
     } else {
-      AQUA_K_FMA(kA, bi);
+      // the loads of batch i + 1 are issued before the arithmetic of batch i; inside the loop
+      // every load is unconditional, so the wait before each batch's arithmetic is exactly "one
+      // batch still in flight"
+      AQUA_K_LOAD(kA, 0);
+      for (; bi + 2 < nbat; bi += 2) {
+        progress_priority(bi, ptot);
+        AQUA_K_LOAD(kB, bi + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        AQUA_K_FMA(kA, bi);
+        AQUA_K_LOAD(kA, bi + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        AQUA_K_FMA(kB, bi + 1);
+      }
+      // the last one or two batches: nothing more to prefetch
+      progress_priority(bi, ptot);
+      if (bi + 1 < nbat) {
+        AQUA_K_LOAD(kB, bi + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        AQUA_K_FMA(kA, bi);
+        __builtin_amdgcn_sched_barrier(0);
+        AQUA_K_FMA(kB, bi + 1);
+      } else {
+        AQUA_K_FMA(kA, bi);
+      }
     }
   }
 #undef AQUA_K_LOAD
@@ -700,7 +793,7 @@ void decode_kernel(DecodeArgs a) {
     float part[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) part[h] = 0.0f;
-    for (int u = lane; u < nUp; u += 64) {
+    for (int u = lane; u < nbat * kUnroll; u += 64) {
       const float kv = s_knew[s_dl[u]];
 #pragma unroll
       for (int h = 0; h < G; ++h) part[h] = fmaf(s_qw[u][h], kv, part[h]);
@@ -749,7 +842,7 @@ void decode_kernel(DecodeArgs a) {
       static_cast<KT *>(a.kp_w)[(static_cast<size_t>(bg) * a.d_store + tid) * a.T_cap + col] =
           store_elem<KT>(s_knew[tid]);
     static_cast<KT *>(a.v_w)[(static_cast<size_t>(bg) * a.T_cap + col) * D + tid] =
-        static_cast<const KT *>(a.v_new)[static_cast<size_t>(bg) * D + tid];
+        store_elem<KT>(s_vnew[tid]);  // exact: s_vnew holds the stored value widened
   }
 
   // ---- phase 2: o = sum_t p_t V_t over this wavefront's cached tokens
@@ -913,9 +1006,14 @@ __device__ __forceinline__ void short_attend(const DecodeArgs &a, const H2OArgs 
   __shared__ float s_wm[4][G], s_wl[4][G], s_M[G], s_L[G];
   __shared__ int s_last;
 
+  // every kernel argument read in one batch, and a grid of (chunk, KV head, batch): as in
+  // decode_kernel
+  asm volatile("" ::"s"(a.kp), "s"(a.v), "s"(a.q_proj), "s"(a.mask), "s"(a.q_raw), "s"(a.k_new),
+               "s"(a.P), "s"(a.partials), "s"(a.mass), "s"(a.Hq), "s"(a.Hkv), "s"(a.d_store),
+               "s"(a.T_cap), "s"(a.len), "s"(a.S), "s"(a.qscale), "s"(a.d_sel), "s"(a.k));
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int bg = blockIdx.x / a.S, split = blockIdx.x - bg * a.S;
-  const int b = bg / a.Hkv, g = bg - b * a.Hkv;
+  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int bg = b * a.Hkv + g;
   const size_t head0 = static_cast<size_t>(b) * a.Hq + static_cast<size_t>(g) * G;
   const size_t slot0 = static_cast<size_t>(bg) * a.T_cap;
   const int t0 = split * kShortChunk;
@@ -1119,8 +1217,7 @@ __device__ __forceinline__ void short_attend(const DecodeArgs &a, const H2OArgs 
       if (tid < a.d_store)
         static_cast<KT *>(a.kp_w)[(static_cast<size_t>(bg) * a.d_store + tid) * a.T_cap +
                                   victim] = store_elem<KT>(s_knew[tid]);
-      static_cast<KT *>(a.v_w)[(slot0 + victim) * D + tid] =
-          static_cast<const KT *>(a.v_new)[static_cast<size_t>(bg) * D + tid];
+      static_cast<KT *>(a.v_w)[(slot0 + victim) * D + tid] = store_elem<KT>(s_vnew[tid]);
     }
   }
 
@@ -1160,7 +1257,7 @@ void h2o_step_kernel(DecodeArgs a, H2OArgs hh) {
 template <typename KT, int D, int G, bool FUSED>
 hipError_t launch_split_g(const DecodeArgs &a, const DecodeLayout &L, hipStream_t s) {
   if (a.S != (a.len + L.split - 1) / L.split) return hipErrorInvalidConfiguration;
-  const dim3 grid(a.B * a.Hkv * a.S);
+  const dim3 grid(a.S, a.Hkv, a.B);
   if constexpr (G == 4) {
     if (L.waves == 8) {
       decode_kernel<KT, D, G, 8, FUSED><<<grid, dim3(512), 0, s>>>(a);
@@ -1192,7 +1289,7 @@ hipError_t launch_split_t(const DecodeArgs &a, const DecodeLayout &L, hipStream_
 template <typename KT, int D, int G, int MODE>
 hipError_t launch_short_g(const DecodeArgs &a, const H2OArgs &h, hipStream_t s) {
   if (a.S != (a.len + kShortChunk - 1) / kShortChunk) return hipErrorInvalidConfiguration;
-  const dim3 grid(a.B * a.Hkv * a.S), block(256);
+  const dim3 grid(a.S, a.Hkv, a.B), block(256);
   if constexpr (MODE == kShortH2O) h2o_step_kernel<KT, D, G><<<grid, block, 0, s>>>(a, h);
   else if constexpr (MODE == kShortStep) decode_step_short_kernel<KT, D, G><<<grid, block, 0, s>>>(a);
   else decode_short_kernel<KT, D, G><<<grid, block, 0, s>>>(a);

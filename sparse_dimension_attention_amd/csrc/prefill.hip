@@ -37,9 +37,9 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 // workgroup of 8 wavefronts walks blocks of 32 rows; wavefront w computes output columns
 // [16w, 16w + 16), its parts of P held in registers, and writes its part of the q' tile to LDS;
 // after one barrier each wavefront selects 4 of the 32 rows (one row at a time, lane l holding
-// dims l and l + 64).  The
-// selection is a latency-bound chain of ballots and scalar steps per row, so the layout keeps
-// the registers low (16 columns' parts of P per wavefront) for four wavefronts per SIMD.
+// dims l and l + 64).  The selection is a latency-bound chain of ballots and scalar steps per
+// row, so the layout keeps the registers low (16 columns' parts of P per wavefront) for four
+// wavefronts per SIMD.
 constexpr int SQS = 128 + 8;  // LDS row stride (floats) of the q' tile
 constexpr int SEL_WAVES = 8;  // wavefronts per selection workgroup
 constexpr int SEL_ROWS_PER_WAVE = 32 / SEL_WAVES;

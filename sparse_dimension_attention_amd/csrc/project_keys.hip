@@ -5,12 +5,17 @@
 //
 // bf16 keys take the library's one bf16 projection (proj_mfma: v_mfma_f32_16x16x32_bf16 on P's
 // exact three-part bf16 split, fp32 accumulation), so a key's K' is the same bits whichever
-// kernel projects it (this one, the fused decode step's, the fused H2O step's).  A workgroup of
-// 8 wavefronts walks tiles of 128 tokens of one (b, g): wavefront w keeps the parts of its 16
-// output dims in registers across the tiles, projects the tile's 16-token blocks, rounds to bf16
-// and transposes through LDS, so that each K' row then gets 128 consecutive tokens (256 bytes)
-// per tile, written 16 bytes per lane.  HBM-bound: 2 d bytes of K read, 2 d_store bytes of K'
-// and 4 d bytes of V moved per token.
+// kernel projects it (this one, the fused decode step's, the fused H2O step's).  One workgroup of
+// 8 wavefronts per tile of 64 tokens of one (b, g), four workgroups per CU (36 KB of LDS each),
+// so that the loads of some overlap the projection and stores of others: wavefront w takes the
+// parts of P for its 16 output dims, the tile's keys are staged in LDS (16 bytes per lane,
+// coalesced) and its values go from registers straight to the cache; the wavefronts project the
+// tile's 16-token blocks, round to bf16 and transpose through LDS, so that each K' row gets 64
+// consecutive tokens (128 bytes), written 16 bytes per lane.  (A loop over tiles per workgroup
+// with the next tile's loads in flight does not pay here: loads and stores share one in-order
+// wait counter, so with a variable number of stores per tile every wait for the next tile's data
+// also waits for this tile's stores.)  HBM-bound: 2 d bytes of K read, 2 d_store bytes of
+// K' and 4 d bytes of V moved per token.
 //
 // fp32 keys (the VALU path): tiles of 32 tokens staged in LDS as fp32; thread (i, group) computes
 // K'[t][i] = sum_j K[t][j] P[j][i] for its tokens (j ascending, fma), then the same transposed
@@ -155,7 +160,7 @@ __global__ __launch_bounds__(256) void project_keys_small_kernel(
 }
 
 // ------------------------------------------------------------------ bf16: MFMA
-constexpr int kMT = 128;  // tokens per tile
+constexpr int kMT = 64;  // tokens per tile (one tile per workgroup)
 
 template <int D>
 __global__ __launch_bounds__(512) void project_keys_mfma_kernel(
@@ -163,65 +168,84 @@ __global__ __launch_bounds__(512) void project_keys_mfma_kernel(
     const float *__restrict__ P, int n, int d_store, int T_cap, int len0,
     const int32_t *__restrict__ slots, bf16_t *__restrict__ kp, bf16_t *__restrict__ vc) {
   constexpr int KS = D / 32, NB = D / 16;
-  constexpr int WPB = 8 / NB;  // wavefronts per column block (they split the token blocks)
-  constexpr int KROW = kMT + 8;  // LDS row stride (bf16) of the transposed tile
+  constexpr int WPB = 8 / NB;      // wavefronts per column block (they split the token blocks)
+  constexpr int KR = D + 8;        // LDS row stride (bf16) of the staged key tile
+  constexpr int KROW = kMT + 8;    // LDS row stride (bf16) of the transposed tile
+  constexpr int PR = D / 8;        // 16-byte pieces per key or value row
+  constexpr int CH = kMT * PR / 512;  // pieces of the tile's K (and of its V) per thread
+  static_assert(CH >= 1 && kMT * PR % 512 == 0, "tile pieces per thread");
+  __shared__ __align__(16) bf16_t ks[kMT][KR];
   __shared__ __align__(16) bf16_t kt[D][KROW];
   __shared__ int cols[kMT];
   const int bg = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int blk = w % NB, tb0 = w / NB;
-  PParts<KS> pp;
-  load_p_parts<KS>(P, 16 * blk, pp);
+  const int t0 = blockIdx.x * kMT, nt = min(kMT, n - t0);
   const bf16_t *kb = k_raw + static_cast<size_t>(bg) * n * D;
-  const int ntiles = (n + kMT - 1) / kMT;
-  for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-    const int t0 = tile * kMT, nt = min(kMT, n - t0);
-    if (tid < kMT) {
-      int col = -1;
-      if (tid < nt) col = slots ? slots[static_cast<size_t>(bg) * n + t0 + tid] : len0 + t0 + tid;
-      cols[tid] = (col >= 0 && col < T_cap) ? col : -1;
-    }
-    // K' of the tile: wavefront (blk, tb0) takes 16-token blocks tb0, tb0 + WPB, ...
-    for (int tb = tb0; tb < kMT / 16; tb += WPB) {
-      const int t = min(t0 + 16 * tb + (lane & 15), n - 1);  // rows past n repeat the last
-      u32x4_t av[KS];
-      load_a_row<KS>(kb + static_cast<size_t>(t) * D, av);
-      const f32x4_t x = proj_mfma<KS>(av, pp);
-      const uint32_t lo = pack_bf16x2(x[0], x[1]), hi = pack_bf16x2(x[2], x[3]);
-      *reinterpret_cast<uint2 *>(&kt[16 * blk + (lane & 15)][16 * tb + 4 * (lane >> 4)]) =
-          make_uint2(lo, hi);
-    }
-    __syncthreads();
-    // K' rows: 16 chunks of 8 tokens per row; a chunk whose 8 columns are consecutive and
-    // 16-byte aligned is one store, any other is written token by token
-    for (int e = tid; e < d_store * (kMT / 8); e += 512) {
-      const int row = e / (kMT / 8), c = e % (kMT / 8);
-      const int ta = 8 * c;
-      if (ta >= nt) continue;
-      bf16_t *dst = kp + (static_cast<size_t>(bg) * d_store + row) * T_cap;
-      const int c0 = cols[ta];
-      bool vec = ta + 8 <= nt && c0 >= 0 && (c0 & 7) == 0;
+  // every load is issued before the first wait: P's values, the tile's keys and values (16 bytes
+  // per lane, coalesced), the destination columns
+  float pv[KS][8];
+  load_p_raw<KS>(P, 16 * blk, pv);
+  u32x4_t kr[CH], vr[CH];
 #pragma unroll
-      for (int j = 1; j < 8; ++j) vec = vec && cols[ta + j] == c0 + j;
-      if (vec) {
-        *reinterpret_cast<uint4 *>(dst + c0) = *reinterpret_cast<const uint4 *>(&kt[row][ta]);
-      } else {
-        for (int j = 0; j < 8 && ta + j < nt; ++j)
-          if (cols[ta + j] >= 0) dst[cols[ta + j]] = kt[row][ta + j];
-      }
+  for (int c = 0; c < CH; ++c) {
+    const int pc = tid + 512 * c;
+    const size_t off = static_cast<size_t>(min(t0 + pc / PR, n - 1)) * D + 8 * (pc % PR);
+    kr[c] = *reinterpret_cast<const u32x4_t *>(kb + off);
+    if (v_raw) vr[c] = *reinterpret_cast<const u32x4_t *>(v_raw + static_cast<size_t>(bg) * n * D + off);
+  }
+  if (tid < kMT) {
+    int col = -1;
+    if (tid < nt) col = slots ? slots[static_cast<size_t>(bg) * n + t0 + tid] : len0 + t0 + tid;
+    cols[tid] = (col >= 0 && col < T_cap) ? col : -1;
+  }
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int pc = tid + 512 * c;
+    *reinterpret_cast<u32x4_t *>(&ks[pc / PR][8 * (pc % PR)]) = kr[c];
+  }
+  PParts<KS> pp;
+  split_p_parts<KS>(pv, pp);
+  __syncthreads();
+  // V rows, 16 bytes per lane, straight from registers
+  if (v_raw) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int pc = tid + 512 * c, t = pc / PR;
+      const int col = cols[t];
+      if (t < nt && col >= 0)
+        *reinterpret_cast<u32x4_t *>(vc + (static_cast<size_t>(bg) * T_cap + col) * D +
+                                     8 * (pc % PR)) = vr[c];
     }
-    // V rows, 16 bytes per lane
-    if (v_raw) {
-      constexpr int PER_ROW = D / 8;
-      for (int e = tid; e < nt * PER_ROW; e += 512) {
-        const int t = e / PER_ROW, c = e % PER_ROW;
-        const int col = cols[t];
-        if (col < 0) continue;
-        *reinterpret_cast<uint4 *>(vc + (static_cast<size_t>(bg) * T_cap + col) * D + 8 * c) =
-            *reinterpret_cast<const uint4 *>(v_raw + (static_cast<size_t>(bg) * n + t0 + t) * D +
-                                             8 * c);
-      }
+  }
+  // K' of the tile: wavefront (blk, tb0) takes 16-token blocks tb0, tb0 + WPB, ...
+#pragma unroll
+  for (int tb = tb0; tb < kMT / 16; tb += WPB) {
+    u32x4_t av[KS];
+#pragma unroll
+    for (int st = 0; st < KS; ++st)
+      av[st] = *reinterpret_cast<const u32x4_t *>(&ks[16 * tb + (lane & 15)]
+                                                    [32 * st + 8 * (lane >> 4)]);
+    const f32x4_t x = proj_mfma<KS>(av, pp);
+    *reinterpret_cast<uint2 *>(&kt[16 * blk + (lane & 15)][16 * tb + 4 * (lane >> 4)]) =
+        make_uint2(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]));
+  }
+  __syncthreads();
+  // K' rows: chunks of 8 tokens; a chunk whose 8 columns are consecutive and 16-byte aligned is
+  // one store, any other is written token by token
+  for (int e = tid; e < d_store * (kMT / 8); e += 512) {
+    const int row = e / (kMT / 8), ta = 8 * (e % (kMT / 8));
+    if (ta >= nt) continue;
+    bf16_t *dst = kp + (static_cast<size_t>(bg) * d_store + row) * T_cap;
+    const int c0 = cols[ta];
+    bool vec = ta + 8 <= nt && c0 >= 0 && (c0 & 7) == 0;
+#pragma unroll
+    for (int j = 1; j < 8; ++j) vec = vec && cols[ta + j] == c0 + j;
+    if (vec) {
+      *reinterpret_cast<uint4 *>(dst + c0) = *reinterpret_cast<const uint4 *>(&kt[row][ta]);
+    } else {
+      for (int j = 0; j < 8 && ta + j < nt; ++j)
+        if (cols[ta + j] >= 0) dst[cols[ta + j]] = kt[row][ta + j];
     }
-    __syncthreads();  // kt and cols are rewritten by the next tile
   }
 }
 
@@ -275,11 +299,7 @@ hipError_t launch_pk(const void *k_raw, const void *v_raw, const float *P, int B
           static_cast<bf16_t *>(v));
       return hipGetLastError();
     }
-    // tiles per (b, g) spread over about 1024 workgroups in all, each walking several tiles
-    // with its parts of P kept in registers
-    const int groups = B * Hkv, ntiles = (n + kMT - 1) / kMT;
-    const int per = std::max(1, 1024 / groups);
-    const dim3 grid(std::min(ntiles, per), groups);
+    const dim3 grid((n + kMT - 1) / kMT, B * Hkv);
     project_keys_mfma_kernel<D><<<grid, dim3(512), 0, s>>>(
         kr, vr, P, n, d_store, T_cap, len0, slots, static_cast<bf16_t *>(kp),
         static_cast<bf16_t *>(v));

@@ -30,7 +30,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 13
+    assert len(names) == 14
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(aq.EXPORTS)
@@ -250,3 +250,10 @@ def test_decode_step_noalloc_rejects(lib, kw, args, status):
                                         None) == status
     assert lib.aqua_last_error().decode() != ""
     assert c.len == kw.get("len", 10)
+
+
+def test_stream_read_probe_rejects(lib):
+    assert lib.aqua_stream_read_probe(None, 1024, 4, FAKE, None) == A.AQUA_ERR_NULL
+    assert lib.aqua_stream_read_probe(FAKE, 1000, 4, FAKE, None) == A.AQUA_ERR_SHAPE
+    assert lib.aqua_stream_read_probe(FAKE, 1024, 0, FAKE, None) == A.AQUA_ERR_SHAPE
+    assert lib.aqua_stream_read_probe(FAKE + 4, 1024, 4, FAKE, None) == A.AQUA_ERR_ALIGN
