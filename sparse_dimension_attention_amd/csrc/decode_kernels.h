@@ -591,6 +591,33 @@ void decode_kernel(DecodeArgs a) {
   const int spec_n = min(NSPEC, spec_w);  // distinct speculative rows
   uint4 kA[kUnroll], kB[kUnroll];
 
+  // V rows of this wavefront's tokens: lane -> row sub of each group of TPI, elements cl * EPL..
+  constexpr int RB = TPI * kUnroll;  // rows per batch
+  const int sub = lane / LPT, cl = lane - sub * LPT;
+  const int nrow = min(WT, len_c - tw0);  // may be <= 0
+  const KT *vbase = static_cast<const KT *>(a.v) +
+                    (static_cast<size_t>(bg) * a.T_cap + tw0) * D + cl * EPL;
+  // With the speculative rows, the fused prologue also requests this wavefront's first batch of
+  // V rows (which no selection decides) and holds it in registers until the V pass, so that HBM
+  // stays busy through the projection and the selection.  (Copies straight into LDS would free
+  // the registers, but the compiler then waits for every outstanding load at each wait while
+  // they are in flight.)
+  constexpr bool VPRE = SPEC;
+  uint4 vC[VPRE ? kUnroll : 1];
+  auto v_prefetch = [&] {
+    if constexpr (VPRE) {
+      // rows past the cached length read the last cached row (their p is 0); a wavefront past
+      // the end reads a valid row too, so that every wavefront issues the same loads
+      const int last = len_c > 0 ? len_c - 1 : 0;
+#pragma unroll
+      for (int i = 0; i < kUnroll; ++i) {
+        const int tok = min(tw0 + i * TPI + sub, last);
+        vC[i] = load16(static_cast<const KT *>(a.v) +
+                       (static_cast<size_t>(bg) * a.T_cap + tok) * D + cl * EPL);
+      }
+    }
+  };
+
   // ---- fused prologue: project the group's queries (and the new key), select their dims
   if constexpr (FUSED) {
     if constexpr (SPEC) {
@@ -606,6 +633,7 @@ void decode_kernel(DecodeArgs a) {
             for (int i = 0; i < kUnroll; ++i)
               kB[i] = load16(kbase + static_cast<size_t>((spec_r0 + kUnroll + i) & (spec_w - 1)) *
                                          a.T_cap);
+            v_prefetch();
           });
     } else if constexpr (sizeof(KT) == 2) {
       fused_project_select_mfma<D, G, NT, false>(a, head0, bg, owner, split == 0, s_qp, s_mw,
@@ -848,16 +876,11 @@ void decode_kernel(DecodeArgs a) {
   // ---- phase 2: o = sum_t p_t V_t over this wavefront's cached tokens
   // Rows past the cached length read the last valid row (their p is 0), to keep loads
   // unconditional.
-  const int sub = lane / LPT, cl = lane - sub * LPT;
-  const int nrow = min(WT, len_c - tw0);  // may be <= 0
-  const KT *vbase = static_cast<const KT *>(a.v) +
-                    (static_cast<size_t>(bg) * a.T_cap + tw0) * D + cl * EPL;
   float o[G][EPL];
 #pragma unroll
   for (int h = 0; h < G; ++h)
 #pragma unroll
     for (int e = 0; e < EPL; ++e) o[h][e] = 0.0f;
-  constexpr int RB = TPI * kUnroll;  // rows per batch
   // same pipeline over batches of RB rows
 #define AQUA_V_LOAD(BUF, BATCH)                                                          \
   _Pragma("unroll") for (int i = 0; i < kUnroll; ++i) BUF[i] = load16(                   \
@@ -873,10 +896,24 @@ void decode_kernel(DecodeArgs a) {
         _Pragma("unroll") for (int e = 0; e < EPL; ++e) o[h][e] = fmaf(p[h], vv[e], o[h][e]); \
   }
   const int vbat = nrow > 0 ? (nrow + RB - 1) / RB : 0;
-  if (vbat > 0) {
-    uint4 vA[kUnroll], vB[kUnroll];
-    AQUA_V_LOAD(vA, 0);
-    int bi = 0;
+  uint4 vA[kUnroll], vB[kUnroll];
+  int bi = 0;
+  if constexpr (VPRE) {
+    // batch 0 came in with the prologue.  Batch 1 is requested, then batch 0 is added, in every
+    // wavefront (one with fewer rows reads valid rows again and adds them at p = 0): a use under
+    // a branch would let the compiler move the prologue's loads down to it.
+    const int last = len_c > 0 ? len_c - 1 : 0;
+#pragma unroll
+    for (int i = 0; i < kUnroll; ++i)
+      vA[i] = load16(static_cast<const KT *>(a.v) +
+                     (static_cast<size_t>(bg) * a.T_cap + min(tw0 + RB + i * TPI + sub, last)) * D +
+                     cl * EPL);
+    __builtin_amdgcn_sched_barrier(0);
+    AQUA_V_FMA(vC, 0);
+    bi = 1;
+  }
+  if (vbat > bi) {
+    if constexpr (!VPRE) AQUA_V_LOAD(vA, 0);
     for (; bi + 2 < vbat; bi += 2) {
       progress_priority(nbat + bi, nbat + WT / (TPI * kUnroll));
       AQUA_V_LOAD(vB, bi + 1);
@@ -893,7 +930,7 @@ void decode_kernel(DecodeArgs a) {
       AQUA_V_FMA(vA, bi);
       __builtin_amdgcn_sched_barrier(0);
       AQUA_V_FMA(vB, bi + 1);
-    } else {
+    } else if (bi < vbat) {
       AQUA_V_FMA(vA, bi);
     }
   }
