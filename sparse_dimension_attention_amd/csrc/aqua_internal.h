@@ -144,15 +144,15 @@ template <int KS> struct PParts {
   u32x4_t h[KS], m[KS], l[KS];
 };
 
-// Columns col0 .. col0 + 15 of P; lane l takes column col0 + l % 16, rows 32 st + 8 (l / 16) + e.
-// load_p_raw issues the loads, split_p_parts turns the values into the three parts (callers that
-// want other loads in flight behind P's issue them in between).
+// Columns col0 .. col0 + 15 of P; lane l takes column col0 + l % 16 (at most col_max), rows
+// 32 st + 8 (l / 16) + e.  load_p_raw issues the loads, split_p_parts turns the values into the
+// three parts (callers that want other loads in flight behind P's issue them in between).
 template <int KS>
 __device__ __forceinline__ void load_p_raw(const float *__restrict__ P, int col0,
-                                           float (&v)[KS][8]) {
+                                           float (&v)[KS][8], int col_max = 32 * KS - 1) {
   constexpr int D = 32 * KS;
   const int lane = threadIdx.x & 63;
-  const float *pc = P + (8 * (lane >> 4)) * D + col0 + (lane & 15);
+  const float *pc = P + (8 * (lane >> 4)) * D + min(col0 + (lane & 15), col_max);
 #pragma unroll
   for (int st = 0; st < KS; ++st)
 #pragma unroll

@@ -249,6 +249,171 @@ __global__ __launch_bounds__(512) void project_keys_mfma_kernel(
   }
 }
 
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+// Bulk append (no slot list, len0 a multiple of 8): each workgroup (about one per CU) streams a
+// contiguous run of whole 64-token tiles of one (b, g), its wavefronts' parts of P held in
+// registers for the whole run; the last workgroup of each (b, g) then takes the ragged tail.
+// Tile i + 3's keys and values are requested before tile i is worked on (four register sets in
+// turn, no copies at the loop latch), and every store of a whole tile is unconditional, so that
+// each wait is exactly "the next three tiles' loads plus their stores still in flight":
+//  * V rows: 16 bytes per lane, from registers, streaming stores;
+//  * the keys: through LDS (two buffers, one barrier per tile) into the MFMA A operands;
+//  * K': each wavefront's 16 dims x 64 tokens go through a slice of LDS of its own (no barrier)
+//    and out as 128 contiguous bytes per K' row, 16 bytes per lane, streaming stores.  Lanes
+//    whose dim is at or past d_store compute dim d_store - 1 again and store that same value.
+constexpr int kNS = 4;  // register sets: tiles in flight ahead of the one worked on, plus one
+template <int D>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+void project_keys_stream_kernel(const bf16_t *__restrict__ k_raw, const bf16_t *__restrict__ v_raw,
+                                const float *__restrict__ P, int n, int d_store, int T_cap,
+                                int len0, int tiles_per_wg, bf16_t *__restrict__ kp,
+                                bf16_t *__restrict__ vc) {
+  constexpr int KS = D / 32, NB = D / 16;
+  constexpr int WPB = 8 / NB;          // wavefronts per column block (they split the token blocks)
+  constexpr int KR = D + 8;            // LDS row stride (bf16) of a staged key tile
+  constexpr int TR = kMT + 8;          // LDS row stride (bf16) of a wavefront's K' slice
+  constexpr int PR = D / 8;            // 16-byte pieces per key or value row
+  constexpr int CH = kMT * PR / 512;   // pieces of a tile's K (and of its V) per thread
+  static_assert(CH >= 1 && kMT * PR % 512 == 0, "tile pieces per thread");
+  static_assert(kMT == 64, "K' slice: 8 lanes of 16 bytes per row, 8 rows per store");
+  __shared__ __align__(16) bf16_t ks[2][kMT][KR];
+  __shared__ __align__(16) bf16_t kt[8][16][TR];
+  asm volatile("" ::"s"(k_raw), "s"(v_raw), "s"(P), "s"(n), "s"(d_store), "s"(T_cap), "s"(len0),
+               "s"(tiles_per_wg), "s"(kp), "s"(vc));
+  const int bg = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int blk = w % NB, tb0 = WPB == 1 ? 0 : w / NB;  // 8 wavefronts
+  const int full = n / kMT;
+  const int x0 = blockIdx.x * tiles_per_wg;
+  const int x1 = min(x0 + tiles_per_wg, full);
+  const bf16_t *kb = k_raw + static_cast<size_t>(bg) * n * D;
+  const bf16_t *vb = v_raw + static_cast<size_t>(bg) * n * D;
+  float pv[KS][8];
+  load_p_raw<KS>(P, 16 * blk, pv, d_store - 1);
+  // This wavefront's tokens: token blocks [TBW tb0, TBW tb0 + TBW) of each tile (all four, or
+  // with two wavefronts per column block a contiguous half each), which it alone writes to its
+  // slice and stores.  Store lanes: row srow + RPS j (j < NST), tokens scol .. scol + 7.
+  constexpr int TBW = (kMT / 16) / WPB;   // token blocks per wavefront
+  constexpr int CPR = TBW * 16 / 8;       // 16-byte chunks per slice row
+  constexpr int RPS = 64 / CPR;           // slice rows per store
+  constexpr int NST = 16 / RPS;           // stores per wavefront per tile
+  const int srow = lane / CPR, scol = TBW * 16 * tb0 + 8 * (lane % CPR);
+  bf16_t *kprow = kp + (static_cast<size_t>(bg) * d_store + min(16 * blk + srow, d_store - 1)) *
+                           T_cap + len0 + scol;
+  // K' row offset from store j = 0 to j = 1 (rows srow and srow + RPS, both clamped)
+  const int kprow8 = (min(16 * blk + srow + RPS, d_store - 1) - min(16 * blk + srow, d_store - 1)) *
+                     T_cap;
+  bf16_t *vcb = vc + (static_cast<size_t>(bg) * T_cap + len0) * D;
+  u32x4_t kS[kNS][CH], vS[kNS][CH];
+  // this wavefront's 16 x 16 block of K' (token block tb) into its slice: lane holds dim
+  // l % 16, tokens 4 (l / 16) .. + 3
+  auto to_slice = [&](int tb, const f32x4_t &pr) {
+    *reinterpret_cast<u32x2_t *>(&kt[w][lane & 15][16 * tb + 4 * (lane >> 4)]) =
+        u32x2_t{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])};
+  };
+#define AQUA_PK_LOAD(S_, X)                                                              \
+  _Pragma("unroll") for (int c = 0; c < CH; ++c) {                                       \
+    const size_t off = static_cast<size_t>(X) * kMT * D + static_cast<size_t>(tid + 512 * c) * 8; \
+    kS[S_][c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(kb + off)); \
+    vS[S_][c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(vb + off)); \
+  }
+#define AQUA_PK_MFMA(BUF)                                                                \
+  _Pragma("unroll") for (int tb = TBW * tb0; tb < TBW * tb0 + TBW; ++tb) {               \
+    u32x4_t av[KS];                                                                      \
+    _Pragma("unroll") for (int st = 0; st < KS; ++st) av[st] =                           \
+        *reinterpret_cast<const u32x4_t *>(&ks[BUF][16 * tb + (lane & 15)][32 * st + 8 * (lane >> 4)]); \
+    to_slice(tb, proj_mfma<KS>(av, pp));                                                 \
+  }
+#define AQUA_PK_TILE(S_, X, BUF)                                                         \
+  {                                                                                      \
+    _Pragma("unroll") for (int c = 0; c < CH; ++c) {                                     \
+      const int pc = tid + 512 * c;                                                      \
+      __builtin_nontemporal_store(                                                       \
+          vS[S_][c], reinterpret_cast<u32x4_t *>(vcb + static_cast<size_t>(X) * kMT * D + pc * 8)); \
+      *reinterpret_cast<u32x4_t *>(&ks[BUF][pc / PR][8 * (pc % PR)]) = kS[S_][c];        \
+    }                                                                                    \
+    lds_barrier();                                                                       \
+    AQUA_PK_MFMA(BUF)                                                                    \
+    bf16_t *dst = kprow + static_cast<size_t>(X) * kMT;                                  \
+    _Pragma("unroll") for (int j = 0; j < NST; ++j) __builtin_nontemporal_store(         \
+        *reinterpret_cast<const u32x4_t *>(&kt[w][srow + RPS * j][scol]),                \
+        reinterpret_cast<u32x4_t *>(dst + j * kprow8));                                  \
+  }
+  // P's parts first (once per workgroup): splitting them with a tile's loads in flight would
+  // need more registers than four wavefronts per SIMD leave
+  PParts<KS> pp;
+  split_p_parts<KS>(pv, pp);
+  int tail_buf = 0;
+  if (x1 - x0 >= kNS) {
+    // tiles x0 .. x0 + kNS - 2 requested, then rotations of kNS tiles: each tile's loads go out
+    // kNS - 1 tiles ahead of its work; the first rotation is peeled so that the loop's entry has
+    // the same loads and stores in flight as its back edge (the waits inside stay exact).  Past
+    // the run's end a rotation works on its last tile again, storing the same values.
+#pragma unroll
+    for (int s = 0; s < kNS - 1; ++s) AQUA_PK_LOAD(s, x0 + s);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < kNS; ++s) {
+      AQUA_PK_LOAD((s + kNS - 1) % kNS, min(x0 + s + kNS - 1, x1 - 1));
+      __builtin_amdgcn_sched_barrier(0);
+      AQUA_PK_TILE(s, x0 + s, s & 1);
+    }
+    for (int x = x0 + kNS; x < x1; x += kNS) {
+#pragma unroll
+      for (int s = 0; s < kNS; ++s) {
+        AQUA_PK_LOAD((s + kNS - 1) % kNS, min(x + s + kNS - 1, x1 - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        AQUA_PK_TILE(s, min(x + s, x1 - 1), s & 1);
+      }
+    }
+  } else {
+    // a short run: one tile at a time
+    for (int x = x0; x < x1; ++x) {
+      AQUA_PK_LOAD(0, x);
+      AQUA_PK_TILE(0, x, x & 1);
+    }
+    tail_buf = (x1 - x0) & 1;
+  }
+  // the ragged tail (tokens full * 64 .. n - 1), by the last workgroup of the (b, g), in the LDS
+  // buffer the last whole tile did not use
+  const int nt = n - full * kMT;
+  if (blockIdx.x != gridDim.x - 1 || nt == 0) return;
+  {
+    const int t0 = full * kMT;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int pc = tid + 512 * c, t = pc / PR;
+      const size_t off = static_cast<size_t>(min(t0 + t, n - 1)) * D + 8 * (pc % PR);
+      const u32x4_t kr = *reinterpret_cast<const u32x4_t *>(kb + off);
+      const u32x4_t vr = *reinterpret_cast<const u32x4_t *>(vb + off);
+      *reinterpret_cast<u32x4_t *>(&ks[tail_buf][t][8 * (pc % PR)]) = kr;
+      if (t < nt)
+        *reinterpret_cast<u32x4_t *>(vcb + static_cast<size_t>(t0 + t) * D + 8 * (pc % PR)) = vr;
+    }
+  }
+  lds_barrier();
+  if (tail_buf) {
+    AQUA_PK_MFMA(1)
+  } else {
+    AQUA_PK_MFMA(0)
+  }
+  bf16_t *dst = kprow + static_cast<size_t>(full) * kMT;
+  // each lane's 8 tokens: whole when inside the tail, else token by token up to its end
+#pragma unroll
+  for (int j = 0; j < NST; ++j) {
+    bf16_t *d = dst + j * kprow8;
+    const bf16_t *src = &kt[w][srow + RPS * j][scol];
+    if (scol + 8 <= nt) {
+      *reinterpret_cast<u32x4_t *>(d) = *reinterpret_cast<const u32x4_t *>(src);
+    } else {
+      for (int e = 0; scol + e < nt; ++e) d[e] = src[e];
+    }
+  }
+#undef AQUA_PK_LOAD
+#undef AQUA_PK_MFMA
+#undef AQUA_PK_TILE
+}
+
 // Few tokens per (b, g) (a decode step's new key, an H2O slot): one workgroup of D/16 wavefronts
 // per (b, g), wavefront w projecting output dims [16 w, 16 w + 16) of the n <= 16 rows.
 template <int D>
@@ -296,6 +461,20 @@ hipError_t launch_pk(const void *k_raw, const void *v_raw, const float *P, int B
     if (n <= 16) {
       project_keys_small_mfma_kernel<D><<<dim3(B * Hkv), dim3(D / 16 * 64), 0, s>>>(
           kr, vr, P, n, d_store, T_cap, len0, slots, static_cast<bf16_t *>(kp),
+          static_cast<bf16_t *>(v));
+      return hipGetLastError();
+    }
+    const int full = n / kMT;
+    if (!slots && vr && len0 % 8 == 0 && full > 0) {
+      // whole tiles stream; about one workgroup per CU, each over a contiguous run of tiles (a
+      // whole number of rotations where runs are long)
+      const int groups = B * Hkv;
+      const int per_group = std::max(1, std::min(full, (device_cu_count() + groups - 1) / groups));
+      int tpw = (full + per_group - 1) / per_group;
+      if (tpw >= kNS) tpw = (tpw + kNS - 1) / kNS * kNS;
+      const int wgs = (full + tpw - 1) / tpw;
+      project_keys_stream_kernel<D><<<dim3(wgs, groups), dim3(512), 0, s>>>(
+          kr, vr, P, n, d_store, T_cap, len0, tpw, static_cast<bf16_t *>(kp),
           static_cast<bf16_t *>(v));
       return hipGetLastError();
     }

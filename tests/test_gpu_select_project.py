@@ -131,6 +131,62 @@ def test_project_keys_append(dtype, d, d_store, n, len0, T_cap):
     assert np.isnan(kp_h[:, :, :, :len0]).all() and np.isnan(kp_h[:, :, :, len0 + n:]).all()
 
 
+@pytest.mark.parametrize("B,Hkv,d,d_store,n,len0,T_cap,groups", [
+    (16, 8, 128, 128, 8191, 0, 8448, (0, 37, 64, 127)),  # the cache fill: runs of 64 and 63
+    (16, 8, 128, 96, 4000, 8, 4096, (1, 90)),           # d_store cut: dims past it recomputed
+    (16, 8, 64, 64, 3000, 64, 3072, (5, 66, 127)),       # d = 64: two wavefronts per column block
+    (4, 8, 128, 128, 5000, 16, 5120, (0, 31)),           # runs of 12 and a last of 6
+])
+def test_project_keys_streamed_runs(B, Hkv, d, d_store, n, len0, T_cap, groups):
+    """Bulk appends of whole tiles (bf16, no slots, aligned start) stream runs of tiles per
+    workgroup; the ragged tail goes through the one-tile kernel.  Sampled (b, g) groups are
+    checked in full against the oracle; V is copied exactly everywhere."""
+    P64 = gen.make_projection(9, d)
+    P32 = torch.from_numpy(P64.astype(np.float32))
+    g = torch.Generator().manual_seed(11)
+    K = (torch.randn(B, Hkv, n, d, generator=g) * 2).to(torch.bfloat16)
+    V = torch.randn(B, Hkv, n, d, generator=g).to(torch.bfloat16)
+    kp, v = new_cache(B, Hkv, d, d_store, T_cap, "bf16")
+    cache = aq.make_cache(kp, v, len0)
+    aq.aqua_project_keys(cache, K.to(DEV), V.to(DEV), P32.to(DEV), n)
+    torch.cuda.synchronize()
+    assert cache.len == len0 + n
+    assert torch.equal(v[:, :, len0:len0 + n].cpu(), V)
+    Pf = storage_to_f64(P32)
+    for flat in groups:
+        b, h = divmod(flat, Hkv)
+        Kg = K[b, h].float().double().numpy()
+        ref = O.project_keys_stored(Kg, Pf, "bf16", d_store)
+        got = kp[b, h, :, len0:len0 + n].float().double().cpu().numpy().T
+        exact = O.project(Kg, Pf)[..., :d_store]
+        acc_err = (3 * d + 1) * 2.0 ** -24 * (np.abs(Kg) @ np.abs(Pf))[..., :d_store]
+        big = np.maximum(np.abs(exact), np.abs(got))
+        assert np.all(np.abs(got - ref) <= _ulp_bf16(big) + acc_err), (b, h)
+        assert np.mean(got == ref) > 0.999, (b, h)
+        kh = kp[b, h].float().cpu().numpy()
+        assert np.isnan(kh[:, :len0]).all() and np.isnan(kh[:, len0 + n:]).all(), (b, h)
+
+
+def test_project_keys_streamed_equals_few_token():
+    """The streamed bulk append (runs of 8 and 7 tiles per workgroup here) and one-token appends
+    give the same K' bits."""
+    B, Hkv, d, n = 16, 8, 128, 1000
+    P32 = torch.from_numpy(gen.make_projection(10, d).astype(np.float32)).to(DEV)
+    g = torch.Generator().manual_seed(12)
+    K = torch.randn(B, Hkv, n, d, generator=g).to(torch.bfloat16).to(DEV)
+    V = torch.randn(B, Hkv, n, d, generator=g).to(torch.bfloat16).to(DEV)
+    kp1, v1 = new_cache(B, Hkv, d, d, 1024, "bf16")
+    kp2, v2 = new_cache(B, Hkv, d, d, 1024, "bf16")
+    c1, c2 = aq.make_cache(kp1, v1, 0), aq.make_cache(kp2, v2, 0)
+    aq.aqua_project_keys(c1, K, V, P32, n)
+    for t in range(n):
+        aq.aqua_project_keys(c2, K[:, :, t:t + 1].contiguous(), V[:, :, t:t + 1].contiguous(),
+                             P32, 1)
+    torch.cuda.synchronize()
+    assert torch.equal(kp1[..., :n], kp2[..., :n])
+    assert torch.equal(v1[:, :, :n], v2[:, :, :n])
+
+
 @pytest.mark.parametrize("n", [5, 40])
 def test_project_keys_slots(n):
     """Explicit destination columns (the H2O slot append): a few-token launch and a tiled one
