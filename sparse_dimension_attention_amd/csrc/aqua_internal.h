@@ -279,12 +279,12 @@ struct DecodeArgs {
   float *mass;           // [B][Hkv][T_cap] or nullptr
   float *out;            // [B][Hq][d]
   // Arrival counters of the cross-workgroup merge, each tagged with the call's epoch in its high
-  // 32 bits (arrive_last): a word left by another call, or garbage, is never taken for this
-  // call's count, so the workspace needs no clearing.
+  // 32 bits (arrive_last): a word left by another call, or garbage, is never taken
+  // for this call's count, so the workspace needs no clearing.
   uint64_t *counters;      // [B*Hkv]
   uint64_t *run_counters;  // [B*Hkv][run_stride]: per run of splits (two-level merge)
   int run_stride;
-  uint32_t epoch;        // nonzero, distinct for calls that may find each other's counters
+  uint32_t epoch;        // nonzero, one more than the previous call's (mod 2^32, 0 skipped)
   float *partials;       // [B][Hq][S][d+2]  (m, l, o[d]) in log2 units
   float *scores;         // [B][Hq][T_cap]   log2-domain scores (mass mode only)
   int B, Hq, Hkv, d, d_store, T_cap, len;

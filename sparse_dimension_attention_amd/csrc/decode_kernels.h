@@ -78,15 +78,31 @@ __device__ __forceinline__ float coherent_load(const float *p) {
 }
 
 // Counts this workgroup's arrival at a counter shared by `total` workgroups of one call; true in
-// the last to arrive.  The word holds (epoch << 32) | count.  The usual arrival is one atomic add
-// on a word that already carries this call's epoch.  The first arrival of a call finds the word of
-// another call (or garbage: the workspace is never cleared) and installs (epoch, 1) by
-// compare-and-swap; an arrival whose add landed on that stale word retries the same way, so stale
+// the last to arrive.  The word holds (epoch << 32) | count.  An arrival first lifts the word to
+// (epoch, 0) with an atomic max (no return; a word already at this epoch keeps its count), then
+// adds 1.  Epochs grow by one per call (0 is never one) and the last arrival of a call clears the
+// word, so the max finds a smaller epoch there.  Each arrival's max and add are one location's
+// modifications in program order, so the call's first operation on the word is a max and every
+// add lands on a word that carries this call's epoch: one round trip, no retries.  (With the add
+// alone, every arrival of a call could land on the stale word before any had replaced it, and
+// all of them then retried in turn: 16 arrivals per group took ~16 us.)  A word that still does
+// not carry the epoch (garbage with a larger one: the workspace is never cleared) gets (epoch, 1)
+// by compare-and-swap; an arrival whose add landed on such a word retries the same way, so stale
 // adds are never counted.  Every failed swap means another arrival changed the word, so the loop
-// ends after at most `total` rounds.  (The low half would carry into the epoch only from a count of
-// 2^32 - 1, which no call reaches.)
-__device__ __forceinline__ bool arrive_last(uint64_t *ctr, uint32_t epoch, uint32_t total) {
+// ends after at most `total` rounds.  (The low half would carry into the epoch only from a count
+// of 2^32 - 1, which no call reaches.)
+// In the forms without a prologue the max goes out at the workgroup's start instead
+// (install_epoch; lifted = true here): the arrival is then the add alone, ~1 us shorter with 16
+// arrivals per group.  (In the fused forms an early max would hold up the prologue's first wait
+// for its loads, which the in-order counter makes wait for the max too.)
+__device__ __forceinline__ void install_epoch(uint64_t *ctr, uint32_t epoch) {
+  atomicMax(reinterpret_cast<unsigned long long *>(ctr),
+            static_cast<unsigned long long>(epoch) << 32);
+}
+__device__ __forceinline__ bool arrive_last(uint64_t *ctr, uint32_t epoch, uint32_t total,
+                                            bool lifted) {
   unsigned long long *p = reinterpret_cast<unsigned long long *>(ctr);
+  if (!lifted) install_epoch(ctr, epoch);
   const unsigned long long old = atomicAdd(p, 1ull);
   if (static_cast<uint32_t>(old >> 32) == epoch) return static_cast<uint32_t>(old) + 1u == total;
   unsigned long long cur = old + 1ull;  // a guess; the swap returns the word's actual value
@@ -276,7 +292,7 @@ __device__ void merge_splits(const DecodeArgs &a, size_t head0, int bg, float *s
 
 // Ends a split's work once its partials are published: the group's last workgroup merges.
 // Returns in every workgroup; s_last is a workgroup-shared flag.
-template <int D, int G, int NT>
+template <int D, int G, int NT, bool LIFTED>
 __device__ __forceinline__ void finish_split(const DecodeArgs &a, size_t head0, int bg,
                                              int split, int *s_last, float *s_M, float *s_L,
                                              int restart) {
@@ -288,20 +304,22 @@ __device__ __forceinline__ void finish_split(const DecodeArgs &a, size_t head0, 
     const int cnt = min(kMergeFan, a.S - first);
     const int nrun = (a.S + kMergeFan - 1) / kMergeFan;
     uint64_t *rc = a.run_counters + static_cast<size_t>(bg) * a.run_stride + run;
-    if (tid == 0) *s_last = arrive_last(rc, a.epoch, static_cast<uint32_t>(cnt));
+    if (tid == 0) *s_last = arrive_last(rc, a.epoch, static_cast<uint32_t>(cnt), LIFTED);
     __syncthreads();
     if (!*s_last) return;
     merge_partials<D, G, NT>(a, head0, first, cnt, 1, first, s_M, s_L);
     if (tid == 0) clear_counter(rc);
     __builtin_amdgcn_s_waitcnt(0);  // the run's result has landed
     __syncthreads();
-    if (tid == 0) *s_last = arrive_last(&a.counters[bg], a.epoch, static_cast<uint32_t>(nrun));
+    if (tid == 0)
+      *s_last = arrive_last(&a.counters[bg], a.epoch, static_cast<uint32_t>(nrun), LIFTED);
     __syncthreads();
     if (!*s_last) return;
     merge_splits<D, G, NT>(a, head0, bg, s_M, s_L, restart, nrun, kMergeFan);
     return;
   }
-  if (tid == 0) *s_last = arrive_last(&a.counters[bg], a.epoch, static_cast<uint32_t>(a.S));
+  if (tid == 0)
+    *s_last = arrive_last(&a.counters[bg], a.epoch, static_cast<uint32_t>(a.S), LIFTED);
   __syncthreads();
   if (!*s_last) return;
   merge_splits<D, G, NT>(a, head0, bg, s_M, s_L, restart, a.S, 1);
@@ -577,6 +595,12 @@ void decode_kernel(DecodeArgs a) {
   // workgroups 16 apart would otherwise start on the same batch (measured at 131072 tokens:
   // 106 us with the plain multiple, 97 us mixed; unchanged at batch 16).
   const int wg_mix = (wg_lin * 5) ^ (wg_lin >> 4);
+  if (!FUSED && tid == 0) {  // this call's epoch into the counters the workgroup arrives at
+    install_epoch(&a.counters[bg], a.epoch);
+    if (a.S > 2 * kMergeFan)
+      install_epoch(a.run_counters + static_cast<size_t>(bg) * a.run_stride + split / kMergeFan,
+                    a.epoch);
+  }
 
   // Fused, bf16 storage: the first two batches of K' rows are requested before the prologue,
   // speculatively, so that HBM is busy while the queries are projected and selected.  They are a
@@ -989,7 +1013,7 @@ void decode_kernel(DecodeArgs a) {
   }
 
   // ---- the last workgroup of this (b, g) merges all splits
-  finish_split<D, G, NT>(a, head0, bg, split, &s_last, s_M, s_L, -1);
+  finish_split<D, G, NT, !FUSED>(a, head0, bg, split, &s_last, s_M, s_L, -1);
 }
 
 // ------------------------------------------------------------------ short contexts
@@ -1054,6 +1078,7 @@ __device__ __forceinline__ void short_attend(const DecodeArgs &a, const H2OArgs 
   const size_t head0 = static_cast<size_t>(b) * a.Hq + static_cast<size_t>(g) * G;
   const size_t slot0 = static_cast<size_t>(bg) * a.T_cap;
   const int t0 = split * kShortChunk;
+  if (!FUSED && tid == 0) install_epoch(&a.counters[bg], a.epoch);
 
   // ---- K' of this chunk, wavefront w's stored dims, every load in flight at once
   const int tl = min(t0 + TPL * lane, a.T_cap - TPL);  // stays inside the row; masked below
@@ -1262,7 +1287,8 @@ __device__ __forceinline__ void short_attend(const DecodeArgs &a, const H2OArgs 
   // context has at most 16 chunks, one merge level
   __builtin_amdgcn_s_waitcnt(0);  // this thread's partials, scores and cache writes have landed
   __syncthreads();
-  if (tid == 0) s_last = arrive_last(&a.counters[bg], a.epoch, static_cast<uint32_t>(a.S));
+  if (tid == 0)
+    s_last = arrive_last(&a.counters[bg], a.epoch, static_cast<uint32_t>(a.S), !FUSED);
   __syncthreads();
   if (!s_last) return;
   if (H2O && victim >= 0 && tid == 0) hh.slot_pos[slot0 + victim] = hh.t_new;
