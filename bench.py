@@ -614,11 +614,31 @@ def bench_retention(dev):
     kc, _ = make_qk_block(c["id"], "calib_k", (0, 0), 8192, d, c["tau"], inp["P64"])
     g = torch.Generator().manual_seed(12345)
     qr, rr = torch.linalg.qr(torch.randn(d, d, dtype=torch.float64, generator=g))
+    calib = torch.from_numpy(np.concatenate([qc, kc])).float().to(dev)
     projections = {
         "generator": inp["P"],
-        "calibrated": calibrate_projection(torch.from_numpy(np.concatenate([qc, kc]))),
+        "calibrated": calibrate_projection(calib),
         "uncalibrated": (qr * torch.sign(torch.diagonal(rr))).float(),
     }
+    # the calibration's GPU part: aqua_gram over the 16384 fp32 vectors (9 exact part products
+    # per pair on MFMA), launches back to back between two events
+    n_cal = calib.shape[0]
+    ws_cal = torch.empty(aq.aqua_gram_workspace(aq.AQUA_F32, n_cal, d), dtype=torch.uint8,
+                         device=dev)
+    gram = torch.empty(d, d, dtype=torch.float64, device=dev)
+    for _ in range(3):
+        aq.aqua_gram(calib, gram, ws_cal)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(20):
+        aq.aqua_gram(calib, gram, ws_cal)
+    e1.record()
+    torch.cuda.synchronize()
+    gram_us = e0.elapsed_time(e1) * 1e3 / 20
+    calibration = {"samples": n_cal, "d": d, "dtype": "f32", "gram_us": gram_us,
+                   "gbs_samples": n_cal * d * 4 / (gram_us * 1e-6) / 1e9,
+                   "tflops_executed": 9 * 2 * n_cal * d * d / (gram_us * 1e-6) / 1e12,
+                   "eigensolve": "host float64 (torch.linalg.eigh of the d x d Gram matrix)"}
     k_all, v_all = inp["k"].to(dev), inp["v"].to(dev)
     q = inp["q"].reshape(B * Hq, d).to(dev)
     scale = 1.0 / math.sqrt(d)
@@ -655,7 +675,8 @@ def bench_retention(dev):
             rows[str(k)] = {"magnitude": lm, "slicing": ls, "slicing_over_magnitude": ls / lm}
         res[name] = rows
     return {"workload": "llama8b_decode_bf16_b4_t4096", "loss": "relative L2 distance of the "
-            "decode output at k from the output at k=128, same P", "by_projection": res}
+            "decode output at k from the output at k=128, same P", "by_projection": res,
+            "calibration": calibration}
 
 
 def bench_h2o(dev, reps: int):

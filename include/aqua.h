@@ -227,11 +227,28 @@ aqua_status aqua_h2o_step(aqua_cache *c, int32_t Hq, const void *q, const void *
                           int32_t recent, int32_t *victim, float *out, float *q_proj_out,
                           uint32_t *mask_out, void *ws, size_t ws_bytes, void *stream);
 
+/* Offline projection: the Gram matrix G = X^T X of calibration vectors X, whose eigenvectors in
+ * decreasing order of eigenvalue are the right singular vectors of X, i.e. the columns of P
+ * (digest of arXiv 2509.11155, section 方法详解 / 技术框架: P from an SVD on a calibration
+ * set; edgentiq blog, "How AQUA Works", step 1).  The d x d eigensolve is the caller's.
+ *   dtype : AQUA_F32 or AQUA_BF16 (of x).
+ *   x     : device [n][d], row-major, one calibration vector (a query or a key) per row.
+ *   n     : rows, >= 1;  d: 64 or 128.
+ *   gram  : out device double [d][d] (the full symmetric matrix).
+ *   ws    : device workspace of aqua_gram_workspace() bytes (contents need no clearing).
+ * Every product is exact (fp32 input as three bf16 parts each); the sums are fp32 within chunks
+ * of 128 rows and fp64 across chunks, so |G - X^T X| <= gamma_m (|X|^T |X|) elementwise with
+ * m = 128 (bf16) or 9 * 128 (fp32) terms, up to the fp64 sum. */
+aqua_status aqua_gram_workspace(int32_t dtype, int64_t n, int32_t d, size_t *bytes);
+aqua_status aqua_gram(int32_t dtype, const void *x, int64_t n, int32_t d, double *gram,
+                      void *ws, size_t ws_bytes, void *stream);
+
 /* Diagnostics.  Streaming-read probe: reads `bytes` of buf once (16-byte non-temporal loads,
  * the decode kernel's access, sixteen in flight per lane; `blocks` workgroups of 256 threads,
  * each over one contiguous slice of ceil(bytes / 16 / blocks) pieces) and writes one folded word
- * per workgroup to sink [blocks] (so that the reads are not optimised away).  Timing a launch gives the device's measured streaming-read bandwidth, the denominator
- * reported next to the vendor's HBM peak.  bytes a positive multiple of 16. */
+ * per workgroup to sink [blocks] (so that the reads are not optimised away).  Timing launches
+ * gives the device's measured streaming-read bandwidth, the denominator reported next to the
+ * vendor's HBM peak.  bytes a positive multiple of 16. */
 aqua_status aqua_stream_read_probe(const void *buf, size_t bytes, int32_t blocks, uint32_t *sink,
                                    void *stream);
 

@@ -28,7 +28,7 @@ EXPORTS = ("aqua_version", "aqua_last_error", "aqua_project_keys", "aqua_select_
            "aqua_decode_workspace", "aqua_decode", "aqua_decode_step", "aqua_decode_step_noalloc",
            "aqua_prefill_workspace",
            "aqua_prefill_chunk", "aqua_h2o_init", "aqua_h2o_victim", "aqua_h2o_step",
-           "aqua_stream_read_probe")
+           "aqua_gram_workspace", "aqua_gram", "aqua_stream_read_probe")
 
 
 class AquaError(RuntimeError):
@@ -73,6 +73,8 @@ def load_library() -> ctypes.CDLL:
         "aqua_h2o_init": ([cp, P, I32, I32, cp, P, P, P], ctypes.c_int),
         "aqua_h2o_victim": ([P, P, I32, I32, I32, I32, I32, P, P], ctypes.c_int),
         "aqua_stream_read_probe": ([P, SZ, I32, P, P], ctypes.c_int),
+        "aqua_gram_workspace": ([I32, ctypes.c_int64, I32, ctypes.POINTER(SZ)], ctypes.c_int),
+        "aqua_gram": ([I32, P, ctypes.c_int64, I32, P, P, SZ, P], ctypes.c_int),
         "aqua_h2o_step": ([cp, I32, P, P, P, P, I32, I32, ctypes.c_float, P, P, I32, I32, P, P, P,
                            P, P, SZ, P], ctypes.c_int),
     }
@@ -211,6 +213,20 @@ def aqua_h2o_step(cache: aqua_cache, Hq: int, q, k_new, v_new, P, d_sel: int, k:
                                         _ptr(mass), _ptr(slot_pos), int(t_new), int(recent),
                                         _ptr(victim), _ptr(out), _ptr(q_proj_out),
                                         _ptr(mask_out), _ptr(ws), nbytes, _stream(stream)))
+
+
+def aqua_gram_workspace(dtype: int, n: int, d: int) -> int:
+    """Bytes of workspace aqua_gram needs for n calibration vectors of d dims."""
+    nb = ctypes.c_size_t()
+    _check(load_library().aqua_gram_workspace(int(dtype), int(n), int(d), ctypes.byref(nb)))
+    return nb.value
+
+
+def aqua_gram(x, gram, ws, stream=None):
+    """gram [d][d] (float64, device) = x^T x for calibration vectors x [n][d] (bf16 or fp32)."""
+    n, d = x.shape
+    _check(load_library().aqua_gram(dtype_code(x.dtype), _ptr(x), int(n), int(d), _ptr(gram),
+                                    _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def aqua_stream_read_probe(buf, blocks: int, sink, stream=None):

@@ -423,6 +423,38 @@ aqua_status aqua_h2o_init(const aqua_cache *full, const float *mass_full, int32_
                     "aqua_h2o_init launch");
 }
 
+static aqua_status gram_check(int32_t dtype, int64_t n, int32_t d) {
+  if (dtype != AQUA_F32 && dtype != AQUA_BF16) return fail(AQUA_ERR_DTYPE, "dtype %d", dtype);
+  if (d != 64 && d != 128) return fail(AQUA_ERR_SHAPE, "d=%d must be 64 or 128", d);
+  if (n < 1 || n > (static_cast<int64_t>(1) << 40) / d)
+    return fail(AQUA_ERR_SHAPE, "n=%lld out of range", static_cast<long long>(n));
+  return AQUA_OK;
+}
+
+aqua_status aqua_gram_workspace(int32_t dtype, int64_t n, int32_t d, size_t *bytes) {
+  g_err[0] = 0;
+  if (!bytes) return fail(AQUA_ERR_NULL, "bytes is required");
+  const aqua_status st = gram_check(dtype, n, d);
+  if (st != AQUA_OK) return st;
+  *bytes = aqua::gram_workspace_bytes(n, d);
+  return AQUA_OK;
+}
+
+aqua_status aqua_gram(int32_t dtype, const void *x, int64_t n, int32_t d, double *gram,
+                      void *ws, size_t ws_bytes, void *stream) {
+  g_err[0] = 0;
+  const aqua_status st = gram_check(dtype, n, d);
+  if (st != AQUA_OK) return st;
+  if (!x || !gram || !ws) return fail(AQUA_ERR_NULL, "x, gram and ws are required");
+  if (!aligned16(x) || !aligned16(gram) || !aligned16(ws))
+    return fail(AQUA_ERR_ALIGN, "x, gram and ws must be 16-byte aligned");
+  const size_t need = aqua::gram_workspace_bytes(n, d);
+  if (ws_bytes < need)
+    return fail(AQUA_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
+  return hip_status(aqua::launch_gram(dtype, x, n, d, gram, ws, static_cast<hipStream_t>(stream)),
+                    "aqua_gram launch");
+}
+
 aqua_status aqua_stream_read_probe(const void *buf, size_t bytes, int32_t blocks,
                                    uint32_t *sink, void *stream) {
   g_err[0] = 0;

@@ -361,6 +361,9 @@ hipError_t launch_prefill(const void *kp, const void *v, int B, int Hq, int Hkv,
                           void *ws, hipStream_t s);
 hipError_t launch_h2o_victim(float *mass, int32_t *slot_pos, int B, int Hkv, int n_slots,
                              int t_new, int recent, int32_t *victim, hipStream_t s);
+size_t gram_workspace_bytes(int64_t n, int d);
+hipError_t launch_gram(int dtype, const void *x, int64_t n, int d, double *g, void *ws,
+                       hipStream_t s);
 hipError_t launch_stream_read(const void *buf, size_t bytes, int blocks, uint32_t *sink,
                               hipStream_t s);
 hipError_t launch_h2o_init(int dtype, const void *kp_full, const void *v_full,

@@ -30,7 +30,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 14
+    assert len(names) == 16
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(aq.EXPORTS)
@@ -257,3 +257,19 @@ def test_stream_read_probe_rejects(lib):
     assert lib.aqua_stream_read_probe(FAKE, 1000, 4, FAKE, None) == A.AQUA_ERR_SHAPE
     assert lib.aqua_stream_read_probe(FAKE, 1024, 0, FAKE, None) == A.AQUA_ERR_SHAPE
     assert lib.aqua_stream_read_probe(FAKE + 4, 1024, 4, FAKE, None) == A.AQUA_ERR_ALIGN
+
+
+def test_gram_rejects(lib):
+    nb = ctypes.c_size_t()
+    assert lib.aqua_gram_workspace(A.AQUA_BF16, 1000, 128, ctypes.byref(nb)) == A.AQUA_OK
+    assert nb.value == 8 * 128 * 128 * 4  # eight 128-row chunks of fp32 partials
+    assert lib.aqua_gram_workspace(A.AQUA_BF16, 1000, 96, ctypes.byref(nb)) == A.AQUA_ERR_SHAPE
+    assert lib.aqua_gram_workspace(7, 1000, 128, ctypes.byref(nb)) == A.AQUA_ERR_DTYPE
+    assert lib.aqua_gram_workspace(A.AQUA_F32, 0, 64, ctypes.byref(nb)) == A.AQUA_ERR_SHAPE
+    assert lib.aqua_gram_workspace(A.AQUA_F32, 10, 64, None) == A.AQUA_ERR_NULL
+    big = 1 << 24
+    assert lib.aqua_gram(A.AQUA_F32, None, 10, 64, FAKE, FAKE, big, None) == A.AQUA_ERR_NULL
+    assert lib.aqua_gram(A.AQUA_F32, FAKE, 10, 64, None, FAKE, big, None) == A.AQUA_ERR_NULL
+    assert lib.aqua_gram(A.AQUA_F32, FAKE + 4, 10, 64, FAKE, FAKE, big, None) == A.AQUA_ERR_ALIGN
+    assert lib.aqua_gram(A.AQUA_F32, FAKE, 10, 64, FAKE, FAKE, 100, None) == A.AQUA_ERR_WORKSPACE
+    assert lib.aqua_gram(A.AQUA_BF16, FAKE, 10, 32, FAKE, FAKE, big, None) == A.AQUA_ERR_SHAPE
