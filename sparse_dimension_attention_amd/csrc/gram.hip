@@ -96,14 +96,24 @@ __global__ __launch_bounds__(512) void gram_partials_kernel(const KT *__restrict
   }
 }
 
-// G[i][j] = the chunks' partials added in fp64, chunk by chunk in order.
+// G[i][j] = the chunks' partials added in fp64, chunk by chunk in order (loads 8 chunks ahead).
 template <int D>
 __global__ __launch_bounds__(256) void gram_reduce_kernel(const float *__restrict__ part,
                                                           int nchunk, double *__restrict__ g) {
+  constexpr int U = 8;
   const int e = blockIdx.x * 256 + threadIdx.x;
   if (e >= D * D) return;
+  const float *p = part + e;
   double s = 0.0;
-  for (int c = 0; c < nchunk; ++c) s += static_cast<double>(part[static_cast<size_t>(c) * D * D + e]);
+  int c = 0;
+  for (; c + U <= nchunk; c += U) {
+    float v[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) v[j] = p[static_cast<size_t>(c + j) * D * D];
+#pragma unroll
+    for (int j = 0; j < U; ++j) s += static_cast<double>(v[j]);
+  }
+  for (; c < nchunk; ++c) s += static_cast<double>(p[static_cast<size_t>(c) * D * D]);
   g[e] = s;
 }
 
