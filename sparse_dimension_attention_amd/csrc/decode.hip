@@ -42,14 +42,23 @@ uint32_t next_epoch() {
 // 8192-token decode).  Counting only full splits keeps the finer layout where a ragged last split
 // would leave CUs without work (at 16 x 8 groups and 4097 .. 8191 tokens, 128 workgroups of 4096
 // tokens carry nearly all of it), and where the grid is small (a 32-workgroup grid at 16384 tokens
-// and batch 1 ran 48 against 35 us).
+// and batch 1 ran 48 against 35 us).  The 8-wavefront grid must also end on a (nearly) whole round
+// of one workgroup per CU: a part-filled last round runs after the first one, where the
+// 4-wavefront grid (two per CU) packs its splits more finely.  Measured at 16 x 8 groups (decode
+// kernel): 8193 .. 12288 tokens, 384 8-wavefront workgroups (1.5 rounds): 117 .. 138 us against
+// 101 .. 130 us with 4 wavefronts; 12289 .. 16384 tokens, 512 (2 rounds): 136 .. 166 us against
+// 144 .. 184 us.
 DecodeLayout decode_layout(int dtype, int G, int groups, int len, int cus) {
   DecodeLayout L;
   L.tokens_wave = 64 * (dtype == 1 ? 8 : 4);
   L.waves = G == 8 ? 2 : 4;
-  if (G == 4) {
-    const long full_wide = static_cast<long>(len) / (8 * L.tokens_wave);
-    if (groups > 0 && static_cast<long>(groups) * full_wide >= cus) L.waves = 8;
+  if (G == 4 && groups > 0) {
+    const long wide = 8L * L.tokens_wave;
+    const long full_wide = static_cast<long>(len) / wide;
+    const long wgs = static_cast<long>(groups) * ((len + wide - 1) / wide);
+    const long last_round = wgs % cus;  // workgroups in a part-filled last round, if any
+    const bool whole_rounds = last_round == 0 || 4 * last_round >= 3L * cus;
+    if (static_cast<long>(groups) * full_wide >= cus && whole_rounds) L.waves = 8;
   }
   L.split = L.waves * L.tokens_wave;
   return L;
