@@ -367,10 +367,11 @@ void project_keys_stream_kernel(const bf16_t *__restrict__ k_raw, const bf16_t *
       }
     }
   } else {
-    // a short run: one tile at a time
+    // a short run: one tile at a time, LDS buffers by the run's own tile count (the tail below
+    // takes the one its last tile did not use)
     for (int x = x0; x < x1; ++x) {
       AQUA_PK_LOAD(0, x);
-      AQUA_PK_TILE(0, x, x & 1);
+      AQUA_PK_TILE(0, x, (x - x0) & 1);
     }
     tail_buf = (x1 - x0) & 1;
   }

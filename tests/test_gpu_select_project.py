@@ -96,6 +96,7 @@ def _ulp_bf16(x):
     ("bf16", 128, 96, 17, 0, 64),      # smallest tiled launch (bf16)
     ("bf16", 128, 128, 256, 0, 256),   # two whole 128-token tiles, aligned 16-byte writes
     ("bf16", 128, 128, 200, 8, 256),   # aligned start, ragged last tile
+    ("bf16", 128, 128, 150, 0, 256),   # streamed: the tail's workgroup starts on an odd tile
     ("bf16", 64, 64, 200, 3, 256),     # d = 64 tiles (two wavefronts per column block)
     ("f32", 128, 96, 9, 0, 64),        # smallest tiled launch (fp32)
     ("f32", 128, 128, 1, 191, 192),    # a decode step filling the last column
