@@ -43,15 +43,49 @@ template <> __device__ __forceinline__ bf16_t store_elem<bf16_t>(float f) {
 }
 
 // ------------------------------------------------------------------ wave helpers (wave64)
+// Butterfly steps on the VALU instead of the LDS crossbar (ds_bpermute).  Each combines the
+// values of lanes i and i ^ off; the result of each step has the same bits in both lanes (the
+// operations are commutative), as a shuffle-based butterfly would give.
+//   off 32, 16: v_permlane32_swap / v_permlane16_swap of a register with itself leave the lower
+//     lane's value in the first result and the upper lane's in the second, in both lanes;
+//   off < 16:   a DPP row rotation by off.  Rotation by 8 is exactly lane ^ 8 within a 16-lane
+//     row; rotation by 4, 2, 1 equals lane ^ off once the values are already equal under
+//     lane ^ 2 off, ..., lane ^ 8 (they are, when the steps run from 32 down, as in wave_sum).
+__device__ __forceinline__ uint2 swap_halves(float v, int off) {
+  const uint32_t u = __float_as_uint(v);
+  const auto s = off == 32 ? __builtin_amdgcn_permlane32_swap(u, u, false, false)
+                           : __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return make_uint2(s[0], s[1]);
+}
+template <int ROR>
+__device__ __forceinline__ float row_ror(float v) {
+  static_assert(ROR >= 1 && ROR <= 15, "DPP row rotation");
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v),
+                                                    0x120 + ROR, 0xf, 0xf, false));
+}
+// v(lane) + v(lane ^ off) for off in {8, 16, 32}, with no precondition on v.
+__device__ __forceinline__ float add_xor(float v, int off) {
+  if (off == 8) return v + row_ror<8>(v);
+  const uint2 s = swap_halves(v, off);
+  return __uint_as_float(s.x) + __uint_as_float(s.y);
+}
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  uint2 s = swap_halves(v, 32);
+  v = fmaxf(__uint_as_float(s.x), __uint_as_float(s.y));
+  s = swap_halves(v, 16);
+  v = fmaxf(__uint_as_float(s.x), __uint_as_float(s.y));
+  v = fmaxf(v, row_ror<8>(v));
+  v = fmaxf(v, row_ror<4>(v));
+  v = fmaxf(v, row_ror<2>(v));
+  return fmaxf(v, row_ror<1>(v));
 }
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  v = add_xor(v, 32);
+  v = add_xor(v, 16);
+  v = add_xor(v, 8);
+  v += row_ror<4>(v);
+  v += row_ror<2>(v);
+  return v + row_ror<1>(v);
 }
 
 // Top-k of one row of D = 64 * E values held by a wavefront, lane l holding dims l + 64 e.

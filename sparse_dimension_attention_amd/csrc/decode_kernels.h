@@ -543,6 +543,7 @@ void decode_kernel(DecodeArgs a) {
   constexpr int WT = SM::WT;       // tokens per wavefront
   constexpr int EPL = Vec<KT>::N;  // V elements per lane per load
   constexpr int LPT = D / EPL;     // lanes per V row
+  static_assert(LPT >= 8, "the V rows' lane butterfly starts at lane ^ 8");
   constexpr int TPI = 64 / LPT;    // V rows per wavefront load
   constexpr int NWORD = SM::NWORD;
   constexpr int NT = NW * 64;
@@ -972,7 +973,7 @@ void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) o[h][e] += __shfl_xor(o[h][e], off, 64);
+      for (int e = 0; e < EPL; ++e) o[h][e] = add_xor(o[h][e], off);
   __syncthreads();  // every wavefront is done with the numerators
 
   // ---- merge the workgroup's wavefronts, write this split's partials
@@ -1051,6 +1052,7 @@ __device__ __forceinline__ void short_attend(const DecodeArgs &a, const H2OArgs 
   constexpr int TPL = 4;                  // tokens per lane per K' row load
   constexpr int EPL = 16 / sizeof(KT);    // V elements per lane per 16-byte load
   constexpr int LPT = D / EPL;            // lanes per V row
+  static_assert(LPT >= 8, "the V rows' lane butterfly starts at lane ^ 8");
   constexpr int TPI = 64 / LPT;           // V rows per wavefront load
   constexpr int RW = D / 4;               // most K' rows a wavefront reads
   constexpr int NL = 64 / TPI;            // V loads per lane
@@ -1236,7 +1238,7 @@ __device__ __forceinline__ void short_attend(const DecodeArgs &a, const H2OArgs 
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) o[h][e] += __shfl_xor(o[h][e], off, 64);
+      for (int e = 0; e < EPL; ++e) o[h][e] = add_xor(o[h][e], off);
 
   // ---- merge the 4 wavefronts, write this chunk's partials
   if (sub == 0) {
