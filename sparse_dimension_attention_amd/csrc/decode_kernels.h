@@ -617,7 +617,6 @@ void decode_kernel(DecodeArgs a) {
   uint4 kA[kUnroll], kB[kUnroll];
 
   // V rows of this wavefront's tokens: lane -> row sub of each group of TPI, elements cl * EPL..
-  constexpr int RB = TPI * kUnroll;  // rows per batch
   const int sub = lane / LPT, cl = lane - sub * LPT;
   const int nrow = min(WT, len_c - tw0);  // may be <= 0
   const KT *vbase = static_cast<const KT *>(a.v) +
@@ -829,6 +828,25 @@ void decode_kernel(DecodeArgs a) {
 #undef AQUA_K_LOAD
 #undef AQUA_K_FMA
 
+  // The V pass's first two batches (batches 1 and 2 when batch 0 came with the prologue) are
+  // requested here, before the softmax and the workgroup barrier: they depend on this
+  // wavefront's tokens only, and without them nothing would be in flight across that stretch.
+  // Rows past the cached length read the last cached row (weight 0), as in the V pass.
+  constexpr int RB = TPI * kUnroll;  // V rows per batch
+  constexpr int VB0 = VPRE ? 1 : 0;  // first batch requested here
+  uint4 vA[kUnroll], vB[kUnroll];
+  {
+    const int last = len_c > 0 ? len_c - 1 : 0;
+    const KT *vg = static_cast<const KT *>(a.v) + static_cast<size_t>(bg) * a.T_cap * D + cl * EPL;
+#pragma unroll
+    for (int i = 0; i < kUnroll; ++i)
+      vA[i] = load16(vg + static_cast<size_t>(min(tw0 + VB0 * RB + i * TPI + sub, last)) * D);
+#pragma unroll
+    for (int i = 0; i < kUnroll; ++i)
+      vB[i] = load16(vg + static_cast<size_t>(min(tw0 + (VB0 + 1) * RB + i * TPI + sub, last)) * D);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
   // ---- softmax numerators within the wavefront
 #pragma unroll
   for (int j = 0; j < TPL; ++j)
@@ -921,43 +939,34 @@ void decode_kernel(DecodeArgs a) {
         _Pragma("unroll") for (int e = 0; e < EPL; ++e) o[h][e] = fmaf(p[h], vv[e], o[h][e]); \
   }
   const int vbat = nrow > 0 ? (nrow + RB - 1) / RB : 0;
-  uint4 vA[kUnroll], vB[kUnroll];
   int bi = 0;
   if constexpr (VPRE) {
-    // batch 0 came in with the prologue.  Batch 1 is requested, then batch 0 is added, in every
-    // wavefront (one with fewer rows reads valid rows again and adds them at p = 0): a use under
-    // a branch would let the compiler move the prologue's loads down to it.
-    const int last = len_c > 0 ? len_c - 1 : 0;
-#pragma unroll
-    for (int i = 0; i < kUnroll; ++i)
-      vA[i] = load16(static_cast<const KT *>(a.v) +
-                     (static_cast<size_t>(bg) * a.T_cap + min(tw0 + RB + i * TPI + sub, last)) * D +
-                     cl * EPL);
-    __builtin_amdgcn_sched_barrier(0);
+    // batch 0 came in with the prologue and is added in every wavefront (one with fewer rows
+    // reads valid rows again and adds them at p = 0): a use under a branch would let the
+    // compiler move the prologue's loads down to it
     AQUA_V_FMA(vC, 0);
     bi = 1;
   }
-  if (vbat > bi) {
-    if constexpr (!VPRE) AQUA_V_LOAD(vA, 0);
-    for (; bi + 2 < vbat; bi += 2) {
-      progress_priority(nbat + bi, nbat + WT / (TPI * kUnroll));
-      AQUA_V_LOAD(vB, bi + 1);
-      __builtin_amdgcn_sched_barrier(0);
-      AQUA_V_FMA(vA, bi);
-      AQUA_V_LOAD(vA, bi + 2);
-      __builtin_amdgcn_sched_barrier(0);
-      AQUA_V_FMA(vB, bi + 1);
-    }
+  // batches bi (vA) and bi + 1 (vB) are in flight; each batch's loads go out two batches ahead
+  for (; bi + 3 < vbat; bi += 2) {
     progress_priority(nbat + bi, nbat + WT / (TPI * kUnroll));
-    if (bi + 1 < vbat) {
-      AQUA_V_LOAD(vB, bi + 1);
-      __builtin_amdgcn_sched_barrier(0);
-      AQUA_V_FMA(vA, bi);
-      __builtin_amdgcn_sched_barrier(0);
-      AQUA_V_FMA(vB, bi + 1);
-    } else if (bi < vbat) {
-      AQUA_V_FMA(vA, bi);
-    }
+    AQUA_V_FMA(vA, bi);
+    AQUA_V_LOAD(vA, bi + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    AQUA_V_FMA(vB, bi + 1);
+    AQUA_V_LOAD(vB, bi + 3);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // the last one to three batches: nothing fetched past the end
+  progress_priority(nbat + bi, nbat + WT / (TPI * kUnroll));
+  {
+    const int left = vbat - bi;
+    if (left >= 1) AQUA_V_FMA(vA, bi);
+    if (left == 3) AQUA_V_LOAD(vA, bi + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    if (left >= 2) AQUA_V_FMA(vB, bi + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (left == 3) AQUA_V_FMA(vA, bi + 2);
   }
 #undef AQUA_V_LOAD
 #undef AQUA_V_FMA
