@@ -463,15 +463,17 @@ __device__ __forceinline__ void select_group_heads(const DecodeArgs &a, size_t h
 // block's values of P are issued before after_loads() (the caller issues its own loads there, and
 // they stay in flight through the projection and the selection: the waits for P's values leave
 // them outstanding); otherwise the blocks go one at a time, each load followed by its use, for
-// fewer live registers.  LDS: s_qp [G+1][D],
+// fewer live registers.  after_proj() runs once the projection is done (more of the caller's
+// loads: issued up front as well, they would stall the prologue's instructions behind a full
+// memory pipeline).  LDS: s_qp [G+1][D],
 // s_mw [G][D/32], s_knew and s_vnew [D].  Ends with a workgroup barrier.
-template <int D, int G, int NT, bool ALL, typename F>
+template <int D, int G, int NT, bool ALL, typename F, typename F2>
 __device__ __forceinline__ void fused_project_select_mfma(const DecodeArgs &a, size_t head0,
                                                           int bg, bool with_key, bool split0,
                                                           float (*s_qp)[D],
                                                           uint32_t (*s_mw)[D / 32],
                                                           float *s_knew, float *s_vnew,
-                                                          F &&after_loads) {
+                                                          F &&after_loads, F2 &&after_proj) {
   constexpr int KS = D / 32, NB = D / 16, NW = NT / 64;
   constexpr int BPW = (NB + NW - 1) / NW;  // column blocks per wavefront
   static_assert(G + 1 <= 16, "queries and key fit one 16-row A operand");
@@ -512,6 +514,7 @@ __device__ __forceinline__ void fused_project_select_mfma(const DecodeArgs &a, s
     }
   }
   if (with_key && tid < D) s_vnew[tid] = vn;
+  after_proj();
   lds_barrier();
   select_group_heads<bf16_t, D, G, NT>(a, head0, with_key, split0, s_qp, s_mw, s_knew);
 }
@@ -645,23 +648,29 @@ void decode_kernel(DecodeArgs a) {
   // ---- fused prologue: project the group's queries (and the new key), select their dims
   if constexpr (FUSED) {
     if constexpr (SPEC) {
+      // The speculative loads go out in three parts, one batch each: at the start, after the
+      // projection, and after the selection.  All at once they would fill the memory pipeline
+      // (a CU holds about 8 KB of loads per wavefront in flight), and every instruction of the
+      // prologue behind them would wait for room to issue them.  Unconditional (a wavefront
+      // past the cached tokens reads its clamped, valid addresses): loads issued under a branch
+      // would make every later wait count them as possibly absent, i.e. wait for all of them.
       fused_project_select_mfma<D, G, NT, true>(
-          a, head0, bg, owner, split == 0, s_qp, s_mw, s_knew, s_vnew, [&] {
-            // unconditional (a wavefront past the cached tokens reads its clamped, valid
-            // addresses): loads issued under a branch would make every later wait count them as
-            // possibly absent, i.e. wait for all of them at once
+          a, head0, bg, owner, split == 0, s_qp, s_mw, s_knew, s_vnew,
+          [&] {
 #pragma unroll
             for (int i = 0; i < kUnroll; ++i)
               kA[i] = load16(kbase + static_cast<size_t>((spec_r0 + i) & (spec_w - 1)) * a.T_cap);
+          },
+          [&] {
 #pragma unroll
             for (int i = 0; i < kUnroll; ++i)
               kB[i] = load16(kbase + static_cast<size_t>((spec_r0 + kUnroll + i) & (spec_w - 1)) *
                                          a.T_cap);
-            v_prefetch();
           });
+      v_prefetch();
     } else if constexpr (sizeof(KT) == 2) {
       fused_project_select_mfma<D, G, NT, false>(a, head0, bg, owner, split == 0, s_qp, s_mw,
-                                                 s_knew, s_vnew, [] {});
+                                                 s_knew, s_vnew, [] {}, [] {});
     } else {
       fused_project_select<KT, D, G, NT>(a, head0, bg, owner, split == 0,
                                          reinterpret_cast<float *>(smem),
@@ -1139,7 +1148,7 @@ __device__ __forceinline__ void short_attend(const DecodeArgs &a, const H2OArgs 
     };
     if constexpr (sizeof(KT) == 2)
       fused_project_select_mfma<D, G, NT, true>(a, head0, bg, owner, split == 0, s_qp, s_mw,
-                                                s_knew, s_vnew, issue);
+                                                s_knew, s_vnew, issue, [] {});
     else
       fused_project_select<KT, D, G, NT>(a, head0, bg, owner, split == 0, sP, sq, s_qp, s_mw,
                                          s_knew, s_vnew, issue);
