@@ -413,12 +413,13 @@ def bench_shard(dev, steps: int, warmup: int):
 
 
 def bench_ragged(cache, q, k_new, v_new, P, c, ws, out, mask, steps: int, warmup: int):
-    """The headline step at context lengths that leave a ragged last split, on the headline's
-    cache (which holds 8192 tokens and room for 256 more): per length, the whole step
+    """The headline step at other context lengths on the headline's cache (which holds 8192
+    tokens and room for 256 more): 2048 and 4096 (at this batch the split-T kernel, not the
+    short one), and lengths that leave a ragged last split; per length, the whole step
     (aqua_decode_step) K times back to back between two HIP events, and its GB/s."""
     B, Hq, Hkv, d, k = c["B"], c["Hq"], c["Hkv"], c["d"], c["k"]
     res = {}
-    for Tn in (4097, 5000, 6000, 7000, 8193):
+    for Tn in (2048, 4096, 4097, 5000, 6000, 7000, 8193):
         def step():
             cache.len = Tn - 1
             aq.aqua_decode_step(cache, Hq, q, k_new, v_new, P, d, k, 1.0 / math.sqrt(d), out, ws,

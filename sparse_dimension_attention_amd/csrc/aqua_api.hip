@@ -374,6 +374,7 @@ aqua_status aqua_h2o_step(aqua_cache *c, int32_t Hq, const void *q, const void *
 
   aqua::DecodeArgs a{};
   fill_decode_args(c, Hq, c->len, scale, mass, out, ws, a);
+  a.S = (c->len + aqua::kShortChunk - 1) / aqua::kShortChunk;  // the step runs the short kernel
   a.kp_w = c->kp;
   a.v_w = c->v;
   a.q_raw = q;

@@ -365,7 +365,7 @@ constexpr int kShortChunk = 256;  // tokens per workgroup of the short-context k
 constexpr int kMergeFan = 8;      // splits per run of the two-level merge
 // forms of the short-context kernel: aqua_decode, aqua_decode_step, aqua_h2o_step
 enum ShortMode { kShortPlain = 0, kShortStep = 1, kShortH2O = 2 };
-bool decode_short(int len);
+bool decode_short(int len, int groups, int cus);  // the short kernel serves this decode
 // partials per head that aqua_decode writes (groups = B * Hkv)
 int decode_splits(int dtype, int G, int groups, int len, int cus);
 size_t decode_workspace_bytes(int dtype, int B, int Hq, int Hkv, int d, int T_cap);

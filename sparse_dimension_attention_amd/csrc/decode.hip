@@ -64,10 +64,20 @@ DecodeLayout decode_layout(int dtype, int G, int groups, int len, int cus) {
   return L;
 }
 
-bool decode_short(int len) { return len <= kDecodeShortMax; }
+// The short kernel (256-token workgroups; its fused form one workgroup per CU at a time) for up
+// to kDecodeShortMax tokens while its grid fills at most two rounds of the device; past that the
+// split-T kernel, whose floor is one 512-token segment per wavefront (~34 us for the decode,
+// ~39 us for the fused step), is faster.  Measured, fused step / decode, short against split-T
+// (Hq 32, Hkv 8, d 128, k 96): B4 x 4096 tokens (512 short workgroups) 39.3 / 23.5 against
+// 39.5 / 34.1 us; B8 x 4096 and B16 x 2048 (1024) 75.0 / 41.0 against 39.5 / 34.3 us; B16 x 4096
+// (2048) 142.8 / 71.7 against 49.8 / 44.9 us; B1 x 256 18.7 / 12.7 against 32.1 / 26.9 us.
+bool decode_short(int len, int groups, int cus) {
+  return len <= kDecodeShortMax &&
+         static_cast<long>(groups) * ((len + kShortChunk - 1) / kShortChunk) <= 2L * cus;
+}
 
 int decode_splits(int dtype, int G, int groups, int len, int cus) {
-  if (decode_short(len)) return (len + kShortChunk - 1) / kShortChunk;
+  if (decode_short(len, groups, cus)) return (len + kShortChunk - 1) / kShortChunk;
   const DecodeLayout L = decode_layout(dtype, G, groups, len, cus);
   return (len + L.split - 1) / L.split;
 }
@@ -125,14 +135,16 @@ hipError_t launch_short(int dtype, const DecodeArgs &a, const H2OArgs &h, int mo
 }  // namespace
 
 hipError_t launch_decode(int dtype, const DecodeArgs &a, hipStream_t s) {
-  if (decode_short(a.len)) return launch_short(dtype, a, H2OArgs{}, kShortPlain, s);
+  if (decode_short(a.len, a.B * a.Hkv, device_cu_count()))
+    return launch_short(dtype, a, H2OArgs{}, kShortPlain, s);
   return launch_split(dtype, a, false, s);
 }
 
-// a.S must be decode_splits(dtype, G, B * Hkv, a.len, cus): the short kernel's chunk count at
-// short lengths
+// a.S must be decode_splits(dtype, G, B * Hkv, a.len, cus): the short kernel's chunk count where
+// decode_short holds
 hipError_t launch_decode_step(int dtype, const DecodeArgs &a, hipStream_t s) {
-  if (decode_short(a.len)) return launch_short(dtype, a, H2OArgs{}, kShortStep, s);
+  if (decode_short(a.len, a.B * a.Hkv, device_cu_count()))
+    return launch_short(dtype, a, H2OArgs{}, kShortStep, s);
   return launch_split(dtype, a, true, s);
 }
 

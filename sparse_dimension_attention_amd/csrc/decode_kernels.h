@@ -1146,9 +1146,9 @@ __device__ __forceinline__ void short_attend(const DecodeArgs &a, const H2OArgs 
       load_k();
       load_v();
     };
-    if constexpr (sizeof(KT) == 2)
+    if constexpr (sizeof(KT) == 2)  // K' at the start, V after the projection (see decode_kernel)
       fused_project_select_mfma<D, G, NT, true>(a, head0, bg, owner, split == 0, s_qp, s_mw,
-                                                s_knew, s_vnew, issue, [] {});
+                                                s_knew, s_vnew, load_k, load_v);
     else
       fused_project_select<KT, D, G, NT>(a, head0, bg, owner, split == 0, sP, sq, s_qp, s_mw,
                                          s_knew, s_vnew, issue);

@@ -103,8 +103,8 @@ def test_decode_fullsize_all_heads(full):
 
 def test_workspace_needs_no_clearing(full):
     """One workspace, filled with random bytes and never cleared, serves calls of different
-    lengths (the 8-wavefront layout at 8192 tokens, the 4-wavefront one at 6000, the short kernel
-    at 3000) in turn: every call gives the bits of the same call on a zeroed workspace of its own,
+    lengths (the 8-wavefront layout at 8192 tokens, the 4-wavefront one at 6000 and at 3000) in
+    turn: every call gives the bits of the same call on a zeroed workspace of its own,
     and those are checked against the oracle on a sample of heads."""
     c, inp, dev = full
     B, Hq, d, k = c["B"], c["Hq"], c["d"], c["k"]
@@ -193,3 +193,34 @@ def test_decode_graph_replay(full):
         aq.aqua_decode(cache, Hq, qbuf, mask, scale, ref, ws)
         torch.cuda.synchronize()
         assert torch.equal(got, ref), f"replay {it} (q' x {f}) differs from the eager call"
+
+
+@pytest.mark.parametrize("n", [2048, 4096])
+def test_short_lengths_large_batch(full, n):
+    """At B16 and up to 4096 tokens the short kernel's grid (256-token workgroups) would fill more
+    than two rounds of the device, so both forms run the split-T kernel there: the fused step over
+    n tokens (a cache of n - 1 plus the new one) and then the decode over the same n, every mask
+    bit-exact, sampled heads against the oracle."""
+    c, inp, dev = full
+    B, Hq, d, k = c["B"], c["Hq"], c["d"], c["k"]
+    cache, kp, v = _cache_with(c, dev, n - 1)
+    ws = torch.empty(aq.aqua_decode_workspace(cache, Hq), dtype=torch.uint8, device=DEV)
+    scale = 1 / math.sqrt(d)
+    out = torch.full((B, Hq, d), float("nan"), device=DEV)
+    qp = torch.full((B, Hq, d), float("nan"), device=DEV)
+    mask = torch.full((B, Hq, d // 32), -1, dtype=torch.int32, device=DEV)
+    aq.aqua_decode_step(cache, Hq, dev["q"], dev["k"][:, :, n - 1].contiguous(),
+                        dev["v"][:, :, n - 1].contiguous(), dev["P"], d, k, scale, out, ws,
+                        q_proj_out=qp, mask_out=mask)
+    torch.cuda.synchronize()
+    assert cache.len == n
+    m = _check_masks(mask, qp, d, k)
+    heads = [(0, 0), (3, 17), (7, 5), (9, 30), (15, 31)]
+    ref = oracle_decode(inp, c, m, length=n, heads=heads)
+    out2 = torch.full_like(out, float("nan"))
+    aq.aqua_decode(cache, Hq, qp.view(B * Hq, d), mask.view(B * Hq, d // 32), scale, out2, ws)
+    torch.cuda.synchronize()
+    for b, h in heads:
+        assert_close(out[b, h].cpu().double().numpy(), ref[b, h], "bf16", f"step, len {n}")
+        assert_close(out2[b, h].cpu().double().numpy(), ref[b, h], "bf16", f"decode, len {n}")
+    assert torch.isfinite(out).all() and torch.isfinite(out2).all()
