@@ -31,6 +31,14 @@ namespace {
 
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 
+// Waits until no vector memory operation of this wavefront is outstanding (vmcnt(0); the LDS and
+// export counters are left alone); memory accesses are not moved across it.
+__device__ __forceinline__ void wait_vmem() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  asm volatile("" ::: "memory");
+}
+
 // ------------------------------------------------------------------ 1. selection
 // q' = q P with the library's one bf16 projection (proj_mfma: v_mfma_f32_16x16x32_bf16 on P's
 // exact three-part bf16 split, fp32 accumulation; the q' of aqua_select_dims bit for bit).  A
@@ -67,6 +75,11 @@ __global__ __launch_bounds__(SEL_WAVES * 64) void prefill_select_kernel(
                     av[hf]);
   };
   if (blockIdx.x < nblk) load_rows(blockIdx.x);
+  // The rows of each block are waited for explicitly, before the previous block's stores are
+  // issued, so the projection needs no wait of its own: the counter of outstanding vector
+  // memory operations counts stores too, and a wait placed in the projection could not tell
+  // the rows from the stores issued after them.
+  wait_vmem();
   int buf = 0;
   for (int blk = blockIdx.x; blk < nblk; blk += gridDim.x, buf ^= 1) {
     const int r0 = blk * 32;
@@ -80,36 +93,63 @@ __global__ __launch_bounds__(SEL_WAVES * 64) void prefill_select_kernel(
     }
     if (blk + static_cast<int>(gridDim.x) < nblk) load_rows(blk + gridDim.x);
     lds_barrier();  // the next block's rows stay in flight through the selection
-    // ---- selection: wavefront w takes rows R w .. R w + R - 1 of the block
+    // ---- selection: wavefront w takes rows R w .. R w + R - 1 of the block; the masks and q'
+    // are held until the next block's rows have landed, then stored
     const int nrows = min(R, N - (r0 + R * w));  // uniform over the wavefront
-    for (int rr = 0; rr < nrows; ++rr) {
-      const int row = r0 + R * w + rr;
-      const float *tr = tile + (R * w + rr) * SQS;
-      const float x[2] = {tr[lane], tr[lane + 64]};
-      bool sel[2];
-      wave_topk_threshold<2>(x, d_sel, k, sel);
-      const uint64_t s0 = __ballot(sel[0]), s1 = __ballot(sel[1]);
-      if (lane < 4) {
-        const uint64_t bb = (lane >> 1) ? s1 : s0;
-        mask[static_cast<size_t>(row) * 4 + lane] =
-            (lane & 1) ? static_cast<uint32_t>(bb >> 32) : static_cast<uint32_t>(bb);
+    uint64_t sm[R][2];
+    float xq[R][2];
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) {
+      sm[rr][0] = sm[rr][1] = 0;
+      xq[rr][0] = xq[rr][1] = 0.0f;
+      if (rr < nrows) {
+        const float *tr = tile + (R * w + rr) * SQS;
+        const float x[2] = {tr[lane], tr[lane + 64]};
+        bool sel[2];
+        wave_topk_threshold<2>(x, d_sel, k, sel);
+        sm[rr][0] = __ballot(sel[0]);
+        sm[rr][1] = __ballot(sel[1]);
+        xq[rr][0] = x[0];
+        xq[rr][1] = x[1];
+        const uint32_t pair =
+            pack_bf16x2(sel[0] ? x[0] * qscale : 0.0f, sel[1] ? x[1] * qscale : 0.0f);
+        qrows[rr * 128 + lane] = static_cast<bf16_t>(pair & 0xffffu);
+        qrows[rr * 128 + lane + 64] = static_cast<bf16_t>(pair >> 16);
+      }
+    }
+    wait_vmem();  // the next block's rows: requested before the selection, landed by now
+    if (nrows > 0) {
+      const size_t row0 = static_cast<size_t>(r0 + R * w);
+      // masks of the wavefront's rows, contiguous: lane 4 rr + j holds word j of row rr
+      if (lane < 4 * nrows) {
+        const int j = lane & 3;
+        uint32_t word = 0;
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr) {
+          const uint32_t w0 = static_cast<uint32_t>(sm[rr][0]);
+          const uint32_t w1 = static_cast<uint32_t>(sm[rr][0] >> 32);
+          const uint32_t w2 = static_cast<uint32_t>(sm[rr][1]);
+          const uint32_t w3 = static_cast<uint32_t>(sm[rr][1] >> 32);
+          const uint32_t v = j == 0 ? w0 : (j == 1 ? w1 : (j == 2 ? w2 : w3));
+          word = (lane >> 2) == rr ? v : word;
+        }
+        __builtin_nontemporal_store(word, mask + row0 * 4 + lane);
       }
       if (q_proj) {
-        q_proj[static_cast<size_t>(row) * 128 + lane] = x[0];
-        q_proj[static_cast<size_t>(row) * 128 + lane + 64] = x[1];
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr)
+          if (rr < nrows) {
+            q_proj[(row0 + rr) * 128 + lane] = xq[rr][0];
+            q_proj[(row0 + rr) * 128 + lane + 64] = xq[rr][1];
+          }
       }
-      const uint32_t pair = pack_bf16x2(sel[0] ? x[0] * qscale : 0.0f, sel[1] ? x[1] * qscale : 0.0f);
-      qrows[rr * 128 + lane] = static_cast<bf16_t>(pair & 0xffffu);
-      qrows[rr * 128 + lane + 64] = static_cast<bf16_t>(pair >> 16);
-    }
-    // the wavefront's rows of qm are contiguous in HBM: 16-byte stores (LDS is in order within
-    // a wavefront, so the values written above are read back here)
-    if (nrows > 0) {
-      bf16_t *dst = qm + static_cast<size_t>(r0 + R * w) * 128;
+      // the wavefront's rows of qm are contiguous in HBM: 16-byte streaming stores (LDS is in
+      // order within a wavefront, so the values written above are read back here)
+      bf16_t *dst = qm + row0 * 128;
       const int c = lane;  // 16-byte chunk: row c / 16
       if (c < nrows * 16)
-        *reinterpret_cast<u32x4_t *>(dst + 8 * c) =
-            *reinterpret_cast<const u32x4_t *>(qrows + 8 * c);
+        __builtin_nontemporal_store(*reinterpret_cast<const u32x4_t *>(qrows + 8 * c),
+                                    reinterpret_cast<u32x4_t *>(dst + 8 * c));
     }
     // the next block writes the other tile; the barrier above it orders this block's reads
   }
