@@ -372,6 +372,14 @@ def run_us(fn, n: int) -> float:
     return e0.elapsed_time(e1) * 1e3 / n
 
 
+def run_us_spread(fn, rounds: int, n: int) -> dict:
+    """p10 / median / p90 over `rounds` rounds of run_us(fn, n) (microseconds per call; each round
+    is n calls back to back between two HIP events, so no marker packet sits between calls)."""
+    vals = [run_us(fn, n) for _ in range(rounds)]
+    return {"p10": float(np.percentile(vals, 10)), "median": float(np.median(vals)),
+            "p90": float(np.percentile(vals, 90)), "rounds": rounds, "calls_per_round": n}
+
+
 def bench_shard(dev, steps: int, warmup: int):
     """One GPU's share of the benchmark step under 8-way KV-head sharding (the usual 8-GPU layout
     of this model): B=16, 4 query heads, 1 KV head, T=8192 (capacity T + 256), k=96.  The whole
@@ -885,6 +893,7 @@ def main():
         res[path] = (ms, gpu_us)
     best = min(res, key=lambda p: res[p][0])
     ms_per_step, step_gpu_us = res[best]
+    spread = run_us_spread(lambda: step(best), 20, 25)
     # the decode kernel of the three-launch form alone, on the step's masks (for reference)
     cache.len = T
     decode_us = run_us(lambda: aq.aqua_decode(cache, Hq, qp, mask, scale, out, ws), args.steps)
@@ -911,6 +920,7 @@ def main():
                      "frac_of_measured_peak": achieved / probe["gbs"]},
         "kernel": kname,
         "step_gpu_us": step_gpu_us,
+        "step_gpu_us_spread": spread,
         "bytes_per_step": nbytes,
         "mean_union_rows": float(U.mean()),
         "ms_per_step_by_path": {p: res[p][0] for p in res},
@@ -921,7 +931,8 @@ def main():
         "stream_probe": probe,
         "timing": "value, ms_per_step: K bare steps between two synchronizations; step_gpu_us "
                   "(roofline.achieved): the same step's launches, K steps back to back on their "
-                  "stream between two HIP events; decode_kernel_us: aqua_decode alone on the "
+                  "stream between two HIP events (step_gpu_us_spread: p10 / median / p90 over "
+                  "20 rounds of 25 such steps); decode_kernel_us: aqua_decode alone on the "
                   "step's masks over the 8192 tokens, the same way (decode_kernel_frac: its own "
                   "algorithmic bytes over that time, against 8 TB/s)",
     }
