@@ -32,7 +32,9 @@ namespace {
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 
 // Waits until no vector memory operation of this wavefront is outstanding (vmcnt(0); the LDS and
-// export counters are left alone); memory accesses are not moved across it.
+// export counters are left alone); memory accesses are not moved across it.  s_waitcnt fields on
+// gfx9: vmcnt bits [3:0] and [15:14] (0 here), expcnt [6:4] (7: no wait), lgkmcnt [11:8] (15: no
+// wait).
 __device__ __forceinline__ void wait_vmem() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(0x0F70);
