@@ -258,35 +258,44 @@ __device__ __forceinline__ void h2o_keep_min(uint64_t &key, int &slot, uint64_t 
   }
 }
 
-__device__ __forceinline__ int h2o_pick_victim(const float *mass, const int32_t *pos, int n_slots,
-                                               int limit) {
+// The scan in parts, for callers that keep the slots' loads in flight behind other work:
+// h2o_victim_load requests one batch (thread tid's slots s0 + 256 i, s0 = base + tid),
+// h2o_victim_fold ranks it into the thread's (key, slot), h2o_victim_reduce takes the workgroup's
+// minimum.  One batch covers 256 * kVictimBatch slots.
+constexpr int kVictimBatch = 16;  // slots per thread whose loads are in flight together
+
+struct H2OVictimBatch {
+  float mv[kVictimBatch];
+  int pv[kVictimBatch];
+};
+
+__device__ __forceinline__ void h2o_victim_load(const float *mass, const int32_t *pos,
+                                                int n_slots, int s0, H2OVictimBatch &bt) {
+#pragma unroll
+  for (int i = 0; i < kVictimBatch; ++i) {  // unconditional loads (clamped), validity in the fold
+    const int s = min(s0 + 256 * i, n_slots - 1);
+    bt.pv[i] = pos[s];
+    bt.mv[i] = mass[s];
+  }
+}
+
+__device__ __forceinline__ void h2o_victim_fold(const H2OVictimBatch &bt, int n_slots, int s0,
+                                                int limit, uint64_t &key, int &slot) {
+#pragma unroll
+  for (int i = 0; i < kVictimBatch; ++i) {
+    const int pv = s0 + 256 * i < n_slots ? bt.pv[i] : -1;
+    if (pv >= 0 && pv <= limit)
+      h2o_keep_min(key, slot,
+                   (static_cast<uint64_t>(__float_as_uint(bt.mv[i])) << 32) |
+                       static_cast<uint32_t>(0x7fffffff - pv),
+                   s0 + 256 * i);
+  }
+}
+
+__device__ __forceinline__ int h2o_victim_reduce(uint64_t key, int slot) {
   __shared__ uint64_t s_key[4];
   __shared__ int s_slot[4];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  uint64_t key = ~0ull;
-  int slot = 0x7fffffff;
-  constexpr int BATCH = 16;  // slots per thread whose loads are in flight together
-  for (int s0 = tid; s0 < n_slots; s0 += 256 * BATCH) {
-    float mv[BATCH];
-    int pv[BATCH];
-#pragma unroll
-    for (int i = 0; i < BATCH; ++i) {  // unconditional loads (clamped), validity applied below
-      const int s = min(s0 + 256 * i, n_slots - 1);
-      pv[i] = pos[s];
-      mv[i] = mass[s];
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = 0; i < BATCH; ++i)
-      if (s0 + 256 * i >= n_slots) pv[i] = -1;
-#pragma unroll
-    for (int i = 0; i < BATCH; ++i)
-      if (pv[i] >= 0 && pv[i] <= limit)
-        h2o_keep_min(key, slot,
-                     (static_cast<uint64_t>(__float_as_uint(mv[i])) << 32) |
-                         static_cast<uint32_t>(0x7fffffff - pv[i]),
-                     s0 + 256 * i);
-  }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
     const uint64_t k2 = __shfl_xor(key, off, 64);
@@ -302,6 +311,19 @@ __device__ __forceinline__ int h2o_pick_victim(const float *mass, const int32_t 
   slot = s_slot[0];
   for (int x = 1; x < 4; ++x) h2o_keep_min(key, slot, s_key[x], s_slot[x]);
   return key == ~0ull ? -1 : slot;
+}
+
+__device__ __forceinline__ int h2o_pick_victim(const float *mass, const int32_t *pos, int n_slots,
+                                               int limit) {
+  uint64_t key = ~0ull;
+  int slot = 0x7fffffff;
+  for (int s0 = threadIdx.x; s0 < n_slots; s0 += 256 * kVictimBatch) {
+    H2OVictimBatch bt;
+    h2o_victim_load(mass, pos, n_slots, s0, bt);
+    __builtin_amdgcn_sched_barrier(0);
+    h2o_victim_fold(bt, n_slots, s0, limit, key, slot);
+  }
+  return h2o_victim_reduce(key, slot);
 }
 
 // ------------------------------------------------------------------ launch parameter blocks

@@ -1134,25 +1134,35 @@ __device__ __forceinline__ void short_attend(const DecodeArgs &a, const H2OArgs 
   }
 
   int victim = -1;  // the column the new token goes to
-  if constexpr (H2O) {
-    victim = h2o_pick_victim(a.mass + slot0, hh.slot_pos + slot0, a.len, hh.t_new - hh.recent);
-    if (split == 0 && tid == 0) hh.victim[bg] = victim;
-  } else if constexpr (FUSED) {
-    victim = a.len - 1;
-  }
-  const bool owner = FUSED && victim >= t0 && victim < t0 + kShortChunk;  // false if victim is -1
+  if constexpr (FUSED && !H2O) victim = a.len - 1;
+  // H2O: the slots' masses and positions are requested here, and ranked only after the
+  // prologue, so their round trip overlaps the prologue's; every workgroup keeps the new token's
+  // K' and V in LDS meanwhile (the key is projected in every workgroup anyway; the victim's
+  // owner uses them).  The compact cache fits one batch of the scan.
+  static_assert(kDecodeShortMax <= 256 * kVictimBatch, "one batch of the victim scan");
+  H2OVictimBatch vb;
+  if constexpr (H2O) h2o_victim_load(a.mass + slot0, hh.slot_pos + slot0, a.len, tid, vb);
+  const bool keep_new = H2O || (FUSED && victim >= t0 && victim < t0 + kShortChunk);
   if constexpr (FUSED) {
     auto issue = [&] {
       load_k();
       load_v();
     };
     if constexpr (sizeof(KT) == 2)  // K' at the start, V after the projection (see decode_kernel)
-      fused_project_select_mfma<D, G, NT, true>(a, head0, bg, owner, split == 0, s_qp, s_mw,
+      fused_project_select_mfma<D, G, NT, true>(a, head0, bg, keep_new, split == 0, s_qp, s_mw,
                                                 s_knew, s_vnew, load_k, load_v);
     else
-      fused_project_select<KT, D, G, NT>(a, head0, bg, owner, split == 0, sP, sq, s_qp, s_mw,
+      fused_project_select<KT, D, G, NT>(a, head0, bg, keep_new, split == 0, sP, sq, s_qp, s_mw,
                                          s_knew, s_vnew, issue);
   }
+  if constexpr (H2O) {
+    uint64_t key = ~0ull;
+    int slot = 0x7fffffff;
+    h2o_victim_fold(vb, a.len, tid, hh.t_new - hh.recent, key, slot);
+    victim = h2o_victim_reduce(key, slot);
+    if (split == 0 && tid == 0) hh.victim[bg] = victim;
+  }
+  const bool owner = FUSED && victim >= t0 && victim < t0 + kShortChunk;  // false if victim is -1
 
   // ---- every stored dim's weight per head: q'_i * scale * log2 e where the head selected it
   if (tid < a.d_store) {

@@ -89,6 +89,8 @@ def _check(inp, c, out, qp, mask, rows, d_sel, k, d_store=None):
     (8, 2, 1024, 512, 96),    # two chunks of 16 blocks
     (16, 2, 640, 128, 64),    # G = 8, five chunks of 4 blocks
     (8, 2, 512, [32, 128, 256, 96], 96),  # paired chunks starting at 32 and 160
+    (1, 1, 77, 77, 96),       # 154 query rows: the last 32-row selection block holds 26, so one
+                              # wavefront of the selection has 2 rows and one has none
 ])
 def test_prefill_small_all_rows(Hq, Hkv, T, chunk, k):
     c = config(4, B=2, Hq=Hq, Hkv=Hkv, T=T, k=k)
