@@ -895,7 +895,7 @@ def main():
         res[path] = (ms, gpu_us)
     best = min(res, key=lambda p: res[p][0])
     ms_per_step, step_gpu_us = res[best]
-    spread = run_us_spread(lambda: step(best), 20, 25)
+    spread = run_us_spread(lambda: step(best), 20, 100)
     # the decode kernel of the three-launch form alone, on the step's masks (for reference)
     cache.len = T
     decode_us = run_us(lambda: aq.aqua_decode(cache, Hq, qp, mask, scale, out, ws), args.steps)
@@ -935,7 +935,7 @@ def main():
                   "per timed region, amortised over K); step_gpu_us "
                   "(roofline.achieved): the same step's launches, K steps back to back on their "
                   "stream between two HIP events (step_gpu_us_spread: p10 / median / p90 over "
-                  "20 rounds of 25 such steps); decode_kernel_us: aqua_decode alone on the "
+                  "20 rounds of 100 such steps); decode_kernel_us: aqua_decode alone on the "
                   "step's masks over the 8192 tokens, the same way (decode_kernel_frac: its own "
                   "algorithmic bytes over that time, against 8 TB/s)",
     }
