@@ -844,11 +844,18 @@ def main():
     v = torch.empty(B, Hkv, T_cap, d, dtype=torch.bfloat16, device=dev)
     cache = aq.make_cache(kp, v, 0)
     k_all, v_all = inp["k"].to(dev), inp["v"].to(dev)
-    aq.aqua_project_keys(cache, k_all[:, :, :T - 1].contiguous(), v_all[:, :, :T - 1].contiguous(),
-                         P, T - 1)
+    k_fill, v_fill = k_all[:, :, :T - 1].contiguous(), v_all[:, :, :T - 1].contiguous()
+
+    def fill():  # the cache fill: T - 1 tokens of every (b, KV head) projected and appended
+        cache.len = 0
+        aq.aqua_project_keys(cache, k_fill, v_fill, P, T - 1)
+
+    fill()
+    fill_us = run_us(fill, 5)  # the same bits rewritten each time
+    fill_bytes = 4 * B * Hkv * (T - 1) * d * 2  # K and V read, K' (d_store = d) and V written
     k_new = k_all[:, :, T - 1].contiguous()
     v_new = v_all[:, :, T - 1].contiguous()
-    del k_all, v_all
+    del k_all, v_all, k_fill, v_fill
     q = inp["q"].to(dev)
     qp = torch.empty(B * Hq, d, device=dev)
     mask = torch.empty(B * Hq, d // 32, dtype=torch.int32, device=dev)
@@ -931,6 +938,12 @@ def main():
         "decode_kernel_bytes": dbytes,
         "decode_kernel_frac": dbytes / (decode_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
         "stream_probe": probe,
+        "cache_fill": {"tokens": T - 1, "groups": B * Hkv, "us": fill_us, "bytes": fill_bytes,
+                       "gbs": fill_bytes / (fill_us * 1e-6) / 1e9,
+                       "frac_hbm_peak": fill_bytes / (fill_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                       "timing": "aqua_project_keys of the whole cache (bulk append), 5 calls "
+                                 "back to back between two HIP events; bytes: K and V read, K' "
+                                 "and V written"},
         "timing": "value, ms_per_step: K bare steps between two synchronizations (a fixed ~0.7 ms "
                   "per timed region, amortised over K); step_gpu_us "
                   "(roofline.achieved): the same step's launches, K steps back to back on their "
