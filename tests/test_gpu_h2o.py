@@ -239,3 +239,68 @@ def test_h2o_fused_step_equals_separate_calls(over):
                            ("slot_pos", st.slot_pos, st2.slot_pos), ("mass", st.mass, st2.mass),
                            ("K'", st.kp, st2.kp), ("V", st.v, st2.v)):
             assert torch.equal(x, y), f"step {s}: {name} differs"
+
+
+@pytest.mark.parametrize("fused", [True, False])
+def test_h2o_steps_graph_replay(fused):
+    """H2O steps captured in a HIP graph and replayed from a restored starting state give the bits
+    of the same steps run eagerly: every replay runs with the epochs taken at capture, and the
+    library needs no clearing between replays.  Eager steps on the same workspace (other epochs
+    in its counters) run between the replays.  The compact cache holds 128 slots, so every
+    attention launch is the short-context kernel (one launch per step, or the four calls)."""
+    c = config(5, Hq=16, Hkv=2, T=700, heavy=96, recent=32, steps=12)
+    inp = make_h2o_inputs(c)
+    B, Hq, d, T, S = c["B"], c["Hq"], c["d"], c["T"], c["steps"]
+    st, _, _, _, P, _ = _seed(inp, c)
+    st.workspace(Hq)
+    scale = 1 / math.sqrt(d)
+    qs, ks, vs = (inp[x].to(DEV) for x in ("q_steps", "k_steps", "v_steps"))
+    out = torch.empty(B, Hq, d, device=DEV)
+    qp = torch.empty(B, Hq, d, device=DEV)
+    mask = torch.empty(B, Hq, d // 32, dtype=torch.int32, device=DEV)
+    state = (st.kp, st.v, st.slot_pos, st.mass)
+    start = [t.clone() for t in state]
+
+    def restore():
+        for dst, src in zip(state, start):
+            dst.copy_(src)
+        for t in (out, qp):
+            t.fill_(float("nan"))
+        mask.fill_(-1)
+        st.victim.fill_(-7)
+
+    def steps():
+        for s in range(S):
+            st.step(qs[s], ks[s], vs[s], P, T + s, c["d_sel"], c["k"], scale, out, qp, mask,
+                    fused=fused)
+
+    def snapshot():
+        return [t.clone() for t in (out, qp, mask, st.victim, *state)]
+
+    restore()
+    steps()
+    torch.cuda.synchronize()
+    ref = snapshot()
+    assert all(torch.isfinite(t).all() for t in (ref[0], ref[1]))
+
+    restore()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    s_cap = torch.cuda.Stream()
+    with torch.cuda.stream(s_cap):
+        with torch.cuda.graph(graph, stream=s_cap):
+            steps()
+    torch.cuda.synchronize()
+    names = ("out", "q_proj", "mask", "victim", "K'", "V", "slot_pos", "mass")
+    for it in range(3):
+        restore()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, got, want in zip(names, snapshot(), ref):
+            assert torch.equal(got, want), f"replay {it}: {name} differs from the eager steps"
+        restore()
+        steps()
+        torch.cuda.synchronize()
+        for name, got, want in zip(names, snapshot(), ref):
+            assert torch.equal(got, want), f"eager run after replay {it}: {name} differs"
