@@ -166,3 +166,72 @@ def test_step_long_context_sampled(k):
     got = r["out"].cpu().double().numpy()
     for b, h in heads:
         assert_close(got[b, h], ref[b, h], "bf16", f"k={k} head {h}")
+
+
+def test_short_steps_graph_replay():
+    """Six aqua_decode_step calls at short lengths (the short-context kernel: 1500 tokens and up,
+    24 workgroups), then an aqua_decode over the result, captured in one HIP graph: three replays
+    from a restored cache give the bits of the same calls run eagerly, with the eager calls on the
+    same workspace (other epochs in its counters) run between the replays."""
+    c = config(2, B=2, Hq=8, Hkv=2, T=1506)
+    inp = make_decode_inputs(c)
+    B, Hq, Hkv, d, k = c["B"], c["Hq"], c["Hkv"], c["d"], c["k"]
+    T0, n = 1500, 6
+    kp, v = new_cache(B, Hkv, d, d, (T0 + n + 63) // 64 * 64, "bf16")
+    cache = aq.make_cache(kp, v, 0)
+    P = inp["P"].to(DEV)
+    aq.aqua_project_keys(cache, inp["k"][:, :, :T0].contiguous().to(DEV),
+                         inp["v"][:, :, :T0].contiguous().to(DEV), P, T0)
+    ws = torch.empty(aq.aqua_decode_workspace(cache, Hq), dtype=torch.uint8, device=DEV)
+    q = inp["q"].to(DEV)
+    kn = [inp["k"][:, :, t].contiguous().to(DEV) for t in range(T0, T0 + n)]
+    vn = [inp["v"][:, :, t].contiguous().to(DEV) for t in range(T0, T0 + n)]
+    outs = [torch.empty(B, Hq, d, device=DEV) for _ in range(n + 1)]
+    qp = torch.empty(B, Hq, d, device=DEV)
+    mask = torch.empty(B, Hq, d // 32, dtype=torch.int32, device=DEV)
+    scale = 1 / math.sqrt(d)
+    start = (kp.clone(), v.clone())
+
+    def restore():
+        kp.copy_(start[0])
+        v.copy_(start[1])
+        for o in outs:
+            o.fill_(float("nan"))
+        cache.len = T0
+
+    def calls():
+        for i in range(n):
+            aq.aqua_decode_step(cache, Hq, q, kn[i], vn[i], P, d, k, scale, outs[i], ws,
+                                q_proj_out=qp, mask_out=mask)
+        aq.aqua_decode(cache, Hq, qp, mask, scale, outs[n], ws)
+
+    def snapshot():  # bit patterns: the cache's unwritten columns hold NaN
+        ts = [o for o in outs] + [qp, mask, kp, v]
+        return [t.view(torch.int16 if t.element_size() == 2 else torch.int32).clone() for t in ts]
+
+    restore()
+    calls()
+    torch.cuda.synchronize()
+    ref = snapshot()
+    assert all(torch.isfinite(o).all() for o in outs)
+
+    restore()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    s_cap = torch.cuda.Stream()
+    with torch.cuda.stream(s_cap):
+        with torch.cuda.graph(graph, stream=s_cap):
+            calls()
+    torch.cuda.synchronize()
+    for it in range(3):
+        restore()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for j, (got, want) in enumerate(zip(snapshot(), ref)):
+            assert torch.equal(got, want), f"replay {it}: tensor {j} differs from the eager calls"
+        restore()
+        calls()
+        torch.cuda.synchronize()
+        for j, (got, want) in enumerate(zip(snapshot(), ref)):
+            assert torch.equal(got, want), f"eager calls after replay {it}: tensor {j} differs"
