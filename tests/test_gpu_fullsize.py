@@ -224,3 +224,36 @@ def test_short_lengths_large_batch(full, n):
         assert_close(out[b, h].cpu().double().numpy(), ref[b, h], "bf16", f"step, len {n}")
         assert_close(out2[b, h].cpu().double().numpy(), ref[b, h], "bf16", f"decode, len {n}")
     assert torch.isfinite(out).all() and torch.isfinite(out2).all()
+
+
+@pytest.mark.parametrize("T", [4097, 8193, 16384])
+def test_step_b16_layouts(T):
+    """The fused step at batch 16 (128 groups) where the layout rule picks other grids than the
+    benchmark's: 4097 tokens (no full 8-wavefront split per group: the 4-wavefront layout, 3
+    splits of 2048), 8193 (the 8-wavefront grid would end on a half round: 4-wavefront, 5 splits)
+    and 16384 (8-wavefront, 4 splits of 4096 filling two whole rounds).  Every mask against the
+    oracle's selection of the GPU's q', the output on a sample of heads in every group."""
+    c = config(2, T=T)
+    inp = make_decode_inputs(c, workers=16)
+    B, Hq, Hkv, d, k = c["B"], c["Hq"], c["Hkv"], c["d"], c["k"]
+    T_cap = T + 256 - T % 64
+    kp, v = new_cache(B, Hkv, d, d, T_cap, "bf16")
+    cache = aq.make_cache(kp, v, 0)
+    P = inp["P"].to(DEV)
+    aq.aqua_project_keys(cache, inp["k"][:, :, :T - 1].contiguous().to(DEV),
+                         inp["v"][:, :, :T - 1].contiguous().to(DEV), P, T - 1)
+    ws = torch.empty(aq.aqua_decode_workspace(cache, Hq), dtype=torch.uint8, device=DEV)
+    out = torch.full((B, Hq, d), float("nan"), device=DEV)
+    qp = torch.full((B, Hq, d), float("nan"), device=DEV)
+    mask = torch.full((B, Hq, d // 32), -1, dtype=torch.int32, device=DEV)
+    aq.aqua_decode_step(cache, Hq, inp["q"].to(DEV), inp["k"][:, :, T - 1].contiguous().to(DEV),
+                        inp["v"][:, :, T - 1].contiguous().to(DEV), P, d, k, 1 / math.sqrt(d),
+                        out, ws, q_proj_out=qp, mask_out=mask)
+    torch.cuda.synchronize()
+    assert cache.len == T
+    m = _check_masks(mask.view(B * Hq, d // 32), qp.view(B * Hq, d), d, k).reshape(B, Hq, d)
+    heads = [(b, 4 * g + (b + g) % 4) for b in range(B) for g in range(Hkv)]  # one per group
+    ref = oracle_decode(inp, c, m, heads=heads)
+    got = out.cpu().double().numpy()
+    for b, h in heads:
+        assert_close(got[b, h], ref[b, h], "bf16", f"T {T}, batch {b}, head {h}")
