@@ -345,6 +345,8 @@ struct DecodeArgs {
   float *scores;         // [B][Hq][T_cap]   log2-domain scores (mass mode only)
   int B, Hq, Hkv, d, d_store, T_cap, len;
   int S;                 // splits per (b, g)
+  int tail_last;         // split-T grid order: 1 deals every group's last split after all the
+                         // others (see decode_kernel), 0 the (split, KV head, batch) order
   float qscale;          // scale * log2(e)
   // fused decode step only: raw queries and the new token, selection parameters
   const void *q_raw;     // [B][Hq][d]

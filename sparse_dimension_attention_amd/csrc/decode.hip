@@ -122,8 +122,15 @@ void decode_workspace_carve(void *ws, int dtype, int B, int Hq, int Hkv, int d, 
 }
 
 namespace {
-hipError_t launch_split(int dtype, const DecodeArgs &a, bool fused, hipStream_t s) {
-  const DecodeLayout L = decode_layout(dtype, a.Hq / a.Hkv, a.B * a.Hkv, a.len, device_cu_count());
+hipError_t launch_split(int dtype, const DecodeArgs &a0, bool fused, hipStream_t s) {
+  const int cus = device_cu_count();
+  const DecodeLayout L = decode_layout(dtype, a0.Hq / a0.Hkv, a0.B * a0.Hkv, a0.len, cus);
+  // Two waves per SIMD stay resident: 8 / waves workgroups per CU.  The ragged last split of
+  // each group is dealt last where the grid takes more than one round (decode_kernel).
+  DecodeArgs a = a0;
+  const long slots = static_cast<long>(cus) * (8 / L.waves);
+  a.tail_last = (a.S >= 2 && a.len % L.split != 0 &&
+                 static_cast<long>(a.S) * a.B * a.Hkv > slots) ? 1 : 0;
   if (dtype == 1) return fused ? launch_split_step_bf16(a, L, s) : launch_split_bf16(a, L, s);
   return launch_split_f32(a, L, fused, s);
 }

@@ -572,12 +572,27 @@ void decode_kernel(DecodeArgs a) {
   // the reads go out one dependent round trip at a time, ~1 us each before the first HBM load.
   asm volatile("" ::"s"(a.kp), "s"(a.v), "s"(a.q_proj), "s"(a.mask), "s"(a.q_raw), "s"(a.k_new),
                "s"(a.P), "s"(a.partials), "s"(a.Hq), "s"(a.Hkv), "s"(a.d_store), "s"(a.T_cap),
-               "s"(a.len), "s"(a.S), "s"(a.qscale), "s"(a.d_sel), "s"(a.k));
+               "s"(a.len), "s"(a.S), "s"(a.qscale), "s"(a.d_sel), "s"(a.k), "s"(a.B),
+               "s"(a.tail_last));
   // Grid (split, KV head, batch): the linear workgroup index (the one the dispatcher deals to
-  // the XCDs in turn) is split + S (g + Hkv b).
+  // the XCDs in turn) is split + S (g + Hkv b).  With tail_last (set where the grid takes more
+  // than one round of resident workgroups and the last split of each group is partial) that
+  // index is dealt differently: first the S - 1 full splits of every group, group by group,
+  // then every group's last split, so that the first round runs full splits only and the
+  // short ones follow, instead of holding slots while full splits wait for the next round.
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int bg = b * a.Hkv + g;
+  int split = blockIdx.x, bg = blockIdx.z * a.Hkv + blockIdx.y;
+  if (a.tail_last) {
+    const int lin = bg * a.S + split, nfull = (a.S - 1) * a.B * a.Hkv;
+    if (lin < nfull) {
+      bg = lin / (a.S - 1);
+      split = lin - bg * (a.S - 1);
+    } else {
+      bg = lin - nfull;
+      split = a.S - 1;
+    }
+  }
+  const int b = bg / a.Hkv, g = bg - b * a.Hkv;
   const int wg_lin = bg * a.S + split;
   const size_t head0 = static_cast<size_t>(b) * a.Hq + static_cast<size_t>(g) * G;
   // Fused: the cache holds len - 1 tokens, the new one is position len - 1.

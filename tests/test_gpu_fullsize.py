@@ -231,8 +231,11 @@ def test_step_b16_layouts(T):
     """The fused step at batch 16 (128 groups) where the layout rule picks other grids than the
     benchmark's: 4097 tokens (no full 8-wavefront split per group: the 4-wavefront layout, 3
     splits of 2048), 8193 (the 8-wavefront grid would end on a half round: 4-wavefront, 5 splits)
-    and 16384 (8-wavefront, 4 splits of 4096 filling two whole rounds).  Every mask against the
-    oracle's selection of the GPU's q', the output on a sample of heads in every group."""
+    and 16384 (8-wavefront, 4 splits of 4096 filling two whole rounds).  At 8193 the grid (640
+    workgroups) takes more than one round of resident workgroups, so every group's one-token last
+    split is dealt after all the full ones.  Every mask against the oracle's selection of the
+    GPU's q'; the output of the step, and of aqua_decode over the same tokens, on a sample of heads
+    in every group."""
     c = config(2, T=T)
     inp = make_decode_inputs(c, workers=16)
     B, Hq, Hkv, d, k = c["B"], c["Hq"], c["Hkv"], c["d"], c["k"]
@@ -254,6 +257,11 @@ def test_step_b16_layouts(T):
     m = _check_masks(mask.view(B * Hq, d // 32), qp.view(B * Hq, d), d, k).reshape(B, Hq, d)
     heads = [(b, 4 * g + (b + g) % 4) for b in range(B) for g in range(Hkv)]  # one per group
     ref = oracle_decode(inp, c, m, heads=heads)
-    got = out.cpu().double().numpy()
-    for b, h in heads:
-        assert_close(got[b, h], ref[b, h], "bf16", f"T {T}, batch {b}, head {h}")
+    # aqua_decode over the same T tokens with the step's q' and masks: the plain kernel's grid
+    out2 = torch.full((B, Hq, d), float("nan"), device=DEV)
+    aq.aqua_decode(cache, Hq, qp, mask, 1 / math.sqrt(d), out2, ws)
+    torch.cuda.synchronize()
+    for name, o in (("aqua_decode_step", out), ("aqua_decode", out2)):
+        got = o.cpu().double().numpy()
+        for b, h in heads:
+            assert_close(got[b, h], ref[b, h], "bf16", f"{name}, T {T}, batch {b}, head {h}")
