@@ -265,3 +265,31 @@ def test_step_b16_layouts(T):
         got = o.cpu().double().numpy()
         for b, h in heads:
             assert_close(got[b, h], ref[b, h], "bf16", f"{name}, T {T}, batch {b}, head {h}")
+
+
+def test_step_one_kv_head_shard():
+    """The benchmark layer's share on one GPU of eight when KV heads are sharded (B16, Hq4,
+    Hkv1, T8192): 16 groups of 4 splits of 2048 tokens, 64 four-wavefront workgroups.  Every mask
+    and every head against the oracle; aqua_decode over the same tokens too."""
+    c = config(2, Hq=4, Hkv=1, T=8192)
+    inp = make_decode_inputs(c, workers=16)
+    B, Hq, Hkv, d, k, T = c["B"], c["Hq"], c["Hkv"], c["d"], c["k"], c["T"]
+    kp, v = new_cache(B, Hkv, d, d, T_CAP, "bf16")
+    cache = aq.make_cache(kp, v, 0)
+    P = inp["P"].to(DEV)
+    aq.aqua_project_keys(cache, inp["k"][:, :, :T - 1].contiguous().to(DEV),
+                         inp["v"][:, :, :T - 1].contiguous().to(DEV), P, T - 1)
+    ws = torch.empty(aq.aqua_decode_workspace(cache, Hq), dtype=torch.uint8, device=DEV)
+    out = torch.full((B, Hq, d), float("nan"), device=DEV)
+    qp = torch.full((B, Hq, d), float("nan"), device=DEV)
+    mask = torch.full((B, Hq, d // 32), -1, dtype=torch.int32, device=DEV)
+    aq.aqua_decode_step(cache, Hq, inp["q"].to(DEV), inp["k"][:, :, T - 1].contiguous().to(DEV),
+                        inp["v"][:, :, T - 1].contiguous().to(DEV), P, d, k, 1 / math.sqrt(d),
+                        out, ws, q_proj_out=qp, mask_out=mask)
+    out2 = torch.full((B, Hq, d), float("nan"), device=DEV)
+    aq.aqua_decode(cache, Hq, qp, mask, 1 / math.sqrt(d), out2, ws)
+    torch.cuda.synchronize()
+    m = _check_masks(mask.view(B * Hq, d // 32), qp.view(B * Hq, d), d, k).reshape(B, Hq, d)
+    ref = oracle_decode(inp, c, m)
+    assert_close(out.cpu().double().numpy(), ref, "bf16", "shard step, all heads")
+    assert_close(out2.cpu().double().numpy(), ref, "bf16", "shard decode, all heads")
