@@ -293,3 +293,37 @@ def test_step_one_kv_head_shard():
     ref = oracle_decode(inp, c, m)
     assert_close(out.cpu().double().numpy(), ref, "bf16", "shard step, all heads")
     assert_close(out2.cpu().double().numpy(), ref, "bf16", "shard decode, all heads")
+
+
+def test_step_tail_last_two_level():
+    """Batch 4 at 40000 tokens: 32 groups of 20 splits of 2048 (640 four-wavefront workgroups, the
+    last split of each group partial), so the grid takes more than one round and the groups' last
+    splits are dealt after all the full ones, with the merge in two levels (runs of 8 splits).
+    Every mask, and two heads of every group for the fused step and aqua_decode, against the
+    oracle."""
+    c = config(2, B=4, T=40000)
+    inp = make_decode_inputs(c, workers=16)
+    B, Hq, Hkv, d, k, T = c["B"], c["Hq"], c["Hkv"], c["d"], c["k"], c["T"]
+    T_cap = T + 256 - T % 64
+    kp, v = new_cache(B, Hkv, d, d, T_cap, "bf16")
+    cache = aq.make_cache(kp, v, 0)
+    P = inp["P"].to(DEV)
+    aq.aqua_project_keys(cache, inp["k"][:, :, :T - 1].contiguous().to(DEV),
+                         inp["v"][:, :, :T - 1].contiguous().to(DEV), P, T - 1)
+    ws = torch.empty(aq.aqua_decode_workspace(cache, Hq), dtype=torch.uint8, device=DEV)
+    out = torch.full((B, Hq, d), float("nan"), device=DEV)
+    qp = torch.full((B, Hq, d), float("nan"), device=DEV)
+    mask = torch.full((B, Hq, d // 32), -1, dtype=torch.int32, device=DEV)
+    aq.aqua_decode_step(cache, Hq, inp["q"].to(DEV), inp["k"][:, :, T - 1].contiguous().to(DEV),
+                        inp["v"][:, :, T - 1].contiguous().to(DEV), P, d, k, 1 / math.sqrt(d),
+                        out, ws, q_proj_out=qp, mask_out=mask)
+    out2 = torch.full((B, Hq, d), float("nan"), device=DEV)
+    aq.aqua_decode(cache, Hq, qp, mask, 1 / math.sqrt(d), out2, ws)
+    torch.cuda.synchronize()
+    m = _check_masks(mask.view(B * Hq, d // 32), qp.view(B * Hq, d), d, k).reshape(B, Hq, d)
+    heads = [(b, 4 * g + j) for b in range(B) for g in range(Hkv) for j in ((b + g) % 4, 3 - (b + g) % 4)]
+    ref = oracle_decode(inp, c, m, heads=heads)
+    for name, o in (("aqua_decode_step", out), ("aqua_decode", out2)):
+        got = o.cpu().double().numpy()
+        for b, h in heads:
+            assert_close(got[b, h], ref[b, h], "bf16", f"{name}, batch {b}, head {h}")
