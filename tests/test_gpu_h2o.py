@@ -150,6 +150,43 @@ def test_h2o_small_bf16_g8():
     _run(c)
 
 
+def _draw_h2o_shapes(n, seed=20261206):
+    """H2O shapes from a fixed seed: batch 1-2, 1-3 KV heads, G = 1/2/4/8, d 64 or 128, any
+    d_store, d_sel and k below it, bf16 or fp32, a compact cache of 64-1024 slots split into a
+    heavy part and a recent window (both non-empty), contexts from the slot count up to 9000
+    tokens (so the seeding decode runs on either decode kernel), 4-12 steps."""
+    rng = np.random.default_rng(seed)
+    shapes = []
+    for _ in range(n):
+        d = int(rng.choice([64, 128]))
+        G = int(rng.choice([1, 2, 4, 8]))
+        Hkv = int(rng.integers(1, 4))
+        d_store = d if rng.random() < 0.33 else int(rng.integers(1, d + 1))
+        d_sel = d_store if rng.random() < 0.5 else int(rng.integers(1, d_store + 1))
+        n_slots = 64 * int(rng.integers(1, 17))
+        recent = int(rng.integers(1, n_slots))
+        shapes.append(dict(B=int(rng.integers(1, 3)), Hq=G * Hkv, Hkv=Hkv, d=d, d_store=d_store,
+                           d_sel=d_sel, k=int(rng.integers(1, d_sel + 1)),
+                           T=int(rng.integers(n_slots, 9001)), heavy=n_slots - recent,
+                           recent=recent, steps=int(rng.integers(4, 13)),
+                           dtype="bf16" if rng.random() < 0.6 else "f32"))
+    return shapes
+
+
+H2O_SHAPES = _draw_h2o_shapes(8)
+
+
+@pytest.mark.parametrize("fused", [True, False])
+@pytest.mark.parametrize("over", H2O_SHAPES, ids=[
+    f"{o['dtype']}-B{o['B']}-Hq{o['Hq']}-Hkv{o['Hkv']}-d{o['d']}-ds{o['d_store']}-dsel{o['d_sel']}"
+    f"-k{o['k']}-T{o['T']}-h{o['heavy']}-r{o['recent']}-s{o['steps']}" for o in H2O_SHAPES])
+def test_h2o_shape_sweep(over, fused):
+    """Drawn shapes through the whole H2O sequence (seeding decode in mass mode, aqua_h2o_init,
+    then the steps as four calls or as the one launch), checked against the oracle at every step
+    as in the workload test above."""
+    _run(config(5, **over), fused=fused)
+
+
 @pytest.mark.parametrize("fused", [False, True])
 def test_h2o_llama8b_t32768_64_steps(fused):
     """The heavy-hitter workload: 32768-token context, 1024 heavy + 256 recent slots, AQUA-Memory
