@@ -807,8 +807,8 @@ def main():
     ap.add_argument("--secondary-reps", type=int, default=5)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the AQUA decode path here runs on a single MI355X "
-              "(--gpus 1); multi-GPU runs are not part of this build.", file=sys.stderr)
+        print("bench.py measures one GPU: the AQUA decode path runs on a single MI355X "
+              "(--gpus 1); runs over several GPUs are not supported.", file=sys.stderr)
         sys.exit(2)
     if not os.path.exists(aq.LIB_PATH):
         import __graft_entry__
