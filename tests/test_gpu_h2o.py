@@ -150,6 +150,16 @@ def test_h2o_small_bf16_g8():
     _run(c)
 
 
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_h2o_step_instances(dtype, d, G):
+    """The one-launch step in every compiled form (storage dtype x d x G): 128 slots (96 heavy,
+    32 recent) over a 400-token context, 3 steps, every step against the oracle."""
+    _run(config(5, B=1, Hq=2 * G, Hkv=2, d=d, d_store=d, d_sel=d, k=3 * d // 4, T=400,
+                heavy=96, recent=32, steps=3, dtype=dtype), fused=True)
+
+
 def _draw_h2o_shapes(n, seed=20261206):
     """H2O shapes from a fixed seed: batch 1-2, 1-3 KV heads, G = 1/2/4/8, d 64 or 128, any
     d_store, d_sel and k below it, bf16 or fp32, a compact cache of 64-1024 slots split into a
