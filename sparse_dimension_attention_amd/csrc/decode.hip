@@ -34,8 +34,10 @@ uint32_t next_epoch() {
   return e;
 }
 
-// Workgroups of 4 wavefronts (2 for G = 8, whose LDS numerators are twice as large per
-// wavefront), each wavefront owning 64 lanes x 16 bytes of tokens.  For G = 4, 8 wavefronts per
+// Workgroups of 4 wavefronts, each wavefront owning 64 lanes x 16 bytes of tokens (for G = 8,
+// whose LDS numerators are twice as large per wavefront, 2-wavefront workgroups ran the 16 x
+// 8-group, 8192-token fused step in 154 us against 103 with 4: LDS held only three of them per
+// CU).  For G = 4 and G = 8, 8 wavefronts per
 // workgroup when the full 8-wavefront splits alone give every CU a workgroup: one 512-thread
 // workgroup per CU, whose wavefronts are all of one age (with two 4-wavefront workgroups per CU
 // the second one resident ran ~4 us behind the first; 8 measured 1 us faster on the 16 x 8-group,
@@ -51,8 +53,8 @@ uint32_t next_epoch() {
 DecodeLayout decode_layout(int dtype, int G, int groups, int len, int cus) {
   DecodeLayout L;
   L.tokens_wave = 64 * (dtype == 1 ? 8 : 4);
-  L.waves = G == 8 ? 2 : 4;
-  if (G == 4 && groups > 0) {
+  L.waves = 4;
+  if ((G == 4 || G == 8) && groups > 0) {
     const long wide = 8L * L.tokens_wave;
     const long full_wide = static_cast<long>(len) / wide;
     const long wgs = static_cast<long>(groups) * ((len + wide - 1) / wide);

@@ -532,12 +532,13 @@ __device__ __forceinline__ void progress_priority(int done, int total) {
 }
 
 // At least two waves per SIMD must stay resident (the decode streams at full bandwidth only
-// then): at most 256 VGPRs.  Wavefronts per workgroup (decode_layout): 2 for G = 8 (its LDS
-// numerators are twice as large per wavefront), 4 otherwise; for G = 4, 8 when that still gives
-// at least one workgroup per CU: one 512-thread workgroup per CU, whose wavefronts are all of one
-// age (with two 4-wavefront workgroups per CU the second one resident ran ~4 us behind the first;
-// 8 measured 1 us faster on the 16 x 8-group, 8192-token decode, but halves the grid, and a
-// 32-workgroup grid at 16384 tokens and batch 1 ran 48 against 35 us).
+// then): at most 256 VGPRs.  Wavefronts per workgroup (decode_layout): 4; for G = 4 and G = 8,
+// 8 when that still gives at least one workgroup per CU: one 512-thread workgroup per CU, whose
+// wavefronts are all of one age (with two 4-wavefront workgroups per CU the second one resident
+// ran ~4 us behind the first; 8 measured 1 us faster on the 16 x 8-group, 8192-token decode, but
+// halves the grid, and a 32-workgroup grid at 16384 tokens and batch 1 ran 48 against 35 us).
+// G = 8 doubles the LDS numerators per wavefront (77 KB per 4-wavefront workgroup, 143 KB per
+// 8-wavefront one in bf16), which still leaves two wavefronts per SIMD.
 template <typename KT, int D, int G, int NW, bool FUSED>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_kernel(DecodeArgs a) {
@@ -626,8 +627,9 @@ void decode_kernel(DecodeArgs a) {
   // cyclic run of 16 of the lowest spec_w stored dims (spec_w: the largest power of two up to
   // 32 and d_store, so that the run wraps with a mask), which the selection nearly always keeps
   // (the offline projection orders its dims by decreasing importance); a speculative row no head
-  // kept is weighted 0.  The walk then goes on over the rest of the union.
-  constexpr bool SPEC = FUSED && sizeof(KT) == 2 && NW >= 4;
+  // kept is weighted 0.  The walk then goes on over the rest of the union.  (Not for G = 8: the
+  // registers the speculative rows hold would spill there.)
+  constexpr bool SPEC = FUSED && sizeof(KT) == 2 && NW >= 4 && G <= 4;
   constexpr int NSPEC = SPEC ? 2 * kUnroll : 0;
   const int spec_w = a.d_store >= 32 ? 32 : 1 << (31 - __clz(a.d_store));
   const int spec_r0 = wg_mix & (spec_w - 1);
@@ -1366,13 +1368,13 @@ template <typename KT, int D, int G, bool FUSED>
 hipError_t launch_split_g(const DecodeArgs &a, const DecodeLayout &L, hipStream_t s) {
   if (a.S != (a.len + L.split - 1) / L.split) return hipErrorInvalidConfiguration;
   const dim3 grid(a.S, a.Hkv, a.B);
-  if constexpr (G == 4) {
+  if constexpr (G == 4 || G == 8) {
     if (L.waves == 8) {
       decode_kernel<KT, D, G, 8, FUSED><<<grid, dim3(512), 0, s>>>(a);
       return hipGetLastError();
     }
   }
-  constexpr int NW = G == 8 ? 2 : 4;
+  constexpr int NW = 4;
   if (L.waves != NW) return hipErrorInvalidConfiguration;
   decode_kernel<KT, D, G, NW, FUSED><<<grid, dim3(NW * 64), 0, s>>>(a);
   return hipGetLastError();

@@ -5,9 +5,9 @@ short-context kernel, the fused short step, the split-T kernel (plain and fused,
 workgroup layouts) and the H2O step.  The matrix below drives each of them: for every dtype,
 d and G, the fused step appends token T-1 to a cache of T-1 tokens and decodes, then aqua_decode
 runs on the same cache with the step's q' and masks, once at 1500 tokens (short-context kernels)
-and once at 5000 (split-T, 4 wavefronts per workgroup, 2 for G = 8).  Three larger shapes take
-the 8-wavefront split-T layout of G = 4 in the forms the benchmark does not: fp32 storage at
-d = 128 and d = 64, and bf16 at d = 64.  Each output is checked against the oracle (all heads in
+and once at 5000 (split-T, 4 wavefronts per workgroup).  Larger shapes take the 8-wavefront
+split-T layout in the forms the benchmark does not: G = 4 with fp32 storage at d = 128 and
+d = 64 and with bf16 at d = 64, and G = 8 in all four.  Each output is checked against the oracle (all heads in
 the matrix, sampled heads of every group in the large shapes), the masks against the oracle's
 selection of the GPU's q', and the appended token's K' and V; a one-token aqua_project_keys of
 the same token is checked the same way.  The streaming-read probe's result (the XOR of every
@@ -89,15 +89,19 @@ def test_instance_matrix(dtype, d, G, T):
     _step_then_decode(c)
 
 
-@pytest.mark.parametrize("dtype,d,B,T", [
-    ("f32", 128, 4, 16384),   # 32 groups x 8 splits of 2048 tokens: 256 workgroups
-    ("f32", 64, 4, 16384),
-    ("bf16", 64, 4, 32768),   # 32 groups x 8 splits of 4096 tokens
+@pytest.mark.parametrize("dtype,d,B,T,G", [
+    ("f32", 128, 4, 16384, 4),   # 32 groups x 8 splits of 2048 tokens: 256 workgroups
+    ("f32", 64, 4, 16384, 4),
+    ("bf16", 64, 4, 32768, 4),   # 32 groups x 8 splits of 4096 tokens
+    ("bf16", 128, 4, 32768, 8),  # G = 8 takes the same layout
+    ("bf16", 64, 4, 32768, 8),
+    ("f32", 128, 4, 16384, 8),
+    ("f32", 64, 4, 16384, 8),
 ])
-def test_eight_wave_layout_forms(dtype, d, B, T):
-    c = config(2 if d == 128 else 1, B=B, Hq=32, Hkv=8, d=d, T=T, k=3 * d // 4, d_store=d,
+def test_eight_wave_layout_forms(dtype, d, B, T, G):
+    c = config(2 if d == 128 else 1, B=B, Hq=8 * G, Hkv=8, d=d, T=T, k=3 * d // 4, d_store=d,
                d_sel=d, dtype=dtype)
-    heads = [(b, 4 * g + (b + g) % 4) for b in range(B) for g in range(8)]
+    heads = [(b, G * g + (b + g) % G) for b in range(B) for g in range(8)]
     _step_then_decode(c, heads=heads)
 
 
