@@ -7,10 +7,10 @@ d and G, the fused step appends token T-1 to a cache of T-1 tokens and decodes, 
 runs on the same cache with the step's q' and masks, once at 1500 tokens (short-context kernels)
 and once at 5000 (split-T, 4 wavefronts per workgroup).  Larger shapes take the 8-wavefront
 split-T layout in the forms the benchmark does not: G = 4 with fp32 storage at d = 128 and
-d = 64 and with bf16 at d = 64, and G = 8 in all four.  Each output is checked against the oracle (all heads in
-the matrix, sampled heads of every group in the large shapes), the masks against the oracle's
-selection of the GPU's q', and the appended token's K' and V; a one-token aqua_project_keys of
-the same token is checked the same way.  The streaming-read probe's result (the XOR of every
+d = 64 and with bf16 at d = 64, and G = 8 in all four.  Each output is checked against the
+oracle (all heads in the matrix, sampled heads of every group in the large shapes), the masks
+against the oracle's selection of the GPU's q', and the appended token's K' and V; a one-token
+aqua_project_keys of the same token is checked the same way.  The streaming-read probe's result (the XOR of every
 32-bit word of each workgroup's slice) is checked against the host's."""
 import math
 
